@@ -1,0 +1,278 @@
+"""SANTA decode-step attention, oracle side (fp64, NumPy).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Source: "Stochastic Sparse Attention for Memory-Bound Inference"
+(arXiv 2605.01910), abstract.  The abstract states that
+
+* every decode step reads all n_k key and value vectors (its first sentence),
+* SANTA samples S << n_k key indices from the post-softmax distribution and
+  aggregates only those value rows (second sentence),
+* this is an unbiased estimate of the post-softmax value aggregation and
+  replaces value-stage multiply-accumulates by gather-and-add (third),
+* stratified and systematic sampling are variance-reduced variants (fourth;
+  the first arXiv version names stratified sampling only),
+* Bernoulli qK^T sampling uses stochastic ternary queries to read fewer key
+  features in the score stage (the sentence introducing it).
+
+Everything below that the abstract leaves open follows the readings listed in
+the design doc (scale argument, inverse-CDF sampling, equal-probability strata,
+weights 1/S, duplicates counted, half-open CDF intervals, key-index CDF order,
+the Philox stream layout, keep probability |q_i| / max|q|).
+
+Per-head functions take 1-D / 2-D float64 arrays and are written to be read
+against those statements; the batched drivers only loop over (b, h).
+All arithmetic is fp64 on the exactly decoded fp16 inputs.
+
+Mode numbers: 0 = i.i.d. multinomial, 1 = stratified, 2 = systematic.
+"""
+
+import numpy as np
+
+from . import philox
+
+IID = 0
+STRATIFIED = 1
+SYSTEMATIC = 2
+MODES = (IID, STRATIFIED, SYSTEMATIC)
+_MODE_TAG = {
+    IID: philox.TAG_IID,
+    STRATIFIED: philox.TAG_STRATIFIED,
+    SYSTEMATIC: philox.TAG_SYSTEMATIC,
+}
+
+
+# ----------------------------------------------------------------------------
+# per-head steps
+# ----------------------------------------------------------------------------
+
+def head_scores(q_h, K_h, scale):
+    """Score stage: s_j = scale * <q, k_j> for every key j (fp64).
+
+    The abstract's premise is that every key is read; the sampling stage needs
+    the full post-softmax distribution, so every score is computed.
+    """
+    q_h = np.asarray(q_h, dtype=np.float64)
+    K_h = np.asarray(K_h, dtype=np.float64)
+    return scale * (K_h @ q_h)
+
+
+def distribution(s):
+    """Post-softmax distribution over key index order.
+
+    Returns (w, cum, F): w_j = exp(s_j - max s), cum = sequential prefix sum of
+    w in key-index order, F_j = cum_j / Z with Z = cum_{n-1}, so F_{n-1} = 1
+    exactly.  F is the CDF that the inverse-CDF sampler inverts.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    w = np.exp(s - np.max(s))
+    cum = np.cumsum(w)  # sequential, in key order
+    F = cum / cum[-1]
+    return w, cum, F
+
+
+def probabilities(s):
+    """p_j = w_j / Z, the post-softmax distribution itself."""
+    w, cum, _ = distribution(s)
+    return w / cum[-1]
+
+
+def points(mode, S, seed, row):
+    """The S sorted points t_0 <= ... <= t_{S-1} in [0, 1) for one query head.
+
+    * i.i.d. multinomial: S independent uniforms, sorted ascending.
+    * stratified: one uniform per equal-probability stratum [k/S, (k+1)/S),
+      t_k = (k + u_k) / S.
+    * systematic: a single uniform offset shared by all strata,
+      t_k = (k + u) / S.
+    ``row`` selects the stream (b * H_q + h); uniforms come from the mode's tag.
+    """
+    if mode not in MODES:
+        raise ValueError("unknown sampling mode %r" % (mode,))
+    tag = _MODE_TAG[mode]
+    k = np.arange(S, dtype=np.float64)
+    if mode == SYSTEMATIC:
+        u = philox.uniforms(seed, row, tag, 1)[0]
+        return (k + u) / S
+    u = philox.uniforms(seed, row, tag, S)
+    if mode == STRATIFIED:
+        return (k + u) / S
+    return np.sort(u, kind="stable")
+
+
+def inverse_cdf(F, t):
+    """Key index of each point: the j with F_{j-1} <= t < F_j (F_{-1} = 0).
+
+    That is the number of CDF values <= t; a point exactly on F_j goes to key
+    j + 1.  The result is clamped to n - 1 (only reachable through rounding).
+    """
+    idx = np.searchsorted(F, t, side="right")
+    return np.minimum(idx, len(F) - 1)
+
+
+def gather_average(V_h, idx, S):
+    """The SANTA estimate: (1/S) * sum_k V[i_k], duplicates counted."""
+    V_h = np.asarray(V_h, dtype=np.float64)
+    return V_h[np.asarray(idx, dtype=np.int64)].sum(axis=0) / S
+
+
+def dense_head(s, V_h):
+    """Exact post-softmax value aggregation sum_j p_j V_j (the estimand)."""
+    w, cum, _ = distribution(s)
+    V_h = np.asarray(V_h, dtype=np.float64)
+    return (w @ V_h) / cum[-1]
+
+
+def ternary_query(q_group, u):
+    """Stochastic ternary queries for the G query heads of one KV head.
+
+    q_group: (G, d) fp64 query vectors; u: (d,) uniforms shared by the group.
+    Keep probability of feature i for head h is |q_hi| / A_h with
+    A_h = max_i |q_hi|; a kept feature becomes sign(q_hi) * A_h, a dropped one
+    0, so E[q~] = q.  Returns (q_tilde (G, d), kept (G, d) bool, A (G,)).
+    The comparison u * A < |q| is exact in fp64 (24-bit times 11-bit product).
+    """
+    q_group = np.asarray(q_group, dtype=np.float64)
+    A = np.max(np.abs(q_group), axis=1)
+    kept = u[None, :] * A[:, None] < np.abs(q_group)
+    q_tilde = np.where(kept, np.sign(q_group) * A[:, None], 0.0)
+    return q_tilde, kept, A
+
+
+# ----------------------------------------------------------------------------
+# batched drivers
+# ----------------------------------------------------------------------------
+
+def _check_shapes(q, K, V, n_k):
+    B, Hq, d = q.shape
+    B2, Hkv, max_n_k, d2 = K.shape
+    if B2 != B or d2 != d or V.shape != K.shape or Hq % Hkv != 0:
+        raise ValueError("inconsistent shapes q%s K%s V%s" % (q.shape, K.shape, V.shape))
+    n_k = np.asarray(n_k, dtype=np.int64).reshape(-1)
+    if n_k.shape != (B,):
+        raise ValueError("n_k must have one entry per batch element")
+    return B, Hq, Hkv, d, max_n_k, n_k
+
+
+def _f64(x):
+    return np.asarray(x).astype(np.float64)
+
+
+def santa_decode(q, K, V, n_k, S, mode, seed, scale, score_override=None,
+                 return_detail=False):
+    """Oracle for one SANTA decode step.
+
+    q: (B, H_q, d); K, V: (B, H_kv, max_n_k, d) (any float dtype, decoded to
+    fp64); n_k: (B,) valid keys per sequence.  Returns (out (B, H_q, d) fp64,
+    indices (B, H_q, S) int64 ascending).  A sequence with n_k outside
+    [1, max_n_k] yields NaN outputs and indices -1.
+
+    ``score_override`` (B, H_q, max_n_k), if given, replaces the score stage
+    (used to re-run the later steps on externally supplied scores).
+    ``return_detail`` adds a dict with per-head points and CDFs.
+    """
+    if S < 1:
+        raise ValueError("S must be >= 1")
+    B, Hq, Hkv, d, max_n_k, n_k = _check_shapes(q, K, V, n_k)
+    G = Hq // Hkv
+    qf, Kf, Vf = _f64(q), K, V
+    out = np.full((B, Hq, d), np.nan)
+    idx_all = np.full((B, Hq, S), -1, dtype=np.int64)
+    detail = {"t": {}, "F": {}}
+    for b in range(B):
+        n = int(n_k[b])
+        if n < 1 or n > max_n_k:
+            continue
+        for h in range(Hq):
+            hk = h // G
+            Vh = _f64(Vf[b, hk, :n])
+            if score_override is None:
+                s = head_scores(qf[b, h], _f64(Kf[b, hk, :n]), scale)
+            else:
+                s = _f64(score_override[b, h, :n])
+            _, _, F = distribution(s)
+            t = points(mode, S, seed, b * Hq + h)
+            idx = inverse_cdf(F, t)
+            out[b, h] = gather_average(Vh, idx, S)
+            idx_all[b, h] = idx
+            if return_detail:
+                detail["t"][(b, h)] = t
+                detail["F"][(b, h)] = F
+    if return_detail:
+        return out, idx_all, detail
+    return out, idx_all
+
+
+def dense_decode(q, K, V, n_k, scale):
+    """Exact attention output softmax(scale * q K^T) V per (b, h) in fp64."""
+    B, Hq, Hkv, d, max_n_k, n_k = _check_shapes(q, K, V, n_k)
+    G = Hq // Hkv
+    qf = _f64(q)
+    out = np.full((B, Hq, d), np.nan)
+    for b in range(B):
+        n = int(n_k[b])
+        if n < 1 or n > max_n_k:
+            continue
+        for hk in range(Hkv):
+            Kh = _f64(K[b, hk, :n])
+            Vh = _f64(V[b, hk, :n])
+            for g in range(G):
+                h = hk * G + g
+                out[b, h] = dense_head(head_scores(qf[b, h], Kh, scale), Vh)
+    return out
+
+
+def bernoulli_queries(q, Hkv, seed):
+    """Ternary queries for every (b, h): (q_tilde, kept, A).
+
+    The d uniforms of KV head (b, h_kv) come from stream row b * H_kv + h_kv of
+    the 'BERN' tag and are shared by the G query heads of that KV head.
+    """
+    qf = _f64(q)
+    B, Hq, d = qf.shape
+    G = Hq // Hkv
+    q_tilde = np.zeros_like(qf)
+    kept = np.zeros(qf.shape, dtype=bool)
+    A = np.zeros((B, Hq))
+    for b in range(B):
+        for hk in range(Hkv):
+            u = philox.uniforms(seed, b * Hkv + hk, philox.TAG_BERNOULLI, d)
+            sl = slice(hk * G, (hk + 1) * G)
+            q_tilde[b, sl], kept[b, sl], A[b, sl] = ternary_query(qf[b, sl], u)
+    return q_tilde, kept, A
+
+
+def bernoulli_decode(q, K, V, n_k, S, mode, seed, scale, return_detail=False):
+    """Bernoulli qK^T mode: ternary-query scores, then the SANTA value stage.
+
+    The scores use q~ in place of q; the softmax, points, search and estimate
+    are those of ``santa_decode`` on the new scores.  Returns
+    (out, indices, kept (B, H_q, d) bool) and, on request, a detail dict.
+    """
+    Hkv = _check_shapes(q, K, V, n_k)[2]
+    q_tilde, kept, _ = bernoulli_queries(q, Hkv, seed)
+    res = santa_decode(q_tilde, K, V, n_k, S, mode, seed, scale,
+                       return_detail=return_detail)
+    if return_detail:
+        out, idx, detail = res
+        return out, idx, kept, detail
+    out, idx = res
+    return out, idx, kept
+
+
+def all_scores(q, K, n_k, scale):
+    """Scores (B, H_q, max_n_k) fp64, NaN beyond n_k (for diagnostics)."""
+    qf = _f64(q)
+    B, Hq, d = qf.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    max_n_k = K.shape[2]
+    n_k = np.asarray(n_k, dtype=np.int64).reshape(-1)
+    s = np.full((B, Hq, max_n_k), np.nan)
+    for b in range(B):
+        n = int(n_k[b])
+        if n < 1 or n > max_n_k:
+            continue
+        for h in range(Hq):
+            s[b, h, :n] = head_scores(qf[b, h], _f64(K[b, h // G, :n]), scale)
+    return s
