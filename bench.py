@@ -1,0 +1,188 @@
+"""Benchmark: SANTA systematic decode step on a Llama-3.1-8B-shaped layer at 32k.
+
+One step = one santa_decode call over the whole decode batch of one attention
+layer (B=1, 32 query heads, 8 KV heads, d=128, n_k=32768, fp16 K/V with 1%
+planted heavy hitters, systematic sampling, S=128).  Inputs are resident in
+HBM before timing starts; steps rotate over R distinct copies of the KV cache
+(like consecutive layers) so that the 256 MiB Infinity Cache cannot serve K
+from a previous step.
+
+value = effective HBM bandwidth in TB/s = algorithmic bytes / step time, where
+the algorithmic bytes are all of K (B * H_kv * n_k * d * 2) plus S value rows
+per KV head (B * H_kv * S * d * 2).  The dense split-K kernel of the same
+library is timed under the same protocol for the speedup figure, and the CPU
+oracle on a bounded sample of the same workload gives `cpu_baseline`.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama32k", choices=["llama32k", "batched", "sweep131k", "bernoulli"])
+    ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid"])
+    ap.add_argument("--S", type=int, default=128)
+    ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of distinct KV copies to rotate over")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+def make_workload(name):
+    from stochastic_sparse_decode_amd import workloads as W
+    if name == "llama32k":
+        return W.llama(B=1, n_k=32768, seed=1001), "Llama-3.1-8B decode layer, B=1, 32q/8kv, d=128, n_k=32768"
+    if name == "batched":
+        return (W.llama(B=16, n_k_range=(8192, 32768), seed=1002),
+                "Llama-3.1-8B decode layer, B=16, n_k~U[8192,32768], 32q/8kv, d=128")
+    if name == "sweep131k":
+        return W.sweep(B=4, n_k=131072, r=1.0, seed=1003), "context sweep B=4, n_k=131072, r=1, 32q/8kv, d=128"
+    return W.bernoulli(B=8, n_k=32768, seed=1004), "Bernoulli case B=8, n_k=32768, 32q/8kv, d=128"
+
+
+def algorithmic_bytes(wl, S, dense=False):
+    k_bytes = int(wl.n_k.astype("int64").sum()) * wl.Hkv * wl.d * 2
+    if dense:
+        return 2 * k_bytes
+    return k_bytes + wl.B * wl.Hkv * S * wl.d * 2
+
+
+def timed(fn, sets, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step (= per launch: one launch per step)
+
+
+def cpu_baseline(wl, S, mode, seconds):
+    """Time the fp64 oracle on whole decode steps of the same workload (bounded)."""
+    from oracle import santa as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, n, wl.scale)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    per_step = (time.perf_counter() - t0) / n
+    tbs = algorithmic_bytes(wl, S) / per_step / 1e12
+    return {"value": tbs, "unit": "TB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full decode step(s) of the same workload, %.2f s per step" % (n, per_step)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on a single GPU; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from stochastic_sparse_decode_amd import santa
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "dispatches": 5}))
+        return
+
+    mode = santa.MODES[args.mode]
+    wl, desc = make_workload(args.workload)
+    q = torch.from_numpy(wl.q).to(dev)
+    nk = torch.from_numpy(wl.n_k.astype(np.int32)).to(dev)
+    K0 = torch.from_numpy(wl.K).to(dev)
+    V0 = torch.from_numpy(wl.V).to(dev)
+    set_bytes = 2 * K0.numel() * 2
+    R = max(1, int(math.ceil(args.rotate_bytes * (1 << 30) / set_bytes)))
+    sets = [(K0, V0)] + [(K0.clone(), V0.clone()) for _ in range(R - 1)]
+    prob = santa.problem(q, K0, wl.scale)
+    ws = santa.new_workspace(prob, dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    S = args.S
+
+    if args.workload == "bernoulli":
+        sets = [(santa.santa_pack_k_feature_major(k), v) for k, v in sets]
+        step = lambda kv: santa.santa_bernoulli_qk(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa
+                                                   workspace=ws)
+    else:
+        step = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
+                                             workspace=ws)
+    ms = timed(step, sets, args.steps, args.warmup)
+    assert santa.santa_workspace_error(ws) == 0
+    nbytes = algorithmic_bytes(wl, S)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+
+    dense_ms = None
+    if not args.no_dense and args.workload != "bernoulli":
+        dstep = lambda kv: santa.santa_dense_decode(q, kv[0], kv[1], nk, wl.scale, out=out, workspace=ws)  # noqa
+        dense_ms = timed(dstep, sets, args.steps, args.warmup)
+
+    res = {
+        "metric": "decode-attention us/step + effective HBM TB/s (% peak), Llama-3.1-8B shape @32k",
+        "value": gbs / 1000.0,
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "us_per_step": ms * 1000.0,
+        "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic (seeded; rotated over %d KV copies, %.2f GiB)" % (R, R * set_bytes / (1 << 30)),
+        "config": {"workload": desc, "mode": args.mode, "S": S, "global_batch": wl.B, "seq_len": int(wl.n_k.max()),
+                   "parallelism": "none (1 GPU)"},
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+    }
+    if dense_ms is not None:
+        dbytes = algorithmic_bytes(wl, S, dense=True)
+        res["dense"] = {"us_per_step": dense_ms * 1000.0, "effective_GBs": dbytes / (dense_ms * 1e-3) / 1e9,
+                        "pct_hbm_peak": 100.0 * dbytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        res["speedup_vs_dense"] = dense_ms / ms
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, S, mode, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,167 @@
+/*
+ * libsanta: SANTA stochastic sparse decode-step attention on MI355X (gfx950).
+ *
+ * The operations follow the abstract of "Stochastic Sparse Attention for
+ * Memory-Bound Inference" (arXiv 2605.01910):
+ *
+ *   - santa_decode: score every key of the KV cache, form the post-softmax
+ *     distribution, draw S key indices from it (i.i.d., stratified, or
+ *     systematic with one offset), gather only those S value rows and average
+ *     them.  This is the abstract's SANTA estimator (its second and third
+ *     sentences: a few key indices drawn from the softmax weights, their value
+ *     rows added and averaged, which estimates the softmax-weighted value sum
+ *     without bias) with the variance-reduced stratified and systematic
+ *     variants of its fourth sentence.
+ *   - santa_dense_decode: the exact softmax(scale q K^T) V, reading all of K
+ *     and V, split over the key sequence (FlashDecoding style; the baseline
+ *     the abstract compares against).
+ *   - santa_bernoulli_qk: the abstract's Bernoulli qK^T sampling, which
+ *     replaces each query by a stochastic ternary vector so that only the kept
+ *     key features are read in the score stage, followed by the SANTA value
+ *     stage.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Shapes: B sequences, H_q query heads, H_kv KV heads (G = H_q / H_kv query
+ *  heads share a KV head: query head h reads KV head h / G), head dimension d.
+ *  Layouts (all row-major, fp16 = IEEE binary16):
+ *    q        [B][H_q][d]              fp16
+ *    K, V     [B][H_kv][max_n_k][d]    fp16; sequence b uses rows 0..n_k[b]-1
+ *    K_fm     [B][H_kv][max_n_k/64][d][64] fp16 (Bernoulli only; see
+ *             santa_pack_k_feature_major)
+ *    n_k      [B]                      int32, in device memory
+ *    out      [B][H_q][d]              fp32
+ *    indices  [B][H_q][S]              int32, ascending key indices (optional)
+ *    scores   [B][H_q][max_n_k]        fp32 scale * <q, k_j> (optional, debug)
+ *  Every pointer argument except `problem` is a device pointer.
+ *  Score: s_j = scale * <q, k_j>; the softmax is taken over j < n_k[b].
+ *
+ *  Ownership: the caller owns every buffer.  The library allocates no device
+ *  memory, keeps no pointer after a call returns, and never synchronises:
+ *  kernels are enqueued on `stream` (a hipStream_t; NULL = default stream) and
+ *  the caller keeps all buffers alive until the stream has completed them.
+ *
+ *  Workspace: a device buffer of at least santa_workspace_bytes(problem)
+ *  bytes, zero-filled by the caller once before first use.  Kernels leave
+ *  their counters at zero when they finish, so the buffer can be reused by
+ *  later calls with the same or a smaller problem.  Calls that share one
+ *  workspace must not run concurrently.  After a call that reported a device
+ *  error (santa_workspace_error != 0) the workspace must be zero-filled again.
+ *
+ *  Errors: every entry point returns a santa_status.  Arguments are checked
+ *  on the host before any HIP call; on a check failure nothing is enqueued.
+ *  n_k lives in device memory and cannot be checked without a sync: a
+ *  sequence with n_k[b] < 1 or n_k[b] > max_n_k yields NaN outputs (and index
+ *  -1) for all its heads.  Asynchronous device faults surface at the caller's
+ *  next synchronisation.
+ *
+ *  Randomness: `seed` (64 bits) is the whole random state of a call.  The
+ *  uniforms come from the counter-based generator Philox4x32-10 (Salmon et
+ *  al., SC'11): uniform k of stream (row, tag) is output word (k & 3) of
+ *  Philox4x32-10 on counter (k >> 2, row, tag, 0) with key (seed low 32 bits,
+ *  seed high 32 bits), mapped to (word >> 8) * 2^-24.  row = b * H_q + h for
+ *  value sampling; tags are the ASCII codes 'SYST' (systematic offset),
+ *  'STRT' (stratified), 'IID ' (i.i.d.), 'BERN' (Bernoulli features, row
+ *  b * H_kv + h_kv).  Equal inputs and seed give bit-identical results.
+ */
+#ifndef SANTA_H_
+#define SANTA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum santa_status {
+  SANTA_OK = 0,
+  SANTA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SANTA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes, S, scale */
+  SANTA_ERR_UNSUPPORTED = 3, /* head_dim, group size or n_k range not built */
+  SANTA_ERR_ALIGN = 4,       /* q/K/V/K_fm not 16-byte or out/indices/scores/n_k not 4-byte aligned */
+  SANTA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than santa_workspace_bytes */
+  SANTA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+  SANTA_ERR_MODE = 7         /* unknown sampling mode */
+} santa_status;
+
+/* Sampling schemes for the S points t_0 <= ... <= t_{S-1} in [0, 1):
+ *  SANTA_IID:        S independent uniforms, sorted;
+ *  SANTA_STRATIFIED: t_k = (k + u_k) / S, one uniform per stratum;
+ *  SANTA_SYSTEMATIC: t_k = (k + u) / S, one uniform offset for all strata.
+ * Point t selects the key j with F_{j-1} <= t < F_j, F the CDF of the
+ * post-softmax distribution in key order (F_{-1} = 0). */
+typedef enum santa_mode { SANTA_IID = 0, SANTA_STRATIFIED = 1, SANTA_SYSTEMATIC = 2 } santa_mode;
+
+/* Problem description (host memory, read during the call only). */
+typedef struct santa_problem {
+  int32_t batch;        /* B >= 1 */
+  int32_t num_q_heads;  /* H_q >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads; /* H_kv >= 1; G = H_q / H_kv must be 1, 2, 4 or 8 */
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t max_n_k;      /* rows reserved per (sequence, KV head) in K and V, >= 1 */
+  float scale;          /* finite; score = scale * <q, k> (typically 1/sqrt(d)) */
+} santa_problem;
+
+/* Largest sample count accepted by santa_decode / santa_bernoulli_qk. */
+#define SANTA_MAX_S 1024
+
+/* Bytes of device workspace needed by every entry point for `problem`
+ * (0 if the problem is invalid). */
+size_t santa_workspace_bytes(const santa_problem* problem);
+
+/* SANTA decode step (the abstract's estimator, its second to fourth sentences).
+ *   out[b][h] = (1/S) * sum_k V[b][h/G][i_k],  i_k drawn by `mode` from the
+ *   post-softmax distribution of scale * q[b][h] . K[b][h/G][j], j < n_k[b].
+ * S in [1, SANTA_MAX_S] (S may exceed n_k: sampling is with replacement).
+ * indices_out (nullable): the S sampled key indices per head, ascending.
+ * scores_out (nullable, debug): the fp32 scores the sampler used.
+ * ceil(max_n_k / 1024) may not exceed the device's resident-workgroup count
+ * for this kernel (>= 256 on MI355X, i.e. max_n_k >= 262144 is always
+ * accepted); larger caches return SANTA_ERR_UNSUPPORTED. */
+int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V,
+                 const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
+                 int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Exact decode attention: out[b][h] = softmax(scale q K^T) V over j < n_k[b]
+ * (the FlashDecoding-style baseline named in the abstract's fifth sentence). */
+int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,
+                       const int32_t* n_k, float* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Bernoulli qK^T step (the abstract's stochastic ternary queries) followed by
+ * the SANTA value stage.  For KV head (b, h_kv) one uniform u_i per feature i
+ * (stream 'BERN', row b * H_kv + h_kv) is shared by its G query heads; head h
+ * keeps feature i iff u_i * A_h < |q_hi| with A_h = max_i |q_hi|, and the kept
+ * feature's query value becomes sign(q_hi) * A_h (so E[q~] = q).  Scores use
+ * q~ and read only the union of the group's kept features from K_fm.
+ * K_fm: feature-major K (max_n_k must be a multiple of 64).  V: row-major.
+ * kept_out (nullable): [B][H_q][d] uint8 mask of kept features. */
+int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* K_fm, const void* V,
+                       const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
+                       int32_t* indices_out, float* scores_out, uint8_t* kept_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Relayout a row-major K [B][H_kv][max_n_k][d] into the 64-key feature-major
+ * tiles read by santa_bernoulli_qk: K_fm[b][h][t][i][x] = K[b][h][64 t + x][i].
+ * max_n_k must be a multiple of 64; K and K_fm must not overlap. */
+int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void* K_fm, void* stream);
+
+/* Copy the device error bits of a workspace to *flags (synchronises `stream`).
+ * Bit 0: a bounded cross-workgroup wait timed out (results invalid). */
+int santa_workspace_error(const void* workspace, uint32_t* flags, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* santa_status_string(int status);
+
+/* ABI version of this header (incremented on incompatible changes). */
+#define SANTA_ABI_VERSION 1
+int32_t santa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SANTA_H_ */

@@ -1,0 +1,191 @@
+// Device helpers shared by the libsanta kernels (gfx950, wave64).
+//
+// Nothing here is specific to one kernel: the Philox4x32-10 generator, fp16
+// row-slice loads, DPP cross-lane moves, wave reductions/scans and the
+// agent-scope atomics used for the cross-workgroup hand-offs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace santa {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11).  Round: 32x32->64-bit products of c0 and c2 with the
+// two round multipliers, output (hi1^c1^k0, lo1, hi0^c3^k1, lo0); the key is
+// bumped by the two Weyl constants between rounds; ten rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+  constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += kWeylA;
+      k1 += kWeylB;
+    }
+    const uint32_t lo_a = kMulA * c.x, hi_a = __umulhi(kMulA, c.x);
+    const uint32_t lo_b = kMulB * c.z, hi_b = __umulhi(kMulB, c.z);
+    c = make_uint4(hi_b ^ c.y ^ k0, lo_b, hi_a ^ c.w ^ k1, lo_a);
+  }
+  return c;
+}
+
+// Stream tags (ASCII of a four-letter name), one stream per use.
+constexpr uint32_t kTagSystematic = 0x53595354u;  // 'SYST'
+constexpr uint32_t kTagStratified = 0x53545254u;  // 'STRT'
+constexpr uint32_t kTagIid = 0x49494420u;         // 'IID '
+constexpr uint32_t kTagBernoulli = 0x4245524Eu;   // 'BERN'
+
+// Block `blk` of stream (seed, row, tag): words 4*blk .. 4*blk+3.
+__device__ __forceinline__ uint4 stream_block(uint64_t seed, uint32_t row, uint32_t tag, uint32_t blk) {
+  return philox4x32_10(make_uint4(blk, row, tag, 0u), (uint32_t)(seed & 0xffffffffu), (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t word_of(uint4 w, int e) {
+  return e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
+}
+
+// 24-bit integer behind a uniform: u = (x >> 8) * 2^-24 exactly.
+__device__ __forceinline__ uint32_t uniform_bits(uint32_t x) { return x >> 8; }
+__device__ __forceinline__ double uniform_f64(uint32_t x) { return (double)(x >> 8) * 0x1.0p-24; }
+
+// ---------------------------------------------------------------------------
+// fp16 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
+
+// 8-element fp16 dot product accumulated in fp32 (v_dot2 on gfx950).
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  float acc = 0.f;
+  acc = __builtin_amdgcn_fdot2(as_h2(a.x), as_h2(b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(b.w), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ void unpack8(uint4 v, float* f) {
+  half2v h;
+  h = as_h2(v.x); f[0] = (float)h.x; f[1] = (float)h.y;
+  h = as_h2(v.y); f[2] = (float)h.x; f[3] = (float)h.y;
+  h = as_h2(v.z); f[4] = (float)h.x; f[5] = (float)h.y;
+  h = as_h2(v.w); f[6] = (float)h.x; f[7] = (float)h.y;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint: the data is read once).
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
+// DPP lane exchanges inside a 16-lane row.
+// ---------------------------------------------------------------------------
+enum DppCtrl : int {
+  kDppXor1 = 0xB1,          // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,          // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141,   // lane ^ 7 inside each group of 8
+  kDppRor8 = 0x128,         // lane ^ 8 inside each row of 16
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Reduce-scatter across the LPR lanes of a key row.  On entry every lane holds
+// NV = LPR partial sums v[0..NV); on exit lane (lane % LPR) holds in v[0] the
+// full sum of combination index (lane % LPR).  Partner lanes are paired with
+// the masks 8, 7, 2, 1 (LPR = 16) or 7, 2, 1 (LPR = 8); the half kept by a lane
+// is chosen by one bit of its lane id that differs between partners.
+template <int LPR>
+__device__ __forceinline__ void row_reduce_scatter(float* v, int lane) {
+  static_assert(LPR == 8 || LPR == 16, "row width");
+  if constexpr (LPR == 16) {
+    const bool hi = (lane >> 3) & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float send = hi ? v[i] : v[i + 8];
+      float keep = hi ? v[i + 8] : v[i];
+      v[i] = keep + dpp<kDppRor8>(send);
+    }
+  }
+  {
+    const bool hi = (lane >> 2) & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float send = hi ? v[i] : v[i + 4];
+      float keep = hi ? v[i + 4] : v[i];
+      v[i] = keep + dpp<kDppHalfMirror>(send);
+    }
+  }
+  {
+    const bool hi = (lane >> 1) & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float send = hi ? v[i] : v[i + 2];
+      float keep = hi ? v[i + 2] : v[i];
+      v[i] = keep + dpp<kDppXor2>(send);
+    }
+  }
+  {
+    const bool hi = lane & 1;
+    float send = hi ? v[0] : v[1];
+    float keep = hi ? v[1] : v[0];
+    v[0] = keep + dpp<kDppXor1>(send);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions and scans (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max_masked(float x, int first_mask) {
+  for (int m = first_mask; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+__device__ __forceinline__ double wave_incl_scan_f64(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    double y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Agent-scope hand-offs between workgroups.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_acquire(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+
+}  // namespace santa

@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace santa {
+
+constexpr int kThreads = 256;   // threads per workgroup (4 waves)
+constexpr int kWaves = kThreads / 64;
+constexpr int kSplit = 1024;    // keys per work item (one split of one KV head)
+constexpr int kMaxS = 1024;     // largest sample count
+constexpr int kTile = 64;       // keys per feature-major tile (Bernoulli mode)
+constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait: ~1 s, then error flag
+
+// Error bits written by kernels into the workspace header.
+constexpr uint32_t kErrSpinTimeout = 1u;
+
+// Device pointers carved out of the caller's workspace.
+struct Workspace {
+  uint32_t* err;        // error bits (never cleared by kernels)
+  uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
+  uint32_t* bar_stats;  // [groups] arrivals of split statistics
+  uint32_t* bar_done;   // [groups] arrivals of split partial outputs
+  float2* stats;        // [groups][ns][G] (local max, local sum-exp)
+  float* partial;       // [groups][ns][G][D + 2] partial outputs (+ m, l for dense)
+};
+
+struct DecodeParams {
+  const void* q;        // [B][Hq][D] fp16
+  const void* K;        // [B][Hkv][max_n_k][D] fp16 (row-major) or feature-major tiles
+  const void* V;        // [B][Hkv][max_n_k][D] fp16
+  const int32_t* n_k;   // [B]
+  float* out;           // [B][Hq][D]
+  int32_t* idx_out;     // [B][Hq][S] or null
+  float* scores_out;    // [B][Hq][max_n_k] or null
+  uint8_t* kept_out;    // [B][Hq][D] or null (Bernoulli)
+  int B, Hq, Hkv, D, G, max_n_k, S, mode;
+  uint64_t seed;
+  float scale;
+  int ns;               // splits per group = ceil(max_n_k / kSplit)
+  int total_items;      // B * Hkv * ns
+  int grid;             // persistent workgroups
+  Workspace ws;
+};
+
+enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2 };
+
+// Resident-workgroup capacity of the current device for a kernel variant.
+int decode_capacity(int D, int G, bool bernoulli);
+int dense_capacity(int D, int G);
+
+hipError_t launch_decode(const DecodeParams& p, bool bernoulli, hipStream_t stream);
+hipError_t launch_dense(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_pack_feature_major(const void* K, void* K_fm, int B, int Hkv, int max_n_k, int D,
+                                     hipStream_t stream);
+
+}  // namespace santa

@@ -1,0 +1,229 @@
+// C-ABI layer of libsanta: argument checks, workspace carving, launch shape.
+// Declarations and the meaning of every argument: include/santa.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+
+#include "../../include/santa.h"
+#include "launch.h"
+
+namespace {
+
+using santa::DecodeParams;
+using santa::Workspace;
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t header, bar_stats, bar_done, stats, partial, total;
+};
+
+bool problem_ok(const santa_problem* p) {
+  if (!p) return false;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 || p->max_n_k < 1) return false;
+  if (p->num_q_heads % p->num_kv_heads != 0) return false;
+  if (!std::isfinite(p->scale)) return false;
+  const long long groups = (long long)p->batch * p->num_kv_heads;
+  const long long ns = ((long long)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
+  if (groups * ns > (1ll << 30)) return false;
+  if ((long long)p->batch * p->num_q_heads > (1ll << 30)) return false;
+  return true;
+}
+
+int group_size(const santa_problem* p) { return p->num_q_heads / p->num_kv_heads; }
+
+bool supported(const santa_problem* p) {
+  const int G = group_size(p);
+  return (p->head_dim == 64 || p->head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+Layout layout_of(const santa_problem* p) {
+  Layout L{};
+  const size_t groups = (size_t)p->batch * p->num_kv_heads;
+  const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
+  const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
+  L.header = 0;
+  L.bar_stats = L.header + kAlign;
+  L.bar_done = L.bar_stats + round_up(groups * sizeof(uint32_t));
+  L.stats = L.bar_done + round_up(groups * sizeof(uint32_t));
+  L.partial = L.stats + round_up(groups * ns * G * sizeof(float2));
+  L.total = L.partial + round_up(groups * ns * G * (D + 2) * sizeof(float));
+  return L;
+}
+
+Workspace carve(void* base, const Layout& L) {
+  unsigned char* b = (unsigned char*)base;
+  Workspace w;
+  w.err = (uint32_t*)(b + L.header);
+  w.work_ctr = (uint32_t*)(b + L.header) + 1;
+  w.bar_stats = (uint32_t*)(b + L.bar_stats);
+  w.bar_done = (uint32_t*)(b + L.bar_done);
+  w.stats = (float2*)(b + L.stats);
+  w.partial = (float*)(b + L.partial);
+  return w;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// Resident-workgroup capacity per (device, kernel variant), computed once.
+constexpr int kMaxDevices = 64;
+constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 3 /*kernel*/;
+std::mutex g_cap_mutex;
+int g_cap[kMaxDevices][kVariants];
+
+int variant_index(int D, int G, int kind) {
+  const int di = D == 128 ? 1 : 0;
+  const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  return (kind * 2 + di) * 4 + gi;
+}
+
+int capacity(int D, int G, int kind) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_cap_mutex);
+  int& slot = g_cap[dev][variant_index(D, G, kind)];
+  if (slot == 0) {
+    slot = kind == santa::kOpDense ? santa::dense_capacity(D, G)
+                                   : santa::decode_capacity(D, G, kind == santa::kOpBernoulli);
+  }
+  return slot;
+}
+
+int common_checks(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
+                  const float* out, const void* ws, size_t ws_bytes) {
+  if (!p) return SANTA_ERR_NULL;
+  if (!q || !K || !V || !n_k || !out) return SANTA_ERR_NULL;
+  if (!problem_ok(p)) return SANTA_ERR_SHAPE;
+  if (!supported(p)) return SANTA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 4) || !aligned(n_k, 4))
+    return SANTA_ERR_ALIGN;
+  if (!ws || ws_bytes < layout_of(p).total || !aligned(ws, 16)) return SANTA_ERR_WORKSPACE;
+  return SANTA_OK;
+}
+
+DecodeParams base_params(const santa_problem* p, const void* q, const void* K, const void* V,
+                         const int32_t* n_k, float* out, void* ws) {
+  DecodeParams d{};
+  d.q = q;
+  d.K = K;
+  d.V = V;
+  d.n_k = n_k;
+  d.out = out;
+  d.B = p->batch;
+  d.Hq = p->num_q_heads;
+  d.Hkv = p->num_kv_heads;
+  d.D = p->head_dim;
+  d.G = group_size(p);
+  d.max_n_k = p->max_n_k;
+  d.scale = p->scale;
+  d.ns = (p->max_n_k + santa::kSplit - 1) / santa::kSplit;
+  d.total_items = p->batch * p->num_kv_heads * d.ns;
+  d.ws = carve(ws, layout_of(p));
+  return d;
+}
+
+// grid = all items if they fit the resident capacity, else the capacity (and
+// then a group's splits must fit in it, for the cross-workgroup waits).
+int choose_grid(DecodeParams& d, int kind) {
+  const int cap = capacity(d.D, d.G, kind);
+  if (cap <= 0) return SANTA_ERR_HIP;
+  d.grid = d.total_items < cap ? d.total_items : cap;
+  if (kind != santa::kOpDense && d.grid < d.total_items && d.ns > d.grid) return SANTA_ERR_UNSUPPORTED;
+  return SANTA_OK;
+}
+
+int sampled_step(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
+                 int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
+                 uint8_t* kept_out, void* ws, size_t ws_bytes, void* stream, int kind) {
+  int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes);
+  if (st != SANTA_OK) return st;
+  if (S < 1 || S > SANTA_MAX_S) return SANTA_ERR_SHAPE;
+  if (mode != SANTA_IID && mode != SANTA_STRATIFIED && mode != SANTA_SYSTEMATIC) return SANTA_ERR_MODE;
+  if ((indices_out && !aligned(indices_out, 4)) || (scores_out && !aligned(scores_out, 4))) return SANTA_ERR_ALIGN;
+  if (kind == santa::kOpBernoulli && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
+  DecodeParams d = base_params(p, q, K, V, n_k, out, ws);
+  d.idx_out = indices_out;
+  d.scores_out = scores_out;
+  d.kept_out = kept_out;
+  d.S = S;
+  d.mode = mode;
+  d.seed = seed;
+  st = choose_grid(d, kind);
+  if (st != SANTA_OK) return st;
+  const hipError_t e = santa::launch_decode(d, kind == santa::kOpBernoulli, (hipStream_t)stream);
+  return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t santa_workspace_bytes(const santa_problem* problem) {
+  if (!problem_ok(problem)) return 0;
+  return layout_of(problem).total;
+}
+
+int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
+                 int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, workspace,
+                      workspace_bytes, stream, santa::kOpDecode);
+}
+
+int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* K_fm, const void* V,
+                       const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
+                       int32_t* indices_out, float* scores_out, uint8_t* kept_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return sampled_step(problem, q, K_fm, V, n_k, S, mode, seed, out, indices_out, scores_out, kept_out, workspace,
+                      workspace_bytes, stream, santa::kOpBernoulli);
+}
+
+int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,
+                       const int32_t* n_k, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes);
+  if (st != SANTA_OK) return st;
+  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace);
+  st = choose_grid(d, santa::kOpDense);
+  if (st != SANTA_OK) return st;
+  const hipError_t e = santa::launch_dense(d, (hipStream_t)stream);
+  return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
+int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void* K_fm, void* stream) {
+  if (!problem || !K || !K_fm) return SANTA_ERR_NULL;
+  if (!problem_ok(problem)) return SANTA_ERR_SHAPE;
+  if (!supported(problem)) return SANTA_ERR_UNSUPPORTED;
+  if (problem->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
+  if (!aligned(K, 16) || !aligned(K_fm, 16)) return SANTA_ERR_ALIGN;
+  const hipError_t e = santa::launch_pack_feature_major(K, K_fm, problem->batch, problem->num_kv_heads,
+                                                        problem->max_n_k, problem->head_dim, (hipStream_t)stream);
+  return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
+int santa_workspace_error(const void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags) return SANTA_ERR_NULL;
+  if (hipMemcpyAsync(flags, workspace, sizeof(uint32_t), hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+    return SANTA_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SANTA_ERR_HIP;
+  return SANTA_OK;
+}
+
+const char* santa_status_string(int status) {
+  switch (status) {
+    case SANTA_OK: return "SANTA_OK";
+    case SANTA_ERR_NULL: return "SANTA_ERR_NULL: a required pointer is NULL";
+    case SANTA_ERR_SHAPE: return "SANTA_ERR_SHAPE: inconsistent or out-of-range sizes";
+    case SANTA_ERR_UNSUPPORTED: return "SANTA_ERR_UNSUPPORTED: head_dim, group size or cache length not supported";
+    case SANTA_ERR_ALIGN: return "SANTA_ERR_ALIGN: misaligned pointer";
+    case SANTA_ERR_WORKSPACE: return "SANTA_ERR_WORKSPACE: workspace missing or too small";
+    case SANTA_ERR_HIP: return "SANTA_ERR_HIP: HIP runtime or launch failure";
+    case SANTA_ERR_MODE: return "SANTA_ERR_MODE: unknown sampling mode";
+    default: return "unknown santa status";
+  }
+}
+
+int32_t santa_abi_version(void) { return SANTA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+"""ctypes binding of libsanta (argument marshalling only).
+
+Every function here has the name of a C entry point in include/santa.h and
+does nothing but check tensor dtypes/shapes/devices, pass ``data_ptr()``
+values, sizes and the current HIP stream, and turn a non-zero status into an
+exception.  All computation runs in the library's HIP kernels; there is no
+fallback path.  PyTorch is used for device memory and streams only.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanta.so")
+
+IID, STRATIFIED, SYSTEMATIC = 0, 1, 2
+MODES = {"iid": IID, "stratified": STRATIFIED, "systematic": SYSTEMATIC}
+MAX_S = 1024
+ERR_SPIN_TIMEOUT = 1
+
+
+class SantaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_n_k", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def library():
+    """Load libsanta.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libsanta.so is not built; run `python -m stochastic_sparse_decode_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Problem)
+    vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    lib.santa_workspace_bytes.argtypes = [P]
+    lib.santa_workspace_bytes.restype = sz
+    lib.santa_decode.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, sz, vp]
+    lib.santa_decode.restype = ctypes.c_int
+    lib.santa_dense_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.santa_dense_decode.restype = ctypes.c_int
+    lib.santa_bernoulli_qk.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, vp, sz, vp]
+    lib.santa_bernoulli_qk.restype = ctypes.c_int
+    lib.santa_pack_k_feature_major.argtypes = [P, vp, vp, vp]
+    lib.santa_pack_k_feature_major.restype = ctypes.c_int
+    lib.santa_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    lib.santa_workspace_error.restype = ctypes.c_int
+    lib.santa_status_string.argtypes = [ctypes.c_int]
+    lib.santa_status_string.restype = ctypes.c_char_p
+    lib.santa_abi_version.argtypes = []
+    lib.santa_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return library().santa_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise SantaError(status, where)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def problem(q, K, scale):
+    """santa_problem for q (B, H_q, d) and K (B, H_kv, max_n_k, d)."""
+    B, Hq, d = q.shape
+    return Problem(B, Hq, K.shape[1], d, K.shape[2], float(scale))
+
+
+def problem_fm(q, K_fm, scale):
+    """santa_problem for q and a feature-major K (B, H_kv, max_n_k/64, d, 64)."""
+    B, Hq, d = q.shape
+    return Problem(B, Hq, K_fm.shape[1], d, K_fm.shape[2] * K_fm.shape[4], float(scale))
+
+
+def workspace_bytes(prob):
+    return int(library().santa_workspace_bytes(ctypes.byref(prob)))
+
+
+def new_workspace(prob, device):
+    """Zero-filled workspace tensor of santa_workspace_bytes(prob) bytes."""
+    n = workspace_bytes(prob)
+    if n == 0:
+        raise SantaError(2, "santa_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _expect(t, name, dtype, device, ndim=None):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+
+
+def santa_decode(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
+                 workspace=None, stream=None):
+    """SANTA decode step; returns ``out`` (B, H_q, d) fp32.
+
+    q (B, H_q, d), K and V (B, H_kv, max_n_k, d): contiguous fp16 on one GPU;
+    n_k (B,) int32 on the same GPU.  ``indices`` (B, H_q, S) int32 and
+    ``scores`` (B, H_q, max_n_k) fp32, if given, receive the sampled indices
+    and the scores.  ``workspace``: from ``new_workspace`` (allocated here if
+    None).
+    """
+    dev = q.device
+    for t, nm in ((q, "q"), (K, "K"), (V, "V")):
+        _expect(t, nm, torch.float16, dev)
+    _expect(n_k, "n_k", torch.int32, dev, 1)
+    prob = problem(q, K, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.float32, dev)
+    if indices is not None:
+        _expect(indices, "indices", torch.int32, dev)
+    if scores is not None:
+        _expect(scores, "scores", torch.float32, dev)
+    if workspace is None:
+        workspace = new_workspace(prob, dev)
+    mode = MODES.get(mode, mode)
+    st = library().santa_decode(ctypes.byref(prob), _ptr(q), _ptr(K), _ptr(V), _ptr(n_k), int(S), int(mode),
+                                int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "santa_decode")
+    return out
+
+
+def santa_dense_decode(q, K, V, n_k, scale, out=None, workspace=None, stream=None):
+    """Exact split-K decode attention; returns ``out`` (B, H_q, d) fp32."""
+    dev = q.device
+    for t, nm in ((q, "q"), (K, "K"), (V, "V")):
+        _expect(t, nm, torch.float16, dev)
+    _expect(n_k, "n_k", torch.int32, dev, 1)
+    prob = problem(q, K, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.float32, dev)
+    if workspace is None:
+        workspace = new_workspace(prob, dev)
+    st = library().santa_dense_decode(ctypes.byref(prob), _ptr(q), _ptr(K), _ptr(V), _ptr(n_k), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "santa_dense_decode")
+    return out
+
+
+def santa_pack_k_feature_major(K, K_fm=None, stream=None):
+    """Feature-major copy of K: (B, H_kv, max_n_k/64, d, 64) fp16."""
+    B, Hkv, n, d = K.shape
+    _expect(K, "K", torch.float16, K.device, 4)
+    if K_fm is None:
+        K_fm = torch.empty((B, Hkv, n // 64, d, 64), dtype=torch.float16, device=K.device)
+    prob = Problem(B, Hkv, Hkv, d, n, 1.0)
+    st = library().santa_pack_k_feature_major(ctypes.byref(prob), _ptr(K), _ptr(K_fm), _stream(stream))
+    _check(st, "santa_pack_k_feature_major")
+    return K_fm
+
+
+def santa_bernoulli_qk(q, K_fm, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
+                       kept=None, workspace=None, stream=None):
+    """Bernoulli qK^T step + SANTA value stage; returns ``out`` (B, H_q, d) fp32."""
+    dev = q.device
+    for t, nm in ((q, "q"), (K_fm, "K_fm"), (V, "V")):
+        _expect(t, nm, torch.float16, dev)
+    _expect(n_k, "n_k", torch.int32, dev, 1)
+    prob = problem_fm(q, K_fm, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    if indices is not None:
+        _expect(indices, "indices", torch.int32, dev)
+    if scores is not None:
+        _expect(scores, "scores", torch.float32, dev)
+    if kept is not None:
+        _expect(kept, "kept", torch.uint8, dev)
+    if workspace is None:
+        workspace = new_workspace(prob, dev)
+    mode = MODES.get(mode, mode)
+    st = library().santa_bernoulli_qk(ctypes.byref(prob), _ptr(q), _ptr(K_fm), _ptr(V), _ptr(n_k), int(S),
+                                      int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
+                                      _ptr(scores), _ptr(kept), _ptr(workspace), workspace.numel(),
+                                      _stream(stream))
+    _check(st, "santa_bernoulli_qk")
+    return out
+
+
+def santa_workspace_error(workspace, stream=None):
+    """Device error bits of a workspace (synchronises the stream)."""
+    flags = ctypes.c_uint32(0)
+    _check(library().santa_workspace_error(_ptr(workspace), ctypes.byref(flags), _stream(stream)),
+           "santa_workspace_error")
+    return flags.value
+
+
+def santa_abi_version():
+    return int(library().santa_abi_version())

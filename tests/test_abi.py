@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports what include/santa.h declares, and rejects
+bad arguments on the host before any HIP call (runs without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from stochastic_sparse_decode_amd import santa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "santa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(santa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return santa.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert santa.santa_abi_version() == 1
+    for code in range(8):
+        assert santa.status_string(code).startswith("SANTA_")
+    assert "unknown" in santa.status_string(99)
+
+
+def _prob(**kw):
+    p = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_n_k=32768, scale=0.125)
+    p.update(kw)
+    return santa.Problem(**p)
+
+
+def test_workspace_bytes(lib):
+    n = santa.workspace_bytes(_prob())
+    # 8 groups x 32 splits x 4 heads x (128 + 2) floats of partials at least
+    assert n >= 8 * 32 * 4 * 130 * 4
+    assert santa.workspace_bytes(_prob(num_q_heads=30)) == 0  # not a multiple of H_kv
+    assert santa.workspace_bytes(_prob(batch=0)) == 0
+    assert santa.workspace_bytes(_prob(scale=float("inf"))) == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its host checks
+
+
+def _decode(lib, prob, S=128, mode=2, q=FAKE, K=FAKE, V=FAKE, nk=FAKE, out=FAKE, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = santa.workspace_bytes(prob) if santa.workspace_bytes(prob) else 1 << 30
+    vp = ctypes.c_void_p
+    return lib.santa_decode(ctypes.byref(prob), vp(q), vp(K), vp(V), vp(nk), S, mode, 0, vp(out), None, None,
+                            vp(ws), ws_bytes, None)
+
+
+def test_host_checks_return_status_without_touching_the_gpu(lib):
+    p = _prob()
+    assert lib.santa_decode(None, None, None, None, None, 1, 2, 0, None, None, None, None, 0, None) == 1
+    assert _decode(lib, p, q=0) == 1                       # NULL q
+    assert _decode(lib, _prob(num_q_heads=30)) == 2        # H_q % H_kv
+    assert _decode(lib, _prob(head_dim=96)) == 3           # unsupported d
+    assert _decode(lib, _prob(num_q_heads=24, num_kv_heads=8)) == 3  # G = 3
+    assert _decode(lib, p, K=FAKE + 8) == 4                # misaligned K
+    assert _decode(lib, p, ws_bytes=16) == 5               # workspace too small
+    assert _decode(lib, p, ws=0) == 5
+    assert _decode(lib, p, S=0) == 2
+    assert _decode(lib, p, S=santa.MAX_S + 1) == 2
+    assert _decode(lib, p, mode=3) == 7
+    vp = ctypes.c_void_p
+    # Bernoulli needs max_n_k % 64 == 0
+    pb = _prob(max_n_k=1000)
+    assert lib.santa_bernoulli_qk(ctypes.byref(pb), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 8, 2, 0, vp(FAKE),
+                                  None, None, None, vp(FAKE), santa.workspace_bytes(pb), None) == 2
+    assert lib.santa_pack_k_feature_major(ctypes.byref(pb), vp(FAKE), vp(FAKE), None) == 2
+    assert lib.santa_dense_decode(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(0), vp(FAKE),
+                                  santa.workspace_bytes(p), None) == 1
+    assert lib.santa_workspace_error(None, None, None) == 1
+
+
+def test_binding_has_no_fallback(tmp_path, monkeypatch):
+    monkeypatch.setattr(santa, "_lib", None)
+    monkeypatch.setattr(santa, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        santa.library()

@@ -1,0 +1,82 @@
+"""GPU parity of santa_bernoulli_qk and of the feature-major packing kernel."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import santa as O
+from stochastic_sparse_decode_amd import santa
+from stochastic_sparse_decode_amd import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def run_bernoulli(wl, S, mode, seed):
+    q, K, V, nk = P.to_dev(wl)
+    K_fm = santa.santa_pack_k_feature_major(K)
+    B, Hq = wl.B, wl.Hq
+    idx = torch.full((B, Hq, S), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Hq, wl.max_n_k), float("nan"), dtype=torch.float32, device="cuda")
+    kept = torch.full((B, Hq, wl.d), 7, dtype=torch.uint8, device="cuda")
+    ws = santa.new_workspace(santa.problem(q, K, wl.scale), q.device)
+    out = santa.santa_bernoulli_qk(q, K_fm, V, nk, S, mode, seed, wl.scale, indices=idx, scores=sc, kept=kept,
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    assert santa.santa_workspace_error(ws) == 0
+    return out.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy(), kept.cpu().numpy().astype(bool)
+
+
+def test_pack_feature_major_is_exact_relayout():
+    wl = W.random_case(2, 4, 2, 128, [256, 192], max_n_k=256, seed=1)
+    K = torch.from_numpy(wl.K).cuda()
+    got = santa.santa_pack_k_feature_major(K).cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), W.feature_major(wl.K).view(np.uint16))
+    wl = W.random_case(1, 2, 1, 64, [128], seed=2)
+    got = santa.santa_pack_k_feature_major(torch.from_numpy(wl.K).cuda()).cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), W.feature_major(wl.K).view(np.uint16))
+
+
+CASES = [
+    ("gqa4", lambda: W.random_case(2, 8, 2, 128, [4096, 2500], max_n_k=4096, seed=11)),
+    ("d64_g1", lambda: W.random_case(1, 2, 2, 64, [1000], max_n_k=1024, seed=12)),
+    ("g8", lambda: W.random_case(1, 16, 2, 128, [3000], max_n_k=3008, seed=13)),
+    ("bernoulli_n8192", lambda: W.bernoulli(B=2, n_k=8192, seed=1004)),
+]
+
+
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_bernoulli_parity(name, make, mode):
+    wl = make()
+    S, seed = 128, 21 + mode
+    print("[bernoulli] %s mode=%d B=%d Hq=%d Hkv=%d d=%d n_k=%s" % (name, mode, wl.B, wl.Hq, wl.Hkv, wl.d,
+                                                                    list(wl.n_k)), flush=True)
+    out_g, idx_g, sc_g, kept_g = run_bernoulli(wl, S, mode, seed)
+    out_o, idx_o, kept_o, det = O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, seed, wl.scale,
+                                                   return_detail=True)
+    assert np.array_equal(kept_g, kept_o)  # exact fp64 decision on both sides
+    flips = set()
+    rep = P.compare_indices(idx_g, idx_o, det, P.BAND, flips)
+    print("   %s" % rep, flush=True)
+    assert rep.bad == 0
+    est = P.oracle_estimate_from_indices(wl.V, idx_g, wl.n_k, wl.Hq, S)
+    assert np.abs(out_g - est).max() <= P.OUT_TOL
+    # scores of the ternary query
+    q_t, _, _ = O.bernoulli_queries(wl.q, wl.Hkv, seed)
+    s_o = O.all_scores(q_t, wl.K, wl.n_k, wl.scale)
+    m = ~np.isnan(s_o)
+    assert np.abs(sc_g[m] - s_o[m]).max() <= 1e-4 * max(1.0, np.abs(s_o[m]).max())
+
+
+def test_bernoulli_equal_magnitudes_match_plain_decode():
+    wl = W.random_case(1, 8, 2, 128, [2048], seed=14)
+    wl.q[:] = np.where(np.random.default_rng(3).random(wl.q.shape) < 0.5, -0.5, 0.5).astype(np.float16)
+    out_b, idx_b, _, kept = run_bernoulli(wl, 64, 2, 4)
+    assert kept.all()
+    q, K, V, nk = P.to_dev(wl)
+    idx = torch.empty((1, 8, 64), dtype=torch.int32, device="cuda")
+    out = santa.santa_decode(q, K, V, nk, 64, 2, 4, wl.scale, indices=idx)
+    torch.cuda.synchronize()
+    # same scores up to fp32 summation order, so indices agree except at boundaries
+    assert (idx.cpu().numpy() != idx_b).mean() < 0.01

@@ -1,0 +1,224 @@
+"""GPU parity of santa_decode against the fp64 oracle (through the C-ABI).
+
+Index parity: bit-exact except for points within 1e-5 of every CDF value that
+separates the GPU's and the oracle's choice (counted and printed); a second
+check re-runs the oracle's sampling steps on the GPU's own fp32 scores, where
+the excused band shrinks to 1e-6.  Output parity: max-abs 2e-3 against the
+oracle's estimate on the GPU's index list, and against the oracle's own output
+for every head without a flip.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import santa as O
+from stochastic_sparse_decode_amd import santa
+from stochastic_sparse_decode_amd import workloads as W
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(wl, S, mode, seed, workspace=None, with_scores=True):
+    q, K, V, nk = P.to_dev(wl)
+    B, Hq = wl.B, wl.Hq
+    idx = torch.full((B, Hq, S), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Hq, wl.max_n_k), float("nan"), dtype=torch.float32, device="cuda") if with_scores else None
+    ws = workspace if workspace is not None else santa.new_workspace(santa.problem(q, K, wl.scale), q.device)
+    out = santa.santa_decode(q, K, V, nk, S, mode, seed, wl.scale, indices=idx, scores=sc, workspace=ws)
+    torch.cuda.synchronize()
+    assert santa.santa_workspace_error(ws) == 0
+    return out.cpu().numpy(), idx.cpu().numpy(), (sc.cpu().numpy() if sc is not None else None)
+
+
+def check_parity(wl, S, mode, seed, label=""):
+    print("[decode] %s S=%d mode=%d seed=%d B=%d Hq=%d Hkv=%d d=%d n_k=%s" % (
+        label, S, mode, seed, wl.B, wl.Hq, wl.Hkv, wl.d, list(wl.n_k)[:4]), flush=True)
+    out_g, idx_g, sc_g = run_decode(wl, S, mode, seed)
+    out_o, idx_o, det = O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, seed, wl.scale, return_detail=True)
+    valid = (wl.n_k >= 1) & (wl.n_k <= wl.max_n_k)
+    # index lists are ascending and inside [0, n_k)
+    for b in np.nonzero(valid)[0]:
+        assert np.all(np.diff(idx_g[b], axis=-1) >= 0)
+        assert idx_g[b].min() >= 0 and idx_g[b].max() < wl.n_k[b]
+    flips = set()
+    rep = P.compare_indices(idx_g, idx_o, det, P.BAND, flips)
+    _, idx_s, det_s = O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, seed, wl.scale,
+                                     score_override=sc_g, return_detail=True)
+    rep2 = P.compare_indices(idx_g, idx_s, det_s, P.BAND_SAME_SCORES)
+    print("   vs oracle: %s | on GPU scores: %s" % (rep, rep2), flush=True)
+    assert rep.bad == 0, rep
+    assert rep2.bad == 0, rep2
+    est = P.oracle_estimate_from_indices(wl.V, idx_g, wl.n_k, wl.Hq, S)
+    err = np.abs(out_g[valid] - est[valid]).max()
+    assert err <= P.OUT_TOL, err
+    for b in np.nonzero(valid)[0]:
+        for h in range(wl.Hq):
+            if (b, h) not in flips:
+                assert np.abs(out_g[b, h] - out_o[b, h]).max() <= P.OUT_TOL
+    # score stage against the oracle's fp64 scores
+    s_o = O.all_scores(wl.q, wl.K, wl.n_k, wl.scale)
+    m = ~np.isnan(s_o)
+    assert np.abs(sc_g[m] - s_o[m]).max() <= 1e-4 * max(1.0, np.abs(s_o[m]).max())
+    return rep
+
+
+# --------------------------------------------------------------------------
+# tiny single-head config (d=64, n_k=1024, 4 planted keys, scale folded in q)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [2, 1, 0])
+@pytest.mark.parametrize("S", [16, 1, 1000])
+def test_tiny_parity(mode, S):
+    wl = W.tiny()
+    for seed in range(3):
+        check_parity(wl, S, mode, seed, "tiny")
+
+
+def test_tiny_systematic_S_equals_n_uniform_is_mean_exactly():
+    wl = W.tiny()
+    wl.q[:] = 0
+    out, idx, _ = run_decode(wl, 1024, 2, 7)
+    assert np.array_equal(idx[0, 0], np.arange(1024))
+    ref = wl.V[0, 0].astype(np.float64).mean(axis=0)
+    assert np.abs(out[0, 0] - ref).max() < 1e-6
+
+
+# --------------------------------------------------------------------------
+# GQA packing, head dims, ragged tails, padding poisoned with NaN
+# --------------------------------------------------------------------------
+
+SMALL = [
+    # B, Hq, Hkv, d, n_k, max_n_k
+    (2, 8, 2, 128, [3000, 1500], 3100),
+    (1, 4, 4, 128, [2049], 2049),
+    (2, 4, 2, 64, [1024, 1], 1024),
+    (1, 16, 2, 128, [4500], 4500),
+    (3, 8, 4, 64, [777, 2048, 1025], 2100),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d" % c[:4])
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_small_shapes_parity(case, mode):
+    B, Hq, Hkv, d, n_k, max_n_k = case
+    wl = W.random_case(B, Hq, Hkv, d, n_k, max_n_k=max_n_k, seed=31 + B + d, planted=True,
+                       pad_value=np.float16(np.nan))
+    for S in (8, 128):
+        check_parity(wl, S, mode, 100 + S, "small")
+
+
+def test_invalid_sequence_lengths():
+    wl = W.random_case(3, 8, 2, 128, [0, 1200, 5000], max_n_k=2048, seed=5)
+    out, idx, _ = run_decode(wl, 16, 2, 3)
+    assert np.isnan(out[0]).all() and (idx[0] == -1).all()
+    assert np.isnan(out[2]).all() and (idx[2] == -1).all()
+    assert not np.isnan(out[1]).any()
+    check_parity(wl, 16, 2, 3, "invalid-n_k")
+
+
+# --------------------------------------------------------------------------
+# Llama-3.1-8B decode layer at 32k (32 q heads, 8 KV heads, d=128)
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def llama32k():
+    return W.llama(B=1, n_k=32768, seed=1001)
+
+
+@pytest.mark.parametrize("mode", [2, 1, 0])
+@pytest.mark.parametrize("S", [32, 64, 128, 256])
+def test_llama32k_parity(llama32k, mode, S):
+    check_parity(llama32k, S, mode, 1 + S, "llama32k")
+
+
+def test_llama32k_max_S(llama32k):
+    check_parity(llama32k, 1024, 0, 9, "llama32k")
+
+
+def test_determinism_and_workspace_reuse(llama32k):
+    wl = llama32k
+    q, K, V, nk = P.to_dev(wl)
+    big = santa.problem(q, K, wl.scale)
+    ws = santa.new_workspace(big, q.device)
+    a = run_decode(wl, 128, 2, 11, workspace=ws)
+    small = W.random_case(2, 8, 2, 128, [3000, 1500], max_n_k=3100, seed=2)
+    run_decode(small, 64, 1, 5, workspace=ws)  # smaller problem on the same workspace
+    b = run_decode(wl, 128, 2, 11, workspace=ws)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert santa.santa_workspace_error(ws) == 0
+
+
+# --------------------------------------------------------------------------
+# batched long context (B=16, n_k uniform in [8192, 32768]) and the context
+# sweep: full-size launches, oracle on sampled heads
+# --------------------------------------------------------------------------
+
+def check_sampled_heads(wl, S, mode, seed, heads):
+    out_g, idx_g, sc_g = run_decode(wl, S, mode, seed)
+    G = wl.Hq // wl.Hkv
+    rep = P.IndexReport()
+    for (b, h) in heads:
+        n = int(wl.n_k[b])
+        s = O.head_scores(wl.q[b, h].astype(np.float64), wl.K[b, h // G, :n].astype(np.float64), wl.scale)
+        _, _, F = O.distribution(s)
+        t = O.points(mode, S, seed, b * wl.Hq + h)
+        io = O.inverse_cdf(F, t)
+        sub = P.compare_indices(idx_g[b:b + 1, h:h + 1], io[None, None, :], {"t": {(0, 0): t}, "F": {(0, 0): F}},
+                                P.BAND)
+        for f in ("points", "exact", "excused", "bad", "heads_with_flips"):
+            setattr(rep, f, getattr(rep, f) + getattr(sub, f))
+        est = O.gather_average(wl.V[b, h // G, :n].astype(np.float64), idx_g[b, h], S)
+        assert np.abs(out_g[b, h] - est).max() <= P.OUT_TOL
+        assert np.abs(sc_g[b, h, :n] - s).max() <= 1e-4 * max(1.0, np.abs(s).max())
+    print("   sampled heads: %s" % rep, flush=True)
+    assert rep.bad == 0, rep
+    # every head: ascending, in range, finite
+    for b in range(wl.B):
+        assert np.all(np.diff(idx_g[b], axis=-1) >= 0) and idx_g[b].min() >= 0 and idx_g[b].max() < wl.n_k[b]
+    assert np.isfinite(out_g).all()
+
+
+def test_batched_long_context_sampled():
+    wl = W.llama(B=16, n_k_range=(8192, 32768), seed=1002)
+    rng = np.random.default_rng(0)
+    heads = [(int(b), int(rng.integers(0, 32))) for b in range(16)]
+    print("[decode] batched B=16 n_k=%s" % list(wl.n_k), flush=True)
+    check_sampled_heads(wl, 128, 2, 77, heads)
+
+
+@pytest.mark.parametrize("n_k,r", [(4096, 0.5), (16384, 4.0), (65536, 1.0), (131072, 1.0)])
+def test_context_sweep_sampled(n_k, r):
+    wl = W.sweep(B=4, n_k=n_k, r=r, seed=1003)
+    heads = [(0, 0), (1, 7), (2, 19), (3, 31)]
+    for mode in (1, 2):
+        print("[decode] sweep n_k=%d r=%g mode=%d" % (n_k, r, mode), flush=True)
+        check_sampled_heads(wl, 128, mode, 5, heads)
+
+
+# --------------------------------------------------------------------------
+# statistics on the GPU: mean over seeds within 3 sigma of dense attention
+# --------------------------------------------------------------------------
+
+def test_gpu_mean_over_seeds_matches_dense():
+    from oracle import moments as M
+    wl = W.tiny()
+    q, K, V, nk = P.to_dev(wl)
+    ws = santa.new_workspace(santa.problem(q, K, wl.scale), q.device)
+    s = O.head_scores(wl.q[0, 0].astype(np.float64), wl.K[0, 0].astype(np.float64), wl.scale)
+    _, _, F = O.distribution(s)
+    Vh = wl.V[0, 0].astype(np.float64)
+    dense = O.dense_head(s, Vh)
+    N, S = 4000, 16
+    for mode in (0, 1, 2):
+        outs = torch.empty((N, wl.d), dtype=torch.float32, device="cuda")
+        for seed in range(N):
+            santa.santa_decode(q, K, V, nk, S, mode, seed, wl.scale, out=outs[seed:seed + 1].view(1, 1, wl.d),
+                               workspace=ws)
+        torch.cuda.synchronize()
+        est = outs.cpu().numpy().astype(np.float64)
+        _, var = M.moments(mode, F, Vh, S)
+        z = (est.mean(axis=0) - dense) / np.sqrt(var / N)
+        print("   mode %d: max |z| = %.2f" % (mode, np.abs(z).max()), flush=True)
+        assert (np.abs(z) > 3).sum() <= 2 and np.abs(z).max() < 5
