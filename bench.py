@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--S", type=int, default=128)
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of distinct KV copies to rotate over")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of a HIP graph")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -66,17 +67,37 @@ def algorithmic_bytes(wl, S, dense=False):
     return k_bytes + wl.B * wl.Hkv * S * wl.d * 2
 
 
-def timed(fn, sets, steps, warmup):
+def timed(fn, sets, steps, warmup, graph=True):
+    """ms per step over exactly `steps` steps, rotating over the KV copies.
+
+    With graph=True the `steps` launches are captured once into a HIP graph
+    and the timed region is one replay, so host-side launch overhead (Python,
+    ctypes) is not part of the measurement; the events are recorded on the
+    stream the kernels run on.  With graph=False every step is launched from
+    Python.
+    """
     import torch
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        fn(sets[i % len(sets)])
-    stop.record(stream)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(sets[i % len(sets)])
+        g.replay()  # untimed replay
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start.record(stream)
+        g.replay()
+        stop.record(stream)
+    else:
+        stream = torch.cuda.current_stream()
+        start.record(stream)
+        for i in range(steps):
+            fn(sets[i % len(sets)])
+        stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps  # ms per step (= per launch: one launch per step)
 
@@ -143,15 +164,21 @@ def main():
     else:
         step = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
                                              workspace=ws)
-    ms = timed(step, sets, args.steps, args.warmup)
+    ms = timed(step, sets, args.steps, args.warmup, graph=not args.eager)
     assert santa.santa_workspace_error(ws) == 0
+    # the graph's last step must equal an eager launch on the same KV copy
+    last = out.clone()
+    step(sets[(args.steps - 1) % len(sets)])
+    torch.cuda.synchronize()
+    assert torch.equal(last, out), "graph replay differs from eager launch"
+    eager_ms = timed(step, sets, min(args.steps, 50), 2, graph=False) if not args.eager else ms
     nbytes = algorithmic_bytes(wl, S)
     gbs = nbytes / (ms * 1e-3) / 1e9
 
     dense_ms = None
     if not args.no_dense and args.workload != "bernoulli":
         dstep = lambda kv: santa.santa_dense_decode(q, kv[0], kv[1], nk, wl.scale, out=out, workspace=ws)  # noqa
-        dense_ms = timed(dstep, sets, args.steps, args.warmup)
+        dense_ms = timed(dstep, sets, args.steps, args.warmup, graph=not args.eager)
 
     res = {
         "metric": "decode-attention us/step + effective HBM TB/s (% peak), Llama-3.1-8B shape @32k",
@@ -171,6 +198,8 @@ def main():
         "config": {"workload": desc, "mode": args.mode, "S": S, "global_batch": wl.B, "seq_len": int(wl.n_k.max()),
                    "parallelism": "none (1 GPU)"},
         "algorithmic_bytes_per_step": nbytes,
+        "timing": "HIP graph of %d steps, one timed replay" % args.steps if not args.eager else "eager launches",
+        "eager_us_per_step": eager_ms * 1000.0,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None},
     }

@@ -41,10 +41,12 @@
  *  kernels are enqueued on `stream` (a hipStream_t; NULL = default stream) and
  *  the caller keeps all buffers alive until the stream has completed them.
  *
- *  Workspace: a device buffer of at least santa_workspace_bytes(problem)
- *  bytes, zero-filled by the caller once before first use.  Kernels leave
- *  their counters at zero when they finish, so the buffer can be reused by
- *  later calls with the same or a smaller problem.  Calls that share one
+ *  Workspace: a 256-byte aligned device buffer of at least
+ *  santa_workspace_bytes(problem) bytes, zero-filled by the caller once
+ *  before first use.  The first 256 bytes hold the error bits; partial
+ *  results follow them; the arrival flags sit at the end of the buffer.
+ *  Kernels leave every flag at zero when they finish, so one buffer serves
+ *  any sequence of calls whose problems each fit in it.  Calls that share one
  *  workspace must not run concurrently.  After a call that reported a device
  *  error (santa_workspace_error != 0) the workspace must be zero-filled again.
  *
@@ -81,7 +83,7 @@ typedef enum santa_status {
   SANTA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes, S, scale */
   SANTA_ERR_UNSUPPORTED = 3, /* head_dim, group size or n_k range not built */
   SANTA_ERR_ALIGN = 4,       /* q/K/V/K_fm not 16-byte or out/indices/scores/n_k not 4-byte aligned */
-  SANTA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than santa_workspace_bytes */
+  SANTA_ERR_WORKSPACE = 5,   /* workspace NULL, not 256-byte aligned, or smaller than santa_workspace_bytes */
   SANTA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
   SANTA_ERR_MODE = 7         /* unknown sampling mode */
 } santa_status;

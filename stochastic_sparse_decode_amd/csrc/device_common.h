@@ -147,6 +147,33 @@ __device__ __forceinline__ void row_reduce_scatter(float* v, int lane) {
 // ---------------------------------------------------------------------------
 // Wave-level reductions and scans (64 lanes).
 // ---------------------------------------------------------------------------
+// DPP move of a 64-bit value (two 32-bit halves); lanes without a source, or
+// outside ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, ROW_MASK, 0xF, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, ROW_MASK, 0xF, true);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive prefix sum over the wave: shifts by 1, 2, 4, 8 inside each row
+// of 16 lanes, then the last lane of row 0 is added to row 1 (and of row 2 to
+// row 3), then the last lane of row 1 to rows 2 and 3.  Integer, so exact.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  v += dpp_u64<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_u64<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_u64<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_u64<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_u64<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_u64<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_bcast_u64(uint64_t v, int lane_src) {
+  const uint32_t lo = __shfl((int)(uint32_t)v, lane_src, 64);
+  const uint32_t hi = __shfl((int)(uint32_t)(v >> 32), lane_src, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ float wave_max_masked(float x, int first_mask) {
   for (int m = first_mask; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
   return x;
@@ -171,21 +198,43 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Agent-scope hand-offs between workgroups.
+// Hand-offs between workgroups.
+//
+// On gfx950 an agent-scope release or acquire fence writes back or
+// invalidates the whole L2 of the XCD (the L2s of the 8 XCDs are not
+// coherent with each other for ordinary loads and stores), which costs
+// microseconds per fence.  Data exchanged between workgroups therefore never
+// goes through ordinary stores plus fences: it is written with device-scope
+// stores (sc1, written through to the device coherence point) and read with
+// device-scope loads (sc1, never served from a stale L2 line).  A producer
+// waits until its device-scope stores are acknowledged (s_waitcnt on all
+// outstanding memory operations) before it bumps the arrival counter with an
+// atomic; a consumer issues its device-scope loads only after it has seen the
+// counter value, so it reads what the producers wrote.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t load_acquire(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t load_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
+__device__ __forceinline__ void store_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_dev(const float2* p) {
+  const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float2*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(float2, v);
+}
+__device__ __forceinline__ void store_dev(float2* p, float2 v) {
+  __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave has issued has completed.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 }  // namespace santa

@@ -21,9 +21,8 @@ constexpr uint32_t kErrSpinTimeout = 1u;
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
-  uint32_t* bar_stats;  // [groups] arrivals of split statistics
-  uint32_t* bar_done;   // [groups] arrivals of split partial outputs
-  float2* stats;        // [groups][ns][G] (local max, local sum-exp)
+  uint32_t* bar_done;   // [groups] arrivals of split partial outputs, back to 0 at kernel end
+  float2* stats;        // [groups][ns][G] (split max, split mass); mass 0 = not yet published
   float* partial;       // [groups][ns][G][D + 2] partial outputs (+ m, l for dense)
 };
 

@@ -16,10 +16,6 @@ using santa::Workspace;
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-struct Layout {
-  size_t header, bar_stats, bar_done, stats, partial, total;
-};
-
 bool problem_ok(const santa_problem* p) {
   if (!p) return false;
   if (p->batch < 1 || p->num_kv_heads < 1 || p->num_q_heads < 1 || p->max_n_k < 1) return false;
@@ -39,29 +35,42 @@ bool supported(const santa_problem* p) {
   return (p->head_dim == 64 || p->head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
+// Workspace layout.  The header (error bits, work counter) sits at offset 0
+// and the partial outputs follow it; the flags that must read zero at the
+// start of a launch (arrival counters, statistics slots) sit at the END of
+// the caller's buffer.  Every launch leaves its flags at zero, and because
+// flags are placed against the end and data against the start, the data of
+// a smaller problem never lands on the flag words of a larger one that uses
+// the same buffer (and the other way round).
+struct Layout {
+  size_t partial_bytes, flag_bytes, total;
+};
+
 Layout layout_of(const santa_problem* p) {
   Layout L{};
   const size_t groups = (size_t)p->batch * p->num_kv_heads;
   const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
-  L.header = 0;
-  L.bar_stats = L.header + kAlign;
-  L.bar_done = L.bar_stats + round_up(groups * sizeof(uint32_t));
-  L.stats = L.bar_done + round_up(groups * sizeof(uint32_t));
-  L.partial = L.stats + round_up(groups * ns * G * sizeof(float2));
-  L.total = L.partial + round_up(groups * ns * G * (D + 2) * sizeof(float));
+  L.partial_bytes = round_up(groups * ns * G * (D + 2) * sizeof(float));
+  L.flag_bytes = round_up(groups * sizeof(uint32_t)) + round_up(groups * ns * G * sizeof(float2));
+  L.total = kAlign + L.partial_bytes + L.flag_bytes;
   return L;
 }
 
-Workspace carve(void* base, const Layout& L) {
+Workspace carve(void* base, size_t bytes, const santa_problem* p) {
   unsigned char* b = (unsigned char*)base;
+  const size_t groups = (size_t)p->batch * p->num_kv_heads;
+  const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
+  const size_t G = (size_t)group_size(p);
+  unsigned char* end = b + bytes / kAlign * kAlign;
+  unsigned char* done = end - round_up(groups * sizeof(uint32_t));
+  unsigned char* stats = done - round_up(groups * ns * G * sizeof(float2));
   Workspace w;
-  w.err = (uint32_t*)(b + L.header);
-  w.work_ctr = (uint32_t*)(b + L.header) + 1;
-  w.bar_stats = (uint32_t*)(b + L.bar_stats);
-  w.bar_done = (uint32_t*)(b + L.bar_done);
-  w.stats = (float2*)(b + L.stats);
-  w.partial = (float*)(b + L.partial);
+  w.err = (uint32_t*)b;
+  w.work_ctr = (uint32_t*)b + 1;
+  w.partial = (float*)(b + kAlign);
+  w.bar_done = (uint32_t*)done;
+  w.stats = (float2*)stats;
   return w;
 }
 
@@ -99,12 +108,12 @@ int common_checks(const santa_problem* p, const void* q, const void* K, const vo
   if (!supported(p)) return SANTA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 4) || !aligned(n_k, 4))
     return SANTA_ERR_ALIGN;
-  if (!ws || ws_bytes < layout_of(p).total || !aligned(ws, 16)) return SANTA_ERR_WORKSPACE;
+  if (!ws || ws_bytes / kAlign * kAlign < layout_of(p).total || !aligned(ws, kAlign)) return SANTA_ERR_WORKSPACE;
   return SANTA_OK;
 }
 
 DecodeParams base_params(const santa_problem* p, const void* q, const void* K, const void* V,
-                         const int32_t* n_k, float* out, void* ws) {
+                         const int32_t* n_k, float* out, void* ws, size_t ws_bytes) {
   DecodeParams d{};
   d.q = q;
   d.K = K;
@@ -120,7 +129,7 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
   d.scale = p->scale;
   d.ns = (p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   d.total_items = p->batch * p->num_kv_heads * d.ns;
-  d.ws = carve(ws, layout_of(p));
+  d.ws = carve(ws, ws_bytes, p);
   return d;
 }
 
@@ -143,7 +152,7 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   if (mode != SANTA_IID && mode != SANTA_STRATIFIED && mode != SANTA_SYSTEMATIC) return SANTA_ERR_MODE;
   if ((indices_out && !aligned(indices_out, 4)) || (scores_out && !aligned(scores_out, 4))) return SANTA_ERR_ALIGN;
   if (kind == santa::kOpBernoulli && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
-  DecodeParams d = base_params(p, q, K, V, n_k, out, ws);
+  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, ws_bytes);
   d.idx_out = indices_out;
   d.scores_out = scores_out;
   d.kept_out = kept_out;
@@ -184,7 +193,7 @@ int santa_dense_decode(const santa_problem* problem, const void* q, const void* 
                        const int32_t* n_k, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes);
   if (st != SANTA_OK) return st;
-  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace);
+  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, workspace_bytes);
   st = choose_grid(d, santa::kOpDense);
   if (st != SANTA_OK) return st;
   const hipError_t e = santa::launch_dense(d, (hipStream_t)stream);

@@ -55,7 +55,7 @@ struct Lds {
 struct Shared {
   float wmax[kWaves][8];
   float lsum[8];
-  double M[8], Z[8], Olo[8], Ohi[8], rs[8];
+  double Z[8], SZ[8], Olo[8], Ohi[8], rs[8], usys[8];
   int wcount[kWaves];
   int n_distinct;
   int last;
@@ -64,17 +64,6 @@ struct Shared {
   float A[8];
   int nu;
 };
-
-// Upper bound in an ascending fp32 array: first j in [0, len) with c[j] > tau,
-// or len - 1 if none (a point can overshoot the local total only by rounding).
-__device__ __forceinline__ int cdf_search(const float* c, int len, double tau) {
-  int lo = 0, hi = len;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((double)c[lidx(mid)] > tau) hi = mid; else lo = mid + 1;
-  }
-  return lo < len ? lo : len - 1;
-}
 
 // ---------------------------------------------------------------------------
 // Score stage, Bernoulli qK^T: the ternary query keeps feature i of head g
@@ -134,9 +123,9 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
   const int half = lane >> 5, t4 = (lane >> 3) & 3, ko = lane & 7;
   const int ti = w * 4 + t4;  // tile of this lane inside the split (16 tiles)
   const int tiles_per_head = p.max_n_k / kTile;
-  const _Float16* tb = (const _Float16*)p.K +
-                       ((size_t)(b * p.Hkv + hk) * tiles_per_head + (k0 / kTile) + ti) * (size_t)(D * kTile);
-  const bool tile_ok = ti * kTile < len;
+  // tiles past the sequence end re-read its last tile (results discarded)
+  const int tile = min(k0 / kTile + ti, (k0 + len - 1) / kTile);
+  const _Float16* tb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * tiles_per_head + tile) * (size_t)(D * kTile);
   const int nu = sh.nu;
   float acc[G][8];
 #pragma unroll
@@ -152,9 +141,10 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
 #pragma unroll
     for (int x = 0; x < UNR; ++x) {
       const int fi = 2 * (f0 + x) + half;
-      const bool ok = tile_ok && (f0 + x) < steps && fi < nu;
-      inf[x] = ok ? info[fi] : 0u;
-      kv[x] = ok ? load_nt((const uint4*)(tb + (size_t)(inf[x] >> 16) * kTile + ko * 8)) : make_uint4(0, 0, 0, 0);
+      const bool ok = fi < nu;
+      const uint32_t e = info[ok ? fi : 0];       // nu >= 1 here
+      inf[x] = ok ? e : (e & 0xffff0000u);          // past the list: keep nothing
+      kv[x] = load_nt((const uint4*)(tb + (size_t)(e >> 16) * kTile + ko * 8));
     }
 #pragma unroll
     for (int x = 0; x < UNR; ++x) {
@@ -180,14 +170,62 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
     for (int e = 0; e < 8; ++e) {
       const float tot = acc[g][e] + __shfl_xor(acc[g][e], 32, 64);
       const int row = ti * kTile + ko * 8 + e;
+      const float s = tot * sc;
       if (half == 0 && row < len) {
-        const float s = tot * sc;
         cdf[g * kPad + lidx(row)] = s;
         mx[g] = fmaxf(mx[g], s);
-        if (p.scores_out) p.scores_out[(size_t)(b * p.Hq + hk * G + g) * p.max_n_k + k0 + row] = s;
       }
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Sampling helpers.
+//
+// Masses are fixed-point integers in units of 2^-31 of a split's largest
+// weight: w = exp(s - m) in (0, 1] becomes q = trunc(w * 2^31), the local CDF
+// c_j = q_0 + ... + q_j is an exact integer (stored as an fp32 value, which
+// keeps it nondecreasing), and the split masses merged across the group are
+// integers too, so split offsets O_s are exact, nondecreasing and identical
+// in every workgroup.  In global units the right edge of key j of split s is
+// x_j = O_s + r_s c_j with r_s = exp(m_s - M); the edges are clamped to the
+// split's range [O_s, O_{s+1}], so the keys of all splits tile [0, Z)
+// without gaps or overlaps.  A point t selects the key whose interval holds
+// t Z (the inverse CDF, with the half-open convention x_{j-1} <= t Z < x_j).
+// ---------------------------------------------------------------------------
+constexpr float kFix = 2147483648.0f;  // 2^31
+
+struct PointSet {
+  int mode, S;
+  double SZ;           // S / Z
+  double u;            // systematic offset
+  const uint32_t* ub;  // stratified: 24-bit uniforms of the S strata
+};
+
+// Number of stratum points with (k + u_k) / S < x / Z (x in mass units).
+// Systematic: #{k : k + u < y} = ceil(y - u); stratified: all strata below
+// floor(y) plus stratum floor(y) when its uniform lies below y - floor(y).
+__device__ __forceinline__ int points_below(const PointSet& ps, double x) {
+  const double y = x * ps.SZ;
+  if (ps.mode == 2) {
+    const double v = ceil(y - ps.u);
+    return v <= 0.0 ? 0 : (v >= (double)ps.S ? ps.S : (int)v);
+  }
+  if (!(y > 0.0)) return 0;
+  const double m = floor(y);
+  if (m >= (double)ps.S) return ps.S;
+  const int mi = (int)m;
+  return mi + ((double)ps.ub[mi] * 0x1.0p-24 < y - m ? 1 : 0);
+}
+
+// First key j in [0, len) whose right edge O + r c_j exceeds tz, else len - 1.
+__device__ __forceinline__ int key_of(const float* c, int len, double O, double r, double tz) {
+  int lo = 0, hi = len;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (fma(r, (double)c[lidx(mid)], O) > tz) hi = mid; else lo = mid + 1;
+  }
+  return lo < len ? lo : len - 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -197,11 +235,11 @@ template <int D, int G, bool BERN>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G>;
-  float* cdf = (float*)smem;
-  uint32_t* cnt = (uint32_t*)(smem + L::cdf_bytes);
+  float* cdf = (float*)smem;                                   // [G][kPad] scores, then local CDF
+  uint32_t* cnt = (uint32_t*)(smem + L::cdf_bytes);             // [G][kSplit] points per key
   unsigned char* aux = smem + L::cdf_bytes + L::cnt_bytes;
-  uint32_t* uni = (uint32_t*)aux;   // [G][kMaxS] (i.i.d. rank, only with idx_out)
-  float* red = (float*)aux;         // [kWaves][G*D] (gather reduction)
+  uint32_t* uni = (uint32_t*)aux;   // [G][kMaxS] 24-bit uniforms (stratified, i.i.d.)
+  float* red = (float*)aux;         // [kWaves][G*D] gather reduction
   uint32_t* list = (uint32_t*)aux;  // [kSplit] distinct selected keys
   __shared__ Shared sh;
   __shared__ uint32_t binfo[128];   // Bernoulli kept-feature union
@@ -226,9 +264,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     } else if (s < nsg) {
       const int k0 = s * kSplit;
       const int len = min(kSplit, n - k0);
+      const bool is_last = (s == nsg - 1);
       float mx[G];
 
-      // ---- score stage -----------------------------------------------------
+      // ---- score stage: all keys of the split, G query heads ----------------
       if constexpr (BERN) {
         bernoulli_setup<D, G>(p, b, hk, p.kept_out != nullptr && s == 0, sh, binfo);
         score_bernoulli<D, G>(p, b, hk, k0, len, cdf, mx, sh, binfo);
@@ -241,25 +280,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         if (lane == 0) sh.wmax[w][g] = m;
       }
       __syncthreads();
+      if (p.scores_out) {
+        write_scores<G>(p, b, hk, k0, len, cdf);
+        __syncthreads();
+      }
 
-      // ---- local CDF: prefix sums of exp(s - local max), fp64 carries ------
+      // ---- local CDF in fixed point, one wave per head ----------------------
       for (int g = w; g < G; g += kWaves) {
         float m = sh.wmax[0][g];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[x][g]);
         float* cg = cdf + g * kPad;
-        double run[kPer];
-        double acc = 0.0;
+        uint64_t run[kPer];
+        uint64_t acc = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
           const int j = lane * kPer + i;
-          const float x = j < len ? expf(cg[lidx(j)] - m) : 0.f;
-          acc += (double)x;
+          const uint32_t q = j < len ? (uint32_t)(expf(cg[lidx(j)] - m) * kFix) : 0u;
+          acc += q;
           run[i] = acc;
         }
-        const double incl = wave_incl_scan_f64(acc, lane);
-        double excl = __shfl_up(incl, 1, 64);
-        if (lane == 0) excl = 0.0;
+        const uint64_t excl = wave_incl_scan_u64(acc) - acc;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
           const int j = lane * kPer + i;
@@ -269,125 +310,128 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             if (j == len - 1) sh.lsum[g] = cv;
           }
         }
-        if (lane == 0) sh.wmax[0][g] = m;  // keep the split max for publishing
+        if (lane == 0) sh.wmax[0][g] = m;
       }
       __syncthreads();
 
-      // ---- publish (local max, local sum) and arrive ------------------------
-      float2* st = p.ws.stats + (size_t)(group * p.ns + s) * G;
-      if (w == 0) {
-        if (lane < G) st[lane] = make_float2(sh.wmax[0][lane], sh.lsum[lane]);
-        __threadfence();
-        if (lane == 0) atomic_add_acq_rel(p.ws.bar_stats + group, 1u);
+      // ---- publish (split max, split mass); the slot doubles as the flag ----
+      float2* slots = p.ws.stats + (size_t)group * p.ns * G;  // [split][head]
+      if (tid < G) {
+        float l = sh.lsum[tid];
+        if (__float_as_uint(l) == 0u) l = -0.0f;  // never publish the all-zero pattern (NaN inputs)
+        store_dev(slots + s * G + tid, make_float2(sh.wmax[0][tid], l));
       }
-      // while the other splits finish: clear the per-key counts
-      for (int i = tid; i < G * kSplit; i += kThreads) cnt[i] = 0u;
-      const bool want_rank = p.idx_out != nullptr && p.mode == 0;
-      if (want_rank) {  // 24-bit uniforms of every point, for the sorted i.i.d. index list
-        for (int t = tid; t < G * ((S + 3) >> 2); t += kThreads) {
-          const int g = t / ((S + 3) >> 2), kb = t % ((S + 3) >> 2);
-          const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + g), kTagIid, (uint32_t)kb);
+
+      // while the other splits finish: uniforms of the points
+      if (p.mode != 2) {
+        const int nb = (S + 3) >> 2;
+        const uint32_t tag = p.mode == 1 ? kTagStratified : kTagIid;
+        for (int t = tid; t < G * nb; t += kThreads) {
+          const int g = t / nb, kb = t % nb;
+          const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + g), tag, (uint32_t)kb);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (kb * 4 + e < S) uni[g * kMaxS + kb * 4 + e] = uniform_bits(word_of(blk, e));
         }
-      }
-      if (tid == 0) {
-        uint32_t spins = 0;
-        while (load_acquire(p.ws.bar_stats + group) < (uint32_t)nsg) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins > kSpinLimit) {
-            atomicOr(p.ws.err, kErrSpinTimeout);
-            break;
-          }
-        }
+        if (p.mode == 0)
+          for (int i = tid; i < G * kSplit; i += kThreads) cnt[i] = 0u;
+      } else if (tid < G) {
+        sh.usys[tid] = uniform_f64(stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + tid), kTagSystematic, 0u).x);
       }
       __syncthreads();
-      fence_acquire();
 
-      // ---- merge split statistics (fp64, split order) ------------------------
-      const float2* gst = p.ws.stats + (size_t)group * p.ns * G;
+      // ---- wait for every split of the group, merge (one wave per head) -----
       for (int g = w; g < G; g += kWaves) {
-        float mloc = -INFINITY;
-        for (int x = lane; x < nsg; x += 64) mloc = fmaxf(mloc, gst[x * G + g].x);
-        const float M = wave_max_masked(mloc, 1);
-        double carry = 0.0;
-        for (int x0 = 0; x0 < nsg; x0 += 64) {
-          const int x = x0 + lane;
-          float r = 0.f;
-          double mass = 0.0;
-          if (x < nsg) {
-            const float2 v = gst[x * G + g];
-            r = expf(v.x - M);
-            mass = (double)v.y * (double)r;
+        float2 v0 = make_float2(-INFINITY, 1.f);
+        for (int c0 = 0; c0 < nsg; c0 += 64) {  // poll every chunk of 64 splits
+          const int x = c0 + lane;
+          uint32_t spins = 0;
+          while (true) {
+            const float2 v = x < nsg ? load_dev(slots + x * G + g) : make_float2(-INFINITY, 1.f);
+            if (c0 == 0) v0 = v;
+            if (__ballot(__float_as_uint(v.y) == 0u) == 0ull) break;  // published mass is never +0.0
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kSpinLimit) {
+              if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
+              break;
+            }
           }
-          const double incl = wave_incl_scan_f64(mass, lane) + carry;
-          double excl = __shfl_up(incl, 1, 64);
-          if (lane == 0) excl = carry;
+        }
+        float Mloc = -INFINITY;
+        for (int c0 = 0; c0 < nsg; c0 += 64) {
+          const int x = c0 + lane;
+          const float2 v = c0 == 0 ? v0 : (x < nsg ? load_dev(slots + x * G + g) : make_float2(-INFINITY, 1.f));
+          Mloc = fmaxf(Mloc, v.x);
+        }
+        const float M = wave_max_masked(Mloc, 1);
+        uint64_t carry = 0;
+        for (int c0 = 0; c0 < nsg; c0 += 64) {
+          const int x = c0 + lane;
+          float2 v = c0 == 0 ? v0 : (x < nsg ? load_dev(slots + x * G + g) : make_float2(-INFINITY, 0.f));
+          const float r = x < nsg ? expf(v.x - M) : 0.f;
+          const uint64_t Q = x < nsg ? (uint64_t)((double)v.y * (double)r) : 0ull;
+          const uint64_t incl = wave_incl_scan_u64(Q) + carry;
           if (x == s) {
-            sh.Olo[g] = excl;
-            sh.Ohi[g] = incl;
+            sh.Olo[g] = (double)(incl - Q);
+            sh.Ohi[g] = (double)incl;
             sh.rs[g] = (double)r;
           }
-          carry = __shfl(incl, 63, 64);
+          carry = wave_bcast_u64(incl, 63);
         }
         if (lane == 0) {
-          sh.M[g] = M;
-          sh.Z[g] = carry;
+          sh.Z[g] = (double)carry;
+          sh.SZ[g] = (double)S / (double)carry;
         }
       }
       __syncthreads();
 
-      // ---- stratum points in this split's probability range, CDF search ----
-      const bool is_last = (s == nsg - 1);
-      for (int g = 0; g < G; ++g) {
-        const double Z = sh.Z[g], Olo = sh.Olo[g], Ohi = sh.Ohi[g], rs = sh.rs[g];
-        const uint32_t row = (uint32_t)(b * p.Hq + h0 + g);
-        int k_lo = 0, k_hi = S - 1;
-        double u_sys = 0.0;
-        if (p.mode == 2) {
-          u_sys = uniform_f64(stream_block(p.seed, row, kTagSystematic, 0u).x);
-          k_lo = max(0, (int)ceil((double)S * (Olo / Z) - u_sys) - 1);
-          if (!is_last) k_hi = min(S - 1, (int)ceil((double)S * (Ohi / Z) - u_sys) + 1);
-        } else if (p.mode == 1) {
-          k_lo = max(0, (int)floor((double)S * (Olo / Z)) - 1);
-          if (!is_last) k_hi = min(S - 1, (int)ceil((double)S * (Ohi / Z)) + 1);
-        }
-        const uint32_t tag = p.mode == 1 ? kTagStratified : kTagIid;
-        const int kb_lo = k_lo >> 2, kb_hi = k_hi >> 2;
-        for (int kb = kb_lo + tid; kb <= kb_hi; kb += kThreads) {
-          uint4 blk = make_uint4(0, 0, 0, 0);
-          if (p.mode != 2) blk = stream_block(p.seed, row, tag, (uint32_t)kb);
+      // ---- points per key -----------------------------------------------------
+      constexpr int KPT = kSplit / kThreads;
+      if (p.mode != 0) {
+        // stratified / systematic: the count of key j is the number of points
+        // below its right edge minus the number below its left edge
+        for (int g = 0; g < G; ++g) {
+          const PointSet ps{p.mode, S, sh.SZ[g], sh.usys[g], uni + g * kMaxS};
+          const double O = sh.Olo[g], r = sh.rs[g];
+          const int Plo = points_below(ps, O);
+          const int Phi = is_last ? S : points_below(ps, sh.Ohi[g]);
+          const float* cg = cdf + g * kPad;
+          const int j0 = tid * KPT;
+          if (j0 >= len) continue;
+          int prev = j0 == 0 ? Plo : min(max(points_below(ps, fma(r, (double)cg[lidx(j0 - 1)], O)), Plo), Phi);
+          const size_t row = (size_t)(b * p.Hq + h0 + g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k = kb * 4 + e;
-            if (k < k_lo || k > k_hi) continue;
-            double t;
-            if (p.mode == 2) t = ((double)k + u_sys) / (double)S;
-            else if (p.mode == 1) t = ((double)k + uniform_f64(word_of(blk, e))) / (double)S;
-            else t = uniform_f64(word_of(blk, e));
-            const double tz = t * Z;
-            if (!(tz >= Olo && (is_last || tz < Ohi))) continue;
-            const int j = cdf_search(cdf + g * kPad, len, (tz - Olo) / rs);
-            atomicAdd(&cnt[g * kSplit + j], 1u);
-            if (p.idx_out) {
-              int pos = k;
-              if (p.mode == 0) {  // rank among the S uniforms, ties by stream index
-                const uint32_t mine = uniform_bits(word_of(blk, e));
-                const uint32_t* ug = uni + g * kMaxS;
-                int rk = 0;
-                for (int x = 0; x < S; ++x) rk += (ug[x] < mine) || (ug[x] == mine && x < k);
-                pos = rk;
-              }
-              p.idx_out[(size_t)row * S + pos] = k0 + j;
-            }
+          for (int x = 0; x < KPT; ++x) {
+            const int j = j0 + x;
+            if (j >= len) break;
+            const int up = j == len - 1 ? Phi : min(max(points_below(ps, fma(r, (double)cg[lidx(j)], O)), Plo), Phi);
+            cnt[g * kSplit + j] = (uint32_t)(up - prev);
+            if (p.idx_out)
+              for (int k = prev; k < up; ++k) p.idx_out[row * S + k] = k0 + j;
+            prev = up;
+          }
+        }
+      } else {
+        // i.i.d.: every point is tested against this split's range and
+        // searched in the local CDF
+        for (int pi = tid; pi < G * S; pi += kThreads) {
+          const int g = pi / S, k = pi % S;
+          const uint32_t ub = uni[g * kMaxS + k];
+          const double tz = (double)ub * 0x1.0p-24 * sh.Z[g];
+          if (tz < sh.Olo[g] || (!is_last && tz >= sh.Ohi[g])) continue;
+          const int j = key_of(cdf + g * kPad, len, sh.Olo[g], sh.rs[g], tz);
+          atomicAdd(&cnt[g * kSplit + j], 1u);
+          if (p.idx_out) {  // position in the sorted list: rank among the S uniforms, ties by stream index
+            const uint32_t* ug = uni + g * kMaxS;
+            int rk = 0;
+            for (int x = 0; x < S; ++x) rk += (ug[x] < ub) || (ug[x] == ub && x < k);
+            p.idx_out[(size_t)(b * p.Hq + h0 + g) * S + rk] = k0 + j;
           }
         }
       }
       __syncthreads();
 
       // ---- distinct selected keys, in key order ------------------------------
-      constexpr int KPT = kSplit / kThreads;
       int flags = 0, nf = 0;
 #pragma unroll
       for (int x = 0; x < KPT; ++x) {
@@ -456,26 +500,43 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         float v = red[i];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) v += red[x * G * D + i];
-        part[i] = v;
+        store_dev(part + i, v);
       }
-      __threadfence();
+      wait_memory();
       __syncthreads();
-      if (tid == 0) sh.last = atomic_add_acq_rel(p.ws.bar_done + group, 1u) == (uint32_t)(nsg - 1);
+      if (tid == 0) sh.last = atomic_add_dev(p.ws.bar_done + group, 1u) == (uint32_t)(nsg - 1);
       __syncthreads();
 
       // ---- last split of the group: add partials in split order -----------
       if (sh.last) {
-        fence_acquire();
         const float* gp = p.ws.partial + (size_t)group * p.ns * G * D;
-        for (int i = tid; i < G * D; i += kThreads) {
-          float v = 0.f;
-          for (int x = 0; x < nsg; ++x) v += gp[(size_t)x * G * D + i];
-          p.out[(size_t)(b * p.Hq + h0) * D + i] = v / (float)S;
+        constexpr int OPT = (G * D + kThreads - 1) / kThreads;
+        constexpr int CH = 32;  // splits loaded at once
+        float sum[OPT];
+#pragma unroll
+        for (int o = 0; o < OPT; ++o) sum[o] = 0.f;
+        for (int x0 = 0; x0 < nsg; x0 += CH) {
+          float t[OPT][CH];
+#pragma unroll
+          for (int o = 0; o < OPT; ++o)
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+              const int i = min(tid + o * kThreads, G * D - 1);
+              t[o][u] = load_dev(gp + (size_t)min(x0 + u, nsg - 1) * G * D + i);
+            }
+#pragma unroll
+          for (int o = 0; o < OPT; ++o)
+#pragma unroll
+            for (int u = 0; u < CH; ++u) sum[o] += x0 + u < nsg ? t[o][u] : 0.f;
         }
-        if (tid == 0) {
-          store_relaxed(p.ws.bar_stats + group, 0u);
-          store_relaxed(p.ws.bar_done + group, 0u);
+#pragma unroll
+        for (int o = 0; o < OPT; ++o) {
+          const int i = tid + o * kThreads;
+          if (i < G * D) p.out[(size_t)(b * p.Hq + h0) * D + i] = sum[o] / (float)S;
         }
+        // leave the group's flags at zero for the next launch
+        for (int i = tid; i < nsg * G; i += kThreads) store_dev(slots + i, make_float2(0.f, 0.f));
+        if (tid == 0) store_dev(p.ws.bar_done + group, 0u);
       }
     }
 
@@ -483,9 +544,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     if (p.grid >= p.total_items) break;
     __syncthreads();
     if (tid == 0) {
-      const uint32_t t = atomic_add_relaxed(p.ws.work_ctr, 1u);
+      const uint32_t t = atomic_add_dev(p.ws.work_ctr, 1u);
       sh.next_item = p.grid + (int)t;
-      if (t == (uint32_t)(p.total_items - 1)) store_relaxed(p.ws.work_ctr, 0u);  // last grab of the launch
+      if (t == (uint32_t)(p.total_items - 1)) store_dev(p.ws.work_ctr, 0u);  // last grab of the launch
     }
     __syncthreads();
     item = sh.next_item;

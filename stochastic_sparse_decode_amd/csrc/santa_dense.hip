@@ -28,9 +28,13 @@ struct DenseLds {
 struct DenseShared {
   float wmax[kWaves][8];
   float wsum[kWaves][8];
+  float M[8];
+  float den[8];
   int last;
   int next_item;
 };
+
+
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
   float* P = (float*)smem;                                  // [G][kPad] scores, then weights
   float* red = (float*)(smem + DenseLds<D, G>::p_bytes);    // [kWaves][G*D]
   __shared__ DenseShared sh;
-  constexpr int LPR = D / 8, RPW = 64 / LPR, UV = 16;
+  constexpr int LPR = D / 8, RPW = 64 / LPR, UV = 8;
   constexpr int PD = D + 2;  // partial record: acc[D], m, l
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
@@ -100,27 +104,39 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
       constexpr int ROWS_IT = UV * kWaves * RPW;
-      for (int base = 0; base < len; base += ROWS_IT) {
-        uint4 vv[UV];
+      // two register buffers in a ping-pong loop: the rows of the next
+      // iteration are in flight while this iteration's FMAs run.  Loads are
+      // unconditional (rows past the end re-read the last row, weight 0), so
+      // the compiler counts outstanding loads exactly.
+      static_assert(kSplit % (2 * ROWS_IT) == 0, "iterations come in pairs");
+      uint4 va[UV], vb[UV];
+      auto issue = [&](uint4 (&bb)[UV], int base) {
 #pragma unroll
         for (int x = 0; x < UV; ++x) {
-          const int row = base + (x * kWaves + w) * RPW + r;
-          vv[x] = row < len ? load_nt((const uint4*)(Vb + (size_t)row * D + c * 8)) : make_uint4(0, 0, 0, 0);
+          const int row = min(base + (x * kWaves + w) * RPW + r, len - 1);
+          bb[x] = load_nt((const uint4*)(Vb + (size_t)row * D + c * 8));
         }
+      };
+      auto consume = [&](const uint4 (&bb)[UV], int base) {
 #pragma unroll
         for (int x = 0; x < UV; ++x) {
           const int row = base + (x * kWaves + w) * RPW + r;
-          if (row < len) {
-            float f[8];
-            unpack8(vv[x], f);
+          float f[8];
+          unpack8(bb[x], f);
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-              const float pw = P[g * kPad + lidx(row)];
+          for (int g = 0; g < G; ++g) {
+            const float pw = row < len ? P[g * kPad + lidx(row)] : 0.f;
 #pragma unroll
-              for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw, f[e], acc[g][e]);
-            }
+            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw, f[e], acc[g][e]);
           }
         }
+      };
+      issue(va, 0);
+      for (int base = 0; base < len; base += 2 * ROWS_IT) {
+        issue(vb, base + ROWS_IT);
+        consume(va, base);
+        issue(va, base + 2 * ROWS_IT);
+        consume(vb, base + ROWS_IT);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -139,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
         float v = red[i];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) v += red[x * G * D + i];
-        part[(i / D) * PD + (i % D)] = v;
+        store_dev(part + (i / D) * PD + (i % D), v);
       }
       if (tid < G) {
         float l = sh.wsum[0][tid];
@@ -148,39 +164,92 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
         float mh = sh.wmax[0][tid];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) mh = fmaxf(mh, sh.wmax[x][tid]);
-        part[tid * PD + D] = mh;
-        part[tid * PD + D + 1] = l;
+        store_dev(part + tid * PD + D, mh);
+        store_dev(part + tid * PD + D + 1, l);
       }
-      __threadfence();
+      wait_memory();
       __syncthreads();
-      if (tid == 0) sh.last = atomic_add_acq_rel(p.ws.bar_done + group, 1u) == (uint32_t)(nsg - 1);
+      if (tid == 0) sh.last = atomic_add_dev(p.ws.bar_done + group, 1u) == (uint32_t)(nsg - 1);
       __syncthreads();
       if (sh.last) {
-        fence_acquire();
+        // out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s, split order
         const float* gp = p.ws.partial + (size_t)group * p.ns * G * PD;
-        for (int i = tid; i < G * D; i += kThreads) {
-          const int g = i / D, d = i % D;
-          float M = -INFINITY;
-          for (int x = 0; x < nsg; ++x) M = fmaxf(M, gp[(size_t)x * G * PD + g * PD + D]);
-          float num = 0.f, den = 0.f;
-          for (int x = 0; x < nsg; ++x) {
-            const float* rec = gp + (size_t)x * G * PD + g * PD;
-            const float sc = expf(rec[D] - M);
-            num = fmaf(sc, rec[d], num);
-            den = fmaf(sc, rec[D + 1], den);
-          }
-          p.out[(size_t)(b * p.Hq + h0) * D + i] = num / den;
+        float mg[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) mg[g] = -INFINITY;
+        for (int x = tid; x < nsg; x += kThreads)
+#pragma unroll
+          for (int g = 0; g < G; ++g) mg[g] = fmaxf(mg[g], load_dev(gp + (size_t)x * G * PD + g * PD + D));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float m = wave_max_masked(mg[g], 1);
+          if (lane == 0) sh.wmax[w][g] = m;
         }
-        if (tid == 0) store_relaxed(p.ws.bar_done + group, 0u);
+        if (tid < G) sh.den[tid] = 0.f;
+        __syncthreads();
+        if (tid < G) {
+          float m = sh.wmax[0][tid];
+#pragma unroll
+          for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[x][tid]);
+          sh.M[tid] = m;
+        }
+        __syncthreads();
+        constexpr int CH = 32;                // splits merged per pass
+        float* scl = P;                       // [CH][G] e^(m_s - M)
+        float* lsc = P + CH * G;              // [CH][G] l_s e^(m_s - M)
+        constexpr int OPT = (G * D + kThreads - 1) / kThreads;
+        float num[OPT];
+#pragma unroll
+        for (int o = 0; o < OPT; ++o) num[o] = 0.f;
+        for (int x0 = 0; x0 < nsg; x0 += CH) {
+          float t[OPT][CH];  // this pass's partial vectors, all loads in flight at once
+#pragma unroll
+          for (int o = 0; o < OPT; ++o) {
+            const int i = min(tid + o * kThreads, G * D - 1);
+            const int g = i / D, d = i % D;
+#pragma unroll
+            for (int u = 0; u < CH; ++u) t[o][u] = load_dev(gp + (size_t)min(x0 + u, nsg - 1) * G * PD + g * PD + d);
+          }
+          if (tid < CH * G) {
+            const int x = x0 + tid / G, g = tid % G;
+            float sc = 0.f, l = 0.f;
+            if (x < nsg) {
+              const float* rec = gp + (size_t)x * G * PD + g * PD;
+              sc = expf(load_dev(rec + D) - sh.M[g]);
+              l = load_dev(rec + D + 1);
+            }
+            scl[tid] = sc;
+            lsc[tid] = l * sc;
+          }
+          __syncthreads();
+#pragma unroll
+          for (int o = 0; o < OPT; ++o) {
+            const int g = min(tid + o * kThreads, G * D - 1) / D;
+#pragma unroll
+            for (int u = 0; u < CH; ++u) num[o] = fmaf(t[o][u], scl[u * G + g], num[o]);  // scl = 0 past nsg
+          }
+          if (tid < G) {
+            float dsum = sh.den[tid];
+            for (int u = 0; u < CH; ++u) dsum += lsc[u * G + tid];
+            sh.den[tid] = dsum;
+          }
+          __syncthreads();
+        }
+#pragma unroll
+        for (int o = 0; o < OPT; ++o) {
+          const int i = tid + o * kThreads;
+          if (i < G * D) p.out[(size_t)(b * p.Hq + h0) * D + i] = num[o] / sh.den[i / D];
+        }
+        if (tid == 0) store_dev(p.ws.bar_done + group, 0u);
       }
     }
 
     if (p.grid >= p.total_items) break;
     __syncthreads();
     if (tid == 0) {
-      const uint32_t t = atomic_add_relaxed(p.ws.work_ctr, 1u);
+      const uint32_t t = atomic_add_dev(p.ws.work_ctr, 1u);
       sh.next_item = p.grid + (int)t;
-      if (t == (uint32_t)(p.total_items - 1)) store_relaxed(p.ws.work_ctr, 0u);
+      if (t == (uint32_t)(p.total_items - 1)) store_dev(p.ws.work_ctr, 0u);
     }
     __syncthreads();
     item = sh.next_item;

@@ -20,6 +20,7 @@ struct Geo {
   static constexpr int NB = (16 / U) > 0 ? (16 / U) : 1;   // blocks in flight per wave
   static constexpr int ROWS_IT = NB * kWaves * BR;          // rows per workgroup iteration
   static_assert(U * G == LPR, "group size must divide the row width");
+  static_assert(kSplit % ROWS_IT == 0, "an iteration never crosses the split end");
 };
 
 // ---------------------------------------------------------------------------
@@ -40,46 +41,56 @@ __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int
   for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qb + g * D + c * 8);
 
   const int my_u = c / G, my_g = c % G;
-  float* scores_out = p.scores_out ? p.scores_out + (size_t)(b * p.Hq + hk * G + my_g) * p.max_n_k + k0 : nullptr;
   float m_run = -INFINITY;
 
-  uint4 cur[Gm::NB][Gm::U], nxt[Gm::NB][Gm::U];
-  auto issue = [&](uint4 (&buf)[Gm::NB][Gm::U], int base) {
+  // A split is always streamed in NIT = kSplit / ROWS_IT fully unrolled
+  // iterations with two register buffers: the loads of iteration i+1 are in
+  // flight while iteration i is reduced.  Loads are unconditional (rows past
+  // the split's end re-read its last row, an L1 hit) so that the compiler
+  // counts outstanding loads exactly and never waits for the prefetch.
+  constexpr int NIT = kSplit / Gm::ROWS_IT;
+  uint4 buf[2][Gm::NB][Gm::U];
+  auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
 #pragma unroll
     for (int nb = 0; nb < Gm::NB; ++nb)
 #pragma unroll
       for (int u = 0; u < Gm::U; ++u) {
-        const int row = base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r;
-        buf[nb][u] = row < len ? load_nt((const uint4*)(Kb + (size_t)row * D + c * 8)) : make_uint4(0, 0, 0, 0);
+        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, len - 1);
+        bb[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 8));
       }
   };
-  issue(cur, 0);
-  for (int base = 0; base < len; base += Gm::ROWS_IT) {
-    const int nbase = base + Gm::ROWS_IT;
-    if (nbase < len) issue(nxt, nbase);
+  issue(buf[0], 0);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int base = it * Gm::ROWS_IT;
+    if (it + 1 < NIT) issue(buf[(it + 1) & 1], base + Gm::ROWS_IT);
 #pragma unroll
     for (int nb = 0; nb < Gm::NB; ++nb) {
       float v[Gm::LPR];
 #pragma unroll
       for (int u = 0; u < Gm::U; ++u)
 #pragma unroll
-        for (int g = 0; g < G; ++g) v[u * G + g] = dot8(cur[nb][u], qv[g]);
+        for (int g = 0; g < G; ++g) v[u * G + g] = dot8(buf[it & 1][nb][u], qv[g]);
       row_reduce_scatter<Gm::LPR>(v, lane);
+      // rows < kSplit always; rows >= len land in unused LDS slots
       const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
-      if (row < len) {
-        const float s = v[0] * p.scale;
-        cdf[my_g * kPad + lidx(row)] = s;
-        m_run = fmaxf(m_run, s);
-        if (scores_out) scores_out[row] = s;
-      }
+      const float s = v[0] * p.scale;
+      cdf[my_g * kPad + lidx(row)] = s;
+      m_run = fmaxf(m_run, row < len ? s : -INFINITY);
     }
-#pragma unroll
-    for (int nb = 0; nb < Gm::NB; ++nb)
-#pragma unroll
-      for (int u = 0; u < Gm::U; ++u) cur[nb][u] = nxt[nb][u];
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+}
+
+// Copy the split's scores from LDS to scores_out (debug output), coalesced.
+template <int G>
+__device__ __forceinline__ void write_scores(const DecodeParams& p, int b, int hk, int k0, int len, const float* cdf) {
+  if (!p.scores_out) return;
+  for (int i = threadIdx.x; i < G * len; i += kThreads) {
+    const int g = i / len, j = i % len;
+    p.scores_out[(size_t)(b * p.Hq + hk * G + g) * p.max_n_k + k0 + j] = cdf[g * kPad + lidx(j)];
+  }
 }
 
 }  // namespace santa

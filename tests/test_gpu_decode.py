@@ -138,15 +138,18 @@ def test_llama32k_max_S(llama32k):
 
 
 def test_determinism_and_workspace_reuse(llama32k):
+    """Bit-identical repeats; one workspace shared by a large and a small problem."""
     wl = llama32k
     q, K, V, nk = P.to_dev(wl)
-    big = santa.problem(q, K, wl.scale)
-    ws = santa.new_workspace(big, q.device)
-    a = run_decode(wl, 128, 2, 11, workspace=ws)
+    ws = santa.new_workspace(santa.problem(q, K, wl.scale), q.device)
     small = W.random_case(2, 8, 2, 128, [3000, 1500], max_n_k=3100, seed=2)
-    run_decode(small, 64, 1, 5, workspace=ws)  # smaller problem on the same workspace
-    b = run_decode(wl, 128, 2, 11, workspace=ws)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    small_fresh = run_decode(small, 64, 1, 5)
+    a = run_decode(wl, 128, 2, 11, workspace=ws)
+    for _ in range(2):
+        sm = run_decode(small, 64, 1, 5, workspace=ws)
+        b = run_decode(wl, 128, 2, 11, workspace=ws)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        assert np.array_equal(sm[0], small_fresh[0]) and np.array_equal(sm[1], small_fresh[1])
     assert santa.santa_workspace_error(ws) == 0
 
 
