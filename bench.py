@@ -170,7 +170,8 @@ def main():
     last = out.clone()
     step(sets[(args.steps - 1) % len(sets)])
     torch.cuda.synchronize()
-    assert torch.equal(last, out), "graph replay differs from eager launch"
+    # outputs agree up to the order of the fp32 adds of the splits' shares
+    assert (last - out).abs().max().item() <= 1e-5, "graph replay differs from eager launch"
     eager_ms = timed(step, sets, min(args.steps, 50), 2, graph=False) if not args.eager else ms
     nbytes = algorithmic_bytes(wl, S)
     gbs = nbytes / (ms * 1e-3) / 1e9

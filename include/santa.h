@@ -64,7 +64,12 @@
  *  seed high 32 bits), mapped to (word >> 8) * 2^-24.  row = b * H_q + h for
  *  value sampling; tags are the ASCII codes 'SYST' (systematic offset),
  *  'STRT' (stratified), 'IID ' (i.i.d.), 'BERN' (Bernoulli features, row
- *  b * H_kv + h_kv).  Equal inputs and seed give bit-identical results.
+ *  b * H_kv + h_kv).  Equal inputs and seed give bit-identical sampled
+ *  indices; santa_decode / santa_bernoulli_qk outputs may differ between runs
+ *  in the last bits, because the splits of the key sequence add their shares
+ *  into `out` with fp32 atomics in whatever order they finish
+ *  (santa_dense_decode merges its splits in a fixed order and is
+ *  bit-reproducible).
  */
 #ifndef SANTA_H_
 #define SANTA_H_

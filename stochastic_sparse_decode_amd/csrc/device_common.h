@@ -169,6 +169,18 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
   return v;
 }
 
+// The same scan on doubles that hold integers below 2^53: every partial sum
+// is exact, so the result does not depend on the order of the additions.
+__device__ __forceinline__ double wave_incl_scan_exact(double v) {
+  v += __builtin_bit_cast(double, dpp_u64<0x111, 0xF>(__builtin_bit_cast(uint64_t, v)));
+  v += __builtin_bit_cast(double, dpp_u64<0x112, 0xF>(__builtin_bit_cast(uint64_t, v)));
+  v += __builtin_bit_cast(double, dpp_u64<0x114, 0xF>(__builtin_bit_cast(uint64_t, v)));
+  v += __builtin_bit_cast(double, dpp_u64<0x118, 0xF>(__builtin_bit_cast(uint64_t, v)));
+  v += __builtin_bit_cast(double, dpp_u64<0x142, 0xA>(__builtin_bit_cast(uint64_t, v)));
+  v += __builtin_bit_cast(double, dpp_u64<0x143, 0xC>(__builtin_bit_cast(uint64_t, v)));
+  return v;
+}
+
 __device__ __forceinline__ uint64_t wave_bcast_u64(uint64_t v, int lane_src) {
   const uint32_t lo = __shfl((int)(uint32_t)v, lane_src, 64);
   const uint32_t hi = __shfl((int)(uint32_t)(v >> 32), lane_src, 64);
@@ -226,6 +238,16 @@ __device__ __forceinline__ float load_dev(const float* p) {
 }
 __device__ __forceinline__ void store_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-scope float add without return (global_atomic_add_f32).
+__device__ __forceinline__ void atomic_add_dev(float* p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float2 load_dev(const float2* p) {
   const uint64_t v = __hip_atomic_load((uint64_t*)const_cast<float2*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

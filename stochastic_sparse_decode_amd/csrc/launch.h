@@ -21,9 +21,11 @@ constexpr uint32_t kErrSpinTimeout = 1u;
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
-  uint32_t* bar_done;   // [groups] arrivals of split partial outputs, back to 0 at kernel end
-  float2* stats;        // [groups][ns][G] (split max, split mass); mass 0 = not yet published
-  float* partial;       // [groups][ns][G][D + 2] partial outputs (+ m, l for dense)
+  uint32_t* epoch;      // launch number: read by every workgroup at start, advanced at kernel end
+  uint32_t* exits;      // workgroups that finished this launch, returns to 0 at kernel end
+  uint32_t* bar_done;   // [groups] arrivals of split partial outputs (dense), back to 0 at kernel end
+  uint64_t* stats;      // [groups][ns][G][2] (epoch:32 | split max bits, epoch:32 | split mass bits)
+  float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
 };
 
 struct DecodeParams {

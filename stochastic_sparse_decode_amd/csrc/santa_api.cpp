@@ -52,7 +52,7 @@ Layout layout_of(const santa_problem* p) {
   const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
   L.partial_bytes = round_up(groups * ns * G * (D + 2) * sizeof(float));
-  L.flag_bytes = round_up(groups * sizeof(uint32_t)) + round_up(groups * ns * G * sizeof(float2));
+  L.flag_bytes = round_up(groups * sizeof(uint32_t)) + round_up(groups * ns * G * 2 * sizeof(uint64_t));
   L.total = kAlign + L.partial_bytes + L.flag_bytes;
   return L;
 }
@@ -64,13 +64,15 @@ Workspace carve(void* base, size_t bytes, const santa_problem* p) {
   const size_t G = (size_t)group_size(p);
   unsigned char* end = b + bytes / kAlign * kAlign;
   unsigned char* done = end - round_up(groups * sizeof(uint32_t));
-  unsigned char* stats = done - round_up(groups * ns * G * sizeof(float2));
+  unsigned char* stats = done - round_up(groups * ns * G * 2 * sizeof(uint64_t));
   Workspace w;
   w.err = (uint32_t*)b;
   w.work_ctr = (uint32_t*)b + 1;
+  w.epoch = (uint32_t*)b + 2;
+  w.exits = (uint32_t*)b + 3;
   w.partial = (float*)(b + kAlign);
   w.bar_done = (uint32_t*)done;
-  w.stats = (float2*)stats;
+  w.stats = (uint64_t*)stats;
   return w;
 }
 

@@ -55,7 +55,8 @@ struct Lds {
 struct Shared {
   float wmax[kWaves][8];
   float lsum[8];
-  double Z[8], SZ[8], Olo[8], Ohi[8], rs[8], usys[8];
+  double Z[8], Olo[8], Ohi[8], rs[8], usys[8];
+  int klo[8], ncand[8], npts[8];
   int wcount[kWaves];
   int n_distinct;
   int last;
@@ -192,31 +193,9 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
 // split's range [O_s, O_{s+1}], so the keys of all splits tile [0, Z)
 // without gaps or overlaps.  A point t selects the key whose interval holds
 // t Z (the inverse CDF, with the half-open convention x_{j-1} <= t Z < x_j).
+// The local CDF is accumulated in doubles holding integers (exact sums).
 // ---------------------------------------------------------------------------
 constexpr float kFix = 2147483648.0f;  // 2^31
-
-struct PointSet {
-  int mode, S;
-  double SZ;           // S / Z
-  double u;            // systematic offset
-  const uint32_t* ub;  // stratified: 24-bit uniforms of the S strata
-};
-
-// Number of stratum points with (k + u_k) / S < x / Z (x in mass units).
-// Systematic: #{k : k + u < y} = ceil(y - u); stratified: all strata below
-// floor(y) plus stratum floor(y) when its uniform lies below y - floor(y).
-__device__ __forceinline__ int points_below(const PointSet& ps, double x) {
-  const double y = x * ps.SZ;
-  if (ps.mode == 2) {
-    const double v = ceil(y - ps.u);
-    return v <= 0.0 ? 0 : (v >= (double)ps.S ? ps.S : (int)v);
-  }
-  if (!(y > 0.0)) return 0;
-  const double m = floor(y);
-  if (m >= (double)ps.S) return ps.S;
-  const int mi = (int)m;
-  return mi + ((double)ps.ub[mi] * 0x1.0p-24 < y - m ? 1 : 0);
-}
 
 // First key j in [0, len) whose right edge O + r c_j exceeds tz, else len - 1.
 __device__ __forceinline__ int key_of(const float* c, int len, double O, double r, double tz) {
@@ -247,6 +226,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
   int item = blockIdx.x;
+  // Launch tag of the statistics slots: the workspace's launch number + 1.
+  // Every workgroup reads the number before any workgroup of this launch can
+  // advance it (that happens when the last one exits), so all agree, and a
+  // slot left by an earlier launch (or an earlier replay of a captured graph)
+  // never carries this tag.
+  // (the load is issued here and first waited for when a slot is written)
+  const uint32_t ep_base = load_dev(p.ws.epoch);
+  auto launch_tag = [&]() -> uint32_t { return ep_base + 1u == 0u ? 1u : ep_base + 1u; };
 
   while (item < p.total_items) {
     const int group = item / p.ns, s = item % p.ns;
@@ -266,6 +253,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       const int len = min(kSplit, n - k0);
       const bool is_last = (s == nsg - 1);
       float mx[G];
+      // split 0 clears the group's output rows; every split adds into them
+      // only after all splits (split 0 included) have published statistics
+      if (s == 0)
+        for (int i = tid; i < G * D; i += kThreads) store_dev(p.out + (size_t)(b * p.Hq + h0) * D + i, 0.f);
 
       // ---- score stage: all keys of the split, G query heads ----------------
       if constexpr (BERN) {
@@ -291,16 +282,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[x][g]);
         float* cg = cdf + g * kPad;
-        uint64_t run[kPer];
-        uint64_t acc = 0;
+        double run[kPer];  // integer-valued: every sum below is exact
+        double acc = 0.0;
+        float sv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) sv[i] = cg[lidx(lane * kPer + i)];  // all reads issued together
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
-          const int j = lane * kPer + i;
-          const uint32_t q = j < len ? (uint32_t)(expf(cg[lidx(j)] - m) * kFix) : 0u;
-          acc += q;
+          const double q = trunc((double)expf(sv[i] - m) * kFix);
+          acc += lane * kPer + i < len ? q : 0.0;
           run[i] = acc;
         }
-        const uint64_t excl = wave_incl_scan_u64(acc) - acc;
+        const double excl = wave_incl_scan_exact(acc) - acc;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
           const int j = lane * kPer + i;
@@ -315,11 +308,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       __syncthreads();
 
       // ---- publish (split max, split mass); the slot doubles as the flag ----
-      float2* slots = p.ws.stats + (size_t)group * p.ns * G;  // [split][head]
+      // each half of a slot carries the launch tag, so a reader accepts it
+      // only when both halves were written by this launch
+      uint64_t* slots = p.ws.stats + (size_t)group * p.ns * G * 2;  // [split][head][2]
       if (tid < G) {
-        float l = sh.lsum[tid];
-        if (__float_as_uint(l) == 0u) l = -0.0f;  // never publish the all-zero pattern (NaN inputs)
-        store_dev(slots + s * G + tid, make_float2(sh.wmax[0][tid], l));
+        const uint64_t tag = (uint64_t)launch_tag() << 32;
+        if (s == 0) wait_memory();  // the cleared output rows are visible first
+        store_dev(slots + (s * G + tid) * 2, tag | __float_as_uint(sh.wmax[0][tid]));
+        store_dev(slots + (s * G + tid) * 2 + 1, tag | __float_as_uint(sh.lsum[tid]));
       }
 
       // while the other splits finish: uniforms of the points
@@ -333,23 +329,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           for (int e = 0; e < 4; ++e)
             if (kb * 4 + e < S) uni[g * kMaxS + kb * 4 + e] = uniform_bits(word_of(blk, e));
         }
-        if (p.mode == 0)
-          for (int i = tid; i < G * kSplit; i += kThreads) cnt[i] = 0u;
       } else if (tid < G) {
         sh.usys[tid] = uniform_f64(stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + tid), kTagSystematic, 0u).x);
       }
+      for (int i = tid; i < G * kSplit; i += kThreads) cnt[i] = 0u;
+      if (tid < G) sh.npts[tid] = 0;
       __syncthreads();
 
       // ---- wait for every split of the group, merge (one wave per head) -----
+      const uint32_t ep = launch_tag();
       for (int g = w; g < G; g += kWaves) {
-        float2 v0 = make_float2(-INFINITY, 1.f);
+        float2 v0 = make_float2(-INFINITY, 0.f);  // (split max, split mass) of lane's split, chunk 0
+        auto read_slot = [&](int x, bool& ok) -> float2 {
+          const uint64_t a = load_dev(slots + (x * G + g) * 2);
+          const uint64_t c = load_dev(slots + (x * G + g) * 2 + 1);
+          ok = (uint32_t)(a >> 32) == ep && (uint32_t)(c >> 32) == ep;
+          return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
+        };
         for (int c0 = 0; c0 < nsg; c0 += 64) {  // poll every chunk of 64 splits
           const int x = c0 + lane;
           uint32_t spins = 0;
           while (true) {
-            const float2 v = x < nsg ? load_dev(slots + x * G + g) : make_float2(-INFINITY, 1.f);
+            bool ok = true;
+            float2 v = make_float2(-INFINITY, 0.f);
+            if (x < nsg) v = read_slot(x, ok);
             if (c0 == 0) v0 = v;
-            if (__ballot(__float_as_uint(v.y) == 0u) == 0ull) break;  // published mass is never +0.0
+            if (__ballot(!ok) == 0ull) break;
             __builtin_amdgcn_s_sleep(1);
             if (++spins > kSpinLimit) {
               if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
@@ -357,17 +362,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
             }
           }
         }
+        auto slot_value = [&](int c0, int x) -> float2 {
+          bool ok;
+          return c0 == 0 ? v0 : (x < nsg ? read_slot(x, ok) : make_float2(-INFINITY, 0.f));
+        };
         float Mloc = -INFINITY;
-        for (int c0 = 0; c0 < nsg; c0 += 64) {
-          const int x = c0 + lane;
-          const float2 v = c0 == 0 ? v0 : (x < nsg ? load_dev(slots + x * G + g) : make_float2(-INFINITY, 1.f));
-          Mloc = fmaxf(Mloc, v.x);
-        }
+        for (int c0 = 0; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, slot_value(c0, c0 + lane).x);
         const float M = wave_max_masked(Mloc, 1);
         uint64_t carry = 0;
         for (int c0 = 0; c0 < nsg; c0 += 64) {
           const int x = c0 + lane;
-          float2 v = c0 == 0 ? v0 : (x < nsg ? load_dev(slots + x * G + g) : make_float2(-INFINITY, 0.f));
+          const float2 v = slot_value(c0, x);
           const float r = x < nsg ? expf(v.x - M) : 0.f;
           const uint64_t Q = x < nsg ? (uint64_t)((double)v.y * (double)r) : 0ull;
           const uint64_t incl = wave_incl_scan_u64(Q) + carry;
@@ -378,60 +383,61 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
           carry = wave_bcast_u64(incl, 63);
         }
-        if (lane == 0) {
-          sh.Z[g] = (double)carry;
-          sh.SZ[g] = (double)S / (double)carry;
-        }
+        if (lane == 0) sh.Z[g] = (double)carry;
       }
       __syncthreads();
 
-      // ---- points per key -----------------------------------------------------
-      constexpr int KPT = kSplit / kThreads;
-      if (p.mode != 0) {
-        // stratified / systematic: the count of key j is the number of points
-        // below its right edge minus the number below its left edge
-        for (int g = 0; g < G; ++g) {
-          const PointSet ps{p.mode, S, sh.SZ[g], sh.usys[g], uni + g * kMaxS};
-          const double O = sh.Olo[g], r = sh.rs[g];
-          const int Plo = points_below(ps, O);
-          const int Phi = is_last ? S : points_below(ps, sh.Ohi[g]);
-          const float* cg = cdf + g * kPad;
-          const int j0 = tid * KPT;
-          if (j0 >= len) continue;
-          int prev = j0 == 0 ? Plo : min(max(points_below(ps, fma(r, (double)cg[lidx(j0 - 1)], O)), Plo), Phi);
-          const size_t row = (size_t)(b * p.Hq + h0 + g);
-#pragma unroll
-          for (int x = 0; x < KPT; ++x) {
-            const int j = j0 + x;
-            if (j >= len) break;
-            const int up = j == len - 1 ? Phi : min(max(points_below(ps, fma(r, (double)cg[lidx(j)], O)), Plo), Phi);
-            cnt[g * kSplit + j] = (uint32_t)(up - prev);
-            if (p.idx_out)
-              for (int k = prev; k < up; ++k) p.idx_out[row * S + k] = k0 + j;
-            prev = up;
-          }
+      // ---- stratum points in this split's range, CDF search -------------------
+      // Candidate points per head: systematic and stratified points are
+      // ordered by k, so only a short range of k can fall in this split (a
+      // margin of one point on each side is tested exactly below); i.i.d.
+      // points are all tested.
+      if (tid < G) {
+        const double Z = sh.Z[tid], lo = sh.Olo[tid] / Z * (double)S, hi = sh.Ohi[tid] / Z * (double)S;
+        int klo = 0, khi = S - 1;
+        if (p.mode == 2) {
+          klo = max(0, (int)ceil(lo - sh.usys[tid]) - 1);
+          if (!is_last) khi = min(S - 1, (int)ceil(hi - sh.usys[tid]) + 1);
+        } else if (p.mode == 1) {
+          klo = max(0, (int)floor(lo) - 1);
+          if (!is_last) khi = min(S - 1, (int)ceil(hi) + 1);
         }
-      } else {
-        // i.i.d.: every point is tested against this split's range and
-        // searched in the local CDF
-        for (int pi = tid; pi < G * S; pi += kThreads) {
-          const int g = pi / S, k = pi % S;
-          const uint32_t ub = uni[g * kMaxS + k];
-          const double tz = (double)ub * 0x1.0p-24 * sh.Z[g];
+        sh.klo[tid] = klo;
+        sh.ncand[tid] = max(0, khi - klo + 1);
+      }
+      __syncthreads();
+      {
+        int total = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) total += sh.ncand[g];
+        for (int pi = tid; pi < total; pi += kThreads) {
+          int g = 0, rem = pi;
+          while (rem >= sh.ncand[g]) rem -= sh.ncand[g++];
+          const int k = sh.klo[g] + rem;
+          const uint32_t* ug = uni + g * kMaxS;
+          double t;
+          if (p.mode == 2) t = ((double)k + sh.usys[g]) / (double)S;
+          else if (p.mode == 1) t = ((double)k + (double)ug[k] * 0x1.0p-24) / (double)S;
+          else t = (double)ug[k] * 0x1.0p-24;
+          const double tz = t * sh.Z[g];
           if (tz < sh.Olo[g] || (!is_last && tz >= sh.Ohi[g])) continue;
           const int j = key_of(cdf + g * kPad, len, sh.Olo[g], sh.rs[g], tz);
           atomicAdd(&cnt[g * kSplit + j], 1u);
-          if (p.idx_out) {  // position in the sorted list: rank among the S uniforms, ties by stream index
-            const uint32_t* ug = uni + g * kMaxS;
-            int rk = 0;
-            for (int x = 0; x < S; ++x) rk += (ug[x] < ub) || (ug[x] == ub && x < k);
-            p.idx_out[(size_t)(b * p.Hq + h0 + g) * S + rk] = k0 + j;
+          atomicAdd(&sh.npts[g], 1);
+          if (p.idx_out) {
+            int pos = k;
+            if (p.mode == 0) {  // rank among the S uniforms, ties by stream index
+              pos = 0;
+              for (int x = 0; x < S; ++x) pos += (ug[x] < ug[k]) || (ug[x] == ug[k] && x < k);
+            }
+            p.idx_out[(size_t)(b * p.Hq + h0 + g) * S + pos] = k0 + j;
           }
         }
       }
       __syncthreads();
 
       // ---- distinct selected keys, in key order ------------------------------
+      constexpr int KPT = kSplit / kThreads;
       int flags = 0, nf = 0;
 #pragma unroll
       for (int x = 0; x < KPT; ++x) {
@@ -495,48 +501,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         }
       }
       __syncthreads();
-      float* part = p.ws.partial + (size_t)(group * p.ns + s) * G * D;
+      // ---- add this split's share into the output rows ----------------------
       for (int i = tid; i < G * D; i += kThreads) {
+        if (sh.npts[i / D] == 0) continue;  // no point of this head fell here
         float v = red[i];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) v += red[x * G * D + i];
-        store_dev(part + i, v);
-      }
-      wait_memory();
-      __syncthreads();
-      if (tid == 0) sh.last = atomic_add_dev(p.ws.bar_done + group, 1u) == (uint32_t)(nsg - 1);
-      __syncthreads();
-
-      // ---- last split of the group: add partials in split order -----------
-      if (sh.last) {
-        const float* gp = p.ws.partial + (size_t)group * p.ns * G * D;
-        constexpr int OPT = (G * D + kThreads - 1) / kThreads;
-        constexpr int CH = 32;  // splits loaded at once
-        float sum[OPT];
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) sum[o] = 0.f;
-        for (int x0 = 0; x0 < nsg; x0 += CH) {
-          float t[OPT][CH];
-#pragma unroll
-          for (int o = 0; o < OPT; ++o)
-#pragma unroll
-            for (int u = 0; u < CH; ++u) {
-              const int i = min(tid + o * kThreads, G * D - 1);
-              t[o][u] = load_dev(gp + (size_t)min(x0 + u, nsg - 1) * G * D + i);
-            }
-#pragma unroll
-          for (int o = 0; o < OPT; ++o)
-#pragma unroll
-            for (int u = 0; u < CH; ++u) sum[o] += x0 + u < nsg ? t[o][u] : 0.f;
-        }
-#pragma unroll
-        for (int o = 0; o < OPT; ++o) {
-          const int i = tid + o * kThreads;
-          if (i < G * D) p.out[(size_t)(b * p.Hq + h0) * D + i] = sum[o] / (float)S;
-        }
-        // leave the group's flags at zero for the next launch
-        for (int i = tid; i < nsg * G; i += kThreads) store_dev(slots + i, make_float2(0.f, 0.f));
-        if (tid == 0) store_dev(p.ws.bar_done + group, 0u);
+        atomic_add_dev(p.out + (size_t)(b * p.Hq + h0) * D + i, v / (float)S);
       }
     }
 
@@ -550,6 +521,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     }
     __syncthreads();
     item = sh.next_item;
+  }
+  // ---- the last workgroup to exit advances the launch number ---------------
+  if (tid == 0 && atomic_add_dev(p.ws.exits, 1u) == (uint32_t)(p.grid - 1)) {
+    store_dev(p.ws.exits, 0u);
+    store_dev(p.ws.epoch, launch_tag());
   }
 }
 
