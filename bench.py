@@ -28,6 +28,36 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "stochastic_sparse_decode_amd", "csrc")
+KERNEL_SOURCES = ("santa_decode.hip", "score_stage.h", "device_common.h", "launch.h")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "santa_decode_llama8b_32k_traffic.txt")
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the decode kernel (ties counter data to a kernel version)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if it is missing or was taken on a different version of the kernel."""
+    try:
+        vals = {}
+        with open(TRAFFIC_PROFILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
+        if vals.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(vals["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -202,7 +232,9 @@ def main():
         "timing": "HIP graph of %d steps, one timed replay" % args.steps if not args.eager else "eager launches",
         "eager_us_per_step": eager_ms * 1000.0,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if args.workload == "llama32k" and args.mode == "systematic"
+                     and S == 128 else None},
     }
     if dense_ms is not None:
         dbytes = algorithmic_bytes(wl, S, dense=True)
