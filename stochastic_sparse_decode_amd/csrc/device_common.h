@@ -186,6 +186,41 @@ __device__ __forceinline__ uint64_t wave_bcast_u64(uint64_t v, int lane_src) {
   const uint32_t hi = __shfl((int)(uint32_t)(v >> 32), lane_src, 64);
   return ((uint64_t)hi << 32) | lo;
 }
+// Maximum over the 64 lanes of a wave, returned in every lane: DPP row
+// shifts (empty sources read -inf) and row broadcasts leave the maximum in
+// lane 63, which is then read as a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  const float other = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, v), CTRL,
+                                         ROW_MASK, 0xF, false));
+  return fmaxf(v, other);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max_step<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Inclusive prefix sum of 32-bit integers over the wave (same DPP pattern).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan_dpp(int v) {
+  v += dpp_i32<0x111, 0xF>(v);
+  v += dpp_i32<0x112, 0xF>(v);
+  v += dpp_i32<0x114, 0xF>(v);
+  v += dpp_i32<0x118, 0xF>(v);
+  v += dpp_i32<0x142, 0xA>(v);
+  v += dpp_i32<0x143, 0xC>(v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max_masked(float x, int first_mask) {
   for (int m = first_mask; m < kWave; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
   return x;

@@ -22,7 +22,7 @@ struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
   uint32_t* epoch;      // launch number: read by every workgroup at start, advanced at kernel end
-  uint32_t* exits;      // workgroups that finished this launch, returns to 0 at kernel end
+  uint32_t* exits;      // workgroups of this launch that have read `epoch`; back to 0 at kernel end
   uint32_t* bar_done;   // [groups] arrivals of split partial outputs (dense), back to 0 at kernel end
   uint64_t* stats;      // [groups][ns][G][2] (epoch:32 | split max bits, epoch:32 | split mass bits)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)

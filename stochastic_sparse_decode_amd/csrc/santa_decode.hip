@@ -57,6 +57,7 @@ struct Shared {
   float lsum[8];
   double Z[8], Olo[8], Ohi[8], rs[8], usys[8];
   int klo[8], ncand[8], npts[8];
+  uint32_t bits[kSplit / 32];  // keys of the split chosen by any head
   int wcount[kWaves];
   int n_distinct;
   int last;
@@ -197,14 +198,28 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
 // ---------------------------------------------------------------------------
 constexpr float kFix = 2147483648.0f;  // 2^31
 
-// First key j in [0, len) whose right edge O + r c_j exceeds tz, else len - 1.
-__device__ __forceinline__ int key_of(const float* c, int len, double O, double r, double tz) {
-  int lo = 0, hi = len;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (fma(r, (double)c[lidx(mid)], O) > tz) hi = mid; else lo = mid + 1;
+// First key j in [0, len) whose local CDF value c_j exceeds tau, else
+// len - 1.  tau = (t Z - O_s) / r_s is the point in the split's own units, so
+// the probes are plain fp32 compares; a monotone rule inside the split keeps
+// the keys of all splits a partition of [0, Z).  Four-way search: three
+// independent probes per round (one LDS latency), then the last <= 4
+// candidates counted at once.
+__device__ __forceinline__ int key_of(const float* c, int len, float tau) {
+  int lo = 0, hi = len;  // the answer lies in [lo, hi]
+  while (hi - lo > 4) {
+    const int q = (hi - lo) >> 2;
+    const int m1 = lo + q, m2 = lo + 2 * q, m3 = lo + 3 * q;
+    const bool b1 = c[lidx(m1)] > tau;
+    const bool b2 = c[lidx(m2)] > tau;
+    const bool b3 = c[lidx(m3)] > tau;
+    lo = b1 ? lo : (b2 ? m1 + 1 : (b3 ? m2 + 1 : m3 + 1));
+    hi = b1 ? m1 : (b2 ? m2 : (b3 ? m3 : hi));
   }
-  return lo < len ? lo : len - 1;
+  int below = 0;  // values <= tau among the last candidates (the values are nondecreasing)
+#pragma unroll
+  for (int x = 0; x < 4; ++x) below += (lo + x < hi && c[lidx(min(lo + x, len - 1))] <= tau) ? 1 : 0;
+  const int j = lo + below;
+  return j < len ? j : len - 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -234,6 +249,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   // (the load is issued here and first waited for when a slot is written)
   const uint32_t ep_base = load_dev(p.ws.epoch);
   auto launch_tag = [&]() -> uint32_t { return ep_base + 1u == 0u ? 1u : ep_base + 1u; };
+  // Each workgroup, once its read of the launch number has completed, counts
+  // itself in; the last one counted advances the number for the next launch
+  // (at its exit), when every workgroup of this launch has read it.  The
+  // count is taken after the first item's output adds are issued (the read
+  // was consumed when the slots were written), so its round trip overlaps
+  // theirs.
+  uint32_t entered = 0xffffffffu;
 
   while (item < p.total_items) {
     const int group = item / p.ns, s = item % p.ns;
@@ -257,6 +279,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       // only after all splits (split 0 included) have published statistics
       if (s == 0)
         for (int i = tid; i < G * D; i += kThreads) store_dev(p.out + (size_t)(b * p.Hq + h0) * D + i, 0.f);
+      // per-key counts, the key bitmap and per-head point counts start at 0
+      // (done here, while the first K loads are in flight)
+      for (int i = tid; i < G * kSplit / 4; i += kThreads) ((uint4*)cnt)[i] = make_uint4(0, 0, 0, 0);
+      if (tid < G) sh.npts[tid] = 0;
+      if (tid < kSplit / 32) sh.bits[tid] = 0u;
+      if (tid < G && p.mode == 2)
+        sh.usys[tid] = uniform_f64(stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + tid), kTagSystematic, 0u).x);
 
       // ---- score stage: all keys of the split, G query heads ----------------
       if constexpr (BERN) {
@@ -267,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float m = wave_max_masked(mx[g], 1);
+        const float m = wave_max(mx[g]);
         if (lane == 0) sh.wmax[w][g] = m;
       }
       __syncthreads();
@@ -329,12 +358,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           for (int e = 0; e < 4; ++e)
             if (kb * 4 + e < S) uni[g * kMaxS + kb * 4 + e] = uniform_bits(word_of(blk, e));
         }
-      } else if (tid < G) {
-        sh.usys[tid] = uniform_f64(stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + tid), kTagSystematic, 0u).x);
+        __syncthreads();
       }
-      for (int i = tid; i < G * kSplit; i += kThreads) cnt[i] = 0u;
-      if (tid < G) sh.npts[tid] = 0;
-      __syncthreads();
 
       // ---- wait for every split of the group, merge (one wave per head) -----
       const uint32_t ep = launch_tag();
@@ -368,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         };
         float Mloc = -INFINITY;
         for (int c0 = 0; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, slot_value(c0, c0 + lane).x);
-        const float M = wave_max_masked(Mloc, 1);
+        const float M = wave_max(Mloc);
         uint64_t carry = 0;
         for (int c0 = 0; c0 < nsg; c0 += 64) {
           const int x = c0 + lane;
@@ -383,47 +408,73 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
           }
           carry = wave_bcast_u64(incl, 63);
         }
-        if (lane == 0) sh.Z[g] = (double)carry;
+        if (lane == 0) {
+          // candidate points of this split: systematic and stratified points
+          // are ordered by k, so only a short range of k can fall in this
+          // split's probability range (one extra point on each side is
+          // tested exactly below); i.i.d. points are all tested
+          const double Z = (double)carry;
+          sh.Z[g] = Z;
+          const double lo = sh.Olo[g] / Z * (double)S, hi = sh.Ohi[g] / Z * (double)S;
+          int klo = 0, khi = S - 1;
+          if (p.mode == 2) {
+            klo = max(0, (int)ceil(lo - sh.usys[g]) - 1);
+            if (!is_last) khi = min(S - 1, (int)ceil(hi - sh.usys[g]) + 1);
+          } else if (p.mode == 1) {
+            klo = max(0, (int)floor(lo) - 1);
+            if (!is_last) khi = min(S - 1, (int)ceil(hi) + 1);
+          }
+          sh.klo[g] = klo;
+          sh.ncand[g] = max(0, khi - klo + 1);
+        }
       }
       __syncthreads();
 
       // ---- stratum points in this split's range, CDF search -------------------
-      // Candidate points per head: systematic and stratified points are
-      // ordered by k, so only a short range of k can fall in this split (a
-      // margin of one point on each side is tested exactly below); i.i.d.
-      // points are all tested.
-      if (tid < G) {
-        const double Z = sh.Z[tid], lo = sh.Olo[tid] / Z * (double)S, hi = sh.Ohi[tid] / Z * (double)S;
-        int klo = 0, khi = S - 1;
-        if (p.mode == 2) {
-          klo = max(0, (int)ceil(lo - sh.usys[tid]) - 1);
-          if (!is_last) khi = min(S - 1, (int)ceil(hi - sh.usys[tid]) + 1);
-        } else if (p.mode == 1) {
-          klo = max(0, (int)floor(lo) - 1);
-          if (!is_last) khi = min(S - 1, (int)ceil(hi) + 1);
-        }
-        sh.klo[tid] = klo;
-        sh.ncand[tid] = max(0, khi - klo + 1);
-      }
-      __syncthreads();
+      // one candidate point per thread; the per-head constants are read once
+      // into registers and selected with compare chains (no LDS round trips)
       {
-        int total = 0;
+        double Zh[G], Ol[G], Oh[G], Rs[G], Us[G];
+        int Kl[G], first[G + 1];
+        first[0] = 0;
 #pragma unroll
-        for (int g = 0; g < G; ++g) total += sh.ncand[g];
-        for (int pi = tid; pi < total; pi += kThreads) {
-          int g = 0, rem = pi;
-          while (rem >= sh.ncand[g]) rem -= sh.ncand[g++];
-          const int k = sh.klo[g] + rem;
+        for (int g = 0; g < G; ++g) {
+          Zh[g] = sh.Z[g];
+          Ol[g] = sh.Olo[g];
+          Oh[g] = sh.Ohi[g];
+          Rs[g] = sh.rs[g];
+          Us[g] = sh.usys[g];
+          Kl[g] = sh.klo[g];
+          first[g + 1] = first[g] + sh.ncand[g];
+        }
+        for (int pi = tid; pi < first[G]; pi += kThreads) {
+          int g = 0;
+#pragma unroll
+          for (int x = 1; x < G; ++x) g = pi >= first[x] ? x : g;
+          double Z = Zh[0], O = Ol[0], Ohg = Oh[0], r = Rs[0], u = Us[0];
+          int k = pi - first[0] + Kl[0];
+#pragma unroll
+          for (int x = 1; x < G; ++x) {
+            if (g == x) {
+              Z = Zh[x];
+              O = Ol[x];
+              Ohg = Oh[x];
+              r = Rs[x];
+              u = Us[x];
+              k = pi - first[x] + Kl[x];
+            }
+          }
           const uint32_t* ug = uni + g * kMaxS;
           double t;
-          if (p.mode == 2) t = ((double)k + sh.usys[g]) / (double)S;
+          if (p.mode == 2) t = ((double)k + u) / (double)S;
           else if (p.mode == 1) t = ((double)k + (double)ug[k] * 0x1.0p-24) / (double)S;
           else t = (double)ug[k] * 0x1.0p-24;
-          const double tz = t * sh.Z[g];
-          if (tz < sh.Olo[g] || (!is_last && tz >= sh.Ohi[g])) continue;
-          const int j = key_of(cdf + g * kPad, len, sh.Olo[g], sh.rs[g], tz);
+          const double tz = t * Z;
+          if (tz < O || (!is_last && tz >= Ohg)) continue;
+          const int j = key_of(cdf + g * kPad, len, (float)((tz - O) / r));
           atomicAdd(&cnt[g * kSplit + j], 1u);
           atomicAdd(&sh.npts[g], 1);
+          atomicOr(&sh.bits[j >> 5], 1u << (j & 31));
           if (p.idx_out) {
             int pos = k;
             if (p.mode == 0) {  // rank among the S uniforms, ties by stream index
@@ -436,68 +487,74 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
       }
       __syncthreads();
 
-      // ---- distinct selected keys, in key order ------------------------------
-      constexpr int KPT = kSplit / kThreads;
-      int flags = 0, nf = 0;
-#pragma unroll
-      for (int x = 0; x < KPT; ++x) {
-        const int j = tid * KPT + x;
-        bool any = false;
-#pragma unroll
-        for (int g = 0; g < G; ++g) any |= cnt[g * kSplit + j] != 0u;
-        if (any && j < len) {
-          flags |= 1 << x;
-          ++nf;
+      // ---- distinct selected keys, in key order (one wave) -------------------
+      if (w == 0) {
+        uint32_t v = (sh.bits[lane >> 1] >> ((lane & 1) * 16)) & 0xFFFFu;  // keys 16*lane .. +15
+        const int nb = __popc(v);
+        const int incl = wave_incl_scan_dpp(nb);
+        int pos = incl - nb;
+        while (v) {
+          const int bit = __ffs(v) - 1;
+          v &= v - 1;
+          list[pos++] = (uint32_t)(lane * 16 + bit);
         }
+        if (lane == 63) sh.n_distinct = incl;
       }
-      const int incl_n = wave_incl_scan_i32(nf, lane);
-      if (lane == 63) sh.wcount[w] = incl_n;
-      __syncthreads();
-      int base = incl_n - nf;
-      for (int x = 0; x < w; ++x) base += sh.wcount[x];
-      if (tid == kThreads - 1) {
-        int tot = 0;
-        for (int x = 0; x < kWaves; ++x) tot += sh.wcount[x];
-        sh.n_distinct = tot;
-      }
-#pragma unroll
-      for (int x = 0; x < KPT; ++x)
-        if (flags & (1 << x)) list[base++] = (uint32_t)(tid * KPT + x);
       __syncthreads();
 
       // ---- gather-add: each distinct row once, added `count` times ---------
+      // A row is spread over LPR lanes (8 features each) and replicated for
+      // GH heads, so a lane accumulates its own head(s) over the rows of its
+      // wave and no cross-lane sum is needed unless a wave holds RG > 1 rows.
       {
-        constexpr int LPR = D / 8, RPW = 64 / LPR;
-        const int r = lane / LPR, c = lane % LPR;
+        constexpr int LPR = D / 8;
+        constexpr int GH = (G * LPR <= 64) ? G : 64 / LPR;  // heads per row copy
+        constexpr int HPL = G / GH;                          // heads per lane
+        constexpr int RG = 64 / (LPR * GH);                  // rows per wave instruction
+        constexpr int UNR = 4;                               // rows in flight per lane
+        const int rg = lane / (LPR * GH), gh = (lane / LPR) % GH, c = lane % LPR;
         const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
-        float acc[G][8];
+        float acc[HPL][8];
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int x = 0; x < HPL; ++x)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+          for (int e = 0; e < 8; ++e) acc[x][e] = 0.f;
         const int nd = sh.n_distinct;
-        for (int i = w * RPW + r; i < nd; i += kWaves * RPW) {
-          const int j = (int)list[i];
-          float f[8];
-          unpack8(*(const uint4*)(Vb + (size_t)j * D + c * 8), f);
+        for (int i0 = 0; i0 < nd; i0 += kWaves * RG * UNR) {
+          uint4 vv[UNR];
+          int jj[UNR];
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float cf = (float)cnt[g * kSplit + j];  // count * v is exact (count <= 1024)
+          for (int u = 0; u < UNR; ++u) {
+            const int i = i0 + (u * kWaves + w) * RG + rg;
+            jj[u] = i < nd ? (int)list[i] : -1;
+            vv[u] = *(const uint4*)(Vb + (size_t)max(jj[u], 0) * D + c * 8);  // key 0 of the split when idle
+          }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(cf, f[e], acc[g][e]);
+          for (int u = 0; u < UNR; ++u) {
+            if (jj[u] < 0) continue;
+            float f[8];
+            unpack8(vv[u], f);
+#pragma unroll
+            for (int x = 0; x < HPL; ++x) {
+              const float cf = (float)cnt[(gh + GH * x) * kSplit + jj[u]];  // count * v is exact
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[x][e] = fmaf(cf, f[e], acc[x][e]);
+            }
           }
         }
+        if constexpr (RG > 1) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+          for (int x = 0; x < HPL; ++x)
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            for (int m = LPR; m < 64; m <<= 1) acc[g][e] += __shfl_xor(acc[g][e], m, 64);
+            for (int e = 0; e < 8; ++e)
+              for (int m = LPR * GH; m < 64; m <<= 1) acc[x][e] += __shfl_xor(acc[x][e], m, 64);
+        }
         __syncthreads();  // `list` aliases `red`
-        if (r == 0) {
+        if (rg == 0) {
 #pragma unroll
-          for (int g = 0; g < G; ++g)
+          for (int x = 0; x < HPL; ++x)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[w * G * D + g * D + c * 8 + e] = acc[g][e];
+            for (int e = 0; e < 8; ++e) red[w * G * D + (gh + GH * x) * D + c * 8 + e] = acc[x][e];
         }
       }
       __syncthreads();
@@ -509,6 +566,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
         for (int x = 1; x < kWaves; ++x) v += red[x * G * D + i];
         atomic_add_dev(p.out + (size_t)(b * p.Hq + h0) * D + i, v / (float)S);
       }
+      if (tid == 0 && entered == 0xffffffffu) entered = atomic_add_dev(p.ws.exits, 1u);
     }
 
     // ---- next work item ----------------------------------------------------
@@ -523,7 +581,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
     item = sh.next_item;
   }
   // ---- the last workgroup to exit advances the launch number ---------------
-  if (tid == 0 && atomic_add_dev(p.ws.exits, 1u) == (uint32_t)(p.grid - 1)) {
+  if (tid == 0 && entered == 0xffffffffu) {  // a workgroup that published nothing
+    wait_memory();                            // its read of the launch number is complete
+    entered = atomic_add_dev(p.ws.exits, 1u);
+  }
+  if (tid == 0 && entered == (uint32_t)(p.grid - 1)) {
     store_dev(p.ws.exits, 0u);
     store_dev(p.ws.epoch, launch_tag());
   }
