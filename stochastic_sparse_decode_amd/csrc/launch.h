@@ -43,13 +43,14 @@ struct DecodeParams {
   int ns;               // splits per group = ceil(max_n_k / kSplit)
   int total_items;      // B * Hkv * ns
   int grid;             // persistent workgroups
+  int occ;              // decode kernel variant: register budget for 1 or 2 workgroups per CU
   Workspace ws;
 };
 
 enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2 };
 
 // Resident-workgroup capacity of the current device for a kernel variant.
-int decode_capacity(int D, int G, bool bernoulli);
+int decode_capacity(int D, int G, bool bernoulli, int occ);
 int dense_capacity(int D, int G);
 
 hipError_t launch_decode(const DecodeParams& p, bool bernoulli, hipStream_t stream);

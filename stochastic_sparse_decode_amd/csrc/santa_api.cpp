@@ -5,7 +5,7 @@
 #include <cmath>
 #include <mutex>
 
-#include "../../include/santa.h"
+#include "santa.h"
 #include "launch.h"
 
 namespace {
@@ -80,24 +80,24 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Resident-workgroup capacity per (device, kernel variant), computed once.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 3 /*kernel*/;
+constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 3 /*kernel*/ * 2 /*workgroups per CU*/;
 std::mutex g_cap_mutex;
 int g_cap[kMaxDevices][kVariants];
 
-int variant_index(int D, int G, int kind) {
+int variant_index(int D, int G, int kind, int occ) {
   const int di = D == 128 ? 1 : 0;
   const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-  return (kind * 2 + di) * 4 + gi;
+  return ((kind * 2 + di) * 4 + gi) * 2 + (occ == 2 ? 1 : 0);
 }
 
-int capacity(int D, int G, int kind) {
+int capacity(int D, int G, int kind, int occ) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(g_cap_mutex);
-  int& slot = g_cap[dev][variant_index(D, G, kind)];
+  int& slot = g_cap[dev][variant_index(D, G, kind, occ)];
   if (slot == 0) {
     slot = kind == santa::kOpDense ? santa::dense_capacity(D, G)
-                                   : santa::decode_capacity(D, G, kind == santa::kOpBernoulli);
+                                   : santa::decode_capacity(D, G, kind == santa::kOpBernoulli, occ);
   }
   return slot;
 }
@@ -136,10 +136,21 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
 }
 
 // grid = all items if they fit the resident capacity, else the capacity (and
-// then a group's splits must fit in it, for the cross-workgroup waits).
+// then a group's splits must fit in it, for the cross-workgroup waits).  The
+// sampling kernel comes in two register budgets: one workgroup per CU when
+// every item gets its own workgroup, two per CU when workgroups take items in
+// turn (one streams while the other waits in its sampling tail).
 int choose_grid(DecodeParams& d, int kind) {
-  const int cap = capacity(d.D, d.G, kind);
+  d.occ = 1;
+  int cap = capacity(d.D, d.G, kind, 1);
   if (cap <= 0) return SANTA_ERR_HIP;
+  if (kind != santa::kOpDense && d.total_items > cap) {
+    const int cap2 = capacity(d.D, d.G, kind, 2);
+    if (cap2 > cap) {
+      d.occ = 2;
+      cap = cap2;
+    }
+  }
   d.grid = d.total_items < cap ? d.total_items : cap;
   if (kind != santa::kOpDense && d.grid < d.total_items && d.ns > d.grid) return SANTA_ERR_UNSUPPORTED;
   return SANTA_OK;

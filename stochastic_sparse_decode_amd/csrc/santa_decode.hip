@@ -225,8 +225,12 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 // ---------------------------------------------------------------------------
 // The fused kernel.
 // ---------------------------------------------------------------------------
-template <int D, int G, bool BERN>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
+// OCC = workgroups per CU the register budget is sized for: 1 when every work
+// item has its own workgroup (no item waits behind another), 2 when
+// workgroups take several items in turn, so that one workgroup streams K
+// while the other is in the latency-bound sampling tail of its item.
+template <int D, int G, bool BERN, int OCC>
+__global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G>;
   float* cdf = (float*)smem;                                   // [G][kPad] scores, then local CDF
@@ -591,42 +595,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int G, bool BERN>
+template <int D, int G>
 size_t lds_bytes() { return Lds<D, G>::bytes; }
 
-template <int D, int G, bool BERN>
+template <int D, int G, bool BERN, int OCC>
 int capacity_t() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  auto fn = decode_kernel<D, G, BERN>;
-  const size_t lds = lds_bytes<D, G, BERN>();
+  auto fn = decode_kernel<D, G, BERN, OCC>;
+  const size_t lds = lds_bytes<D, G>();
   (void)hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess) return 0;
   return per_cu * cus;
 }
 
-template <int D, int G, bool BERN>
+template <int D, int G, bool BERN, int OCC>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const size_t lds = lds_bytes<D, G, BERN>();
-  hipLaunchKernelGGL((decode_kernel<D, G, BERN>), dim3(p.grid), dim3(kThreads), lds, stream, p);
+  const size_t lds = lds_bytes<D, G>();
+  hipLaunchKernelGGL((decode_kernel<D, G, BERN, OCC>), dim3(p.grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-template <bool BERN>
+template <bool BERN, int OCC>
 hipError_t dispatch(const DecodeParams& p, hipStream_t stream) {
 #define SANTA_CASE(DD, GG) \
-  if (p.D == DD && p.G == GG) return launch_t<DD, GG, BERN>(p, stream);
+  if (p.D == DD && p.G == GG) return launch_t<DD, GG, BERN, OCC>(p, stream);
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
   return hipErrorInvalidValue;
 }
 
-template <bool BERN>
+template <bool BERN, int OCC>
 int capacity(int D, int G) {
 #define SANTA_CASE(DD, GG) \
-  if (D == DD && G == GG) return capacity_t<DD, GG, BERN>();
+  if (D == DD && G == GG) return capacity_t<DD, GG, BERN, OCC>();
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
@@ -635,10 +639,14 @@ int capacity(int D, int G) {
 
 }  // namespace
 
-int decode_capacity(int D, int G, bool bernoulli) { return bernoulli ? capacity<true>(D, G) : capacity<false>(D, G); }
+int decode_capacity(int D, int G, bool bernoulli, int occ) {
+  if (occ == 2) return bernoulli ? capacity<true, 2>(D, G) : capacity<false, 2>(D, G);
+  return bernoulli ? capacity<true, 1>(D, G) : capacity<false, 1>(D, G);
+}
 
 hipError_t launch_decode(const DecodeParams& p, bool bernoulli, hipStream_t stream) {
-  return bernoulli ? dispatch<true>(p, stream) : dispatch<false>(p, stream);
+  if (p.occ == 2) return bernoulli ? dispatch<true, 2>(p, stream) : dispatch<false, 2>(p, stream);
+  return bernoulli ? dispatch<true, 1>(p, stream) : dispatch<false, 1>(p, stream);
 }
 
 }  // namespace santa
