@@ -11,21 +11,27 @@
 //
 // Work decomposition (one GPU, gfx950):
 //   work item = (sequence b, KV head, split of kSplit keys).  Items of one KV
-//   head ("group") are consecutive.  Each workgroup (256 threads) takes an
-//   item, streams that split's K rows once with 16-byte loads, scores the G
-//   query heads of the group (GQA packing: one K read serves G heads), keeps
-//   the scores in LDS, turns them into a local CDF (prefix sums of
-//   exp(s - local max)), publishes (local max, local sum) and waits until all
-//   splits of the group have published.  From the merged statistics every
-//   workgroup knows the global normaliser and its split's CDF offset, places
-//   the stratum points that fall in its probability range, searches its local
-//   CDF, gathers each selected value row once (adding it count times), and
-//   writes a partial sum.  The last workgroup of the group to finish adds the
-//   partials in split order and writes the output.
+//   head ("group") are consecutive.  A workgroup (256 threads, 4 waves) takes
+//   an item and streams that split's K rows once with 16-byte loads, scoring
+//   the G query heads of the group from one read (GQA packing); the scores
+//   stay in LDS.  After one barrier (the split maximum of each head), wave g
+//   owns query head g for the rest of the item, with no further barriers:
+//     1. fixed-point weights of its 1024 keys, 16 consecutive keys per lane,
+//        kept in registers with their exact running sums;
+//     2. publishes the split's (max, mass) as soon as the wave scan gives the
+//        total, then polls the other splits' slots of the same head;
+//     3. merges them: global max, exact integer split offsets, normaliser;
+//     4. gets the number of sample points of each of its keys: for the
+//        systematic and stratified schemes in closed form from the key's two
+//        CDF edges, for i.i.d. draws by searching each point in the split's
+//        CDF;
+//     5. gathers each selected value row once, weighted by its count, and
+//        adds the split's share of the estimate to the output row with fp32
+//        device atomics (split 0 clears the row before it publishes).
 //
 // Scheduling: `grid` workgroups are all resident (grid <= occupancy capacity).
 // Workgroup w starts with item w; further items are taken in increasing order
-// from an atomic counter.  A workgroup only waits for splits of its own group,
+// from an atomic counter.  A wave only waits for splits of its own group,
 // all of which have been taken by running workgroups or will be taken by
 // workgroups that finish earlier groups, so the waits always end as long as a
 // group has no more splits than there are workgroups.  Every wait is bounded
@@ -38,32 +44,27 @@ namespace santa {
 
 namespace {
 
+// Dynamic LDS of one workgroup:
+//   sc  [G][kPad]        fp32 scores; the i.i.d. scheme overwrites a head's
+//                        scores with its local CDF once the weights are known
+//   uni [G][kMaxS]       24-bit uniforms of the points (stratified, i.i.d.);
+//                        afterwards the head's list of selected keys
+//   cnt [G][kSplit / 2]  i.i.d. points per key, two 16-bit counters a word
 template <int D, int G>
 struct Lds {
-  // float cdf[G][kPad]; uint32 cnt[G][kSplit]; aux (uniform bits / reduction / list)
-  static constexpr size_t cdf_bytes = sizeof(float) * G * kPad;
-  static constexpr size_t cnt_bytes = sizeof(uint32_t) * G * kSplit;
+  static constexpr size_t sc_bytes = sizeof(float) * G * kPad;
   static constexpr size_t uni_bytes = sizeof(uint32_t) * G * kMaxS;
-  static constexpr size_t red_bytes = sizeof(float) * kWaves * G * D;
-  static constexpr size_t list_bytes = sizeof(uint32_t) * kSplit;
-  static constexpr size_t aux_bytes =
-      uni_bytes > red_bytes ? (uni_bytes > list_bytes ? uni_bytes : list_bytes)
-                            : (red_bytes > list_bytes ? red_bytes : list_bytes);
-  static constexpr size_t bytes = cdf_bytes + cnt_bytes + aux_bytes;
+  static constexpr size_t cnt_bytes = sizeof(uint32_t) * G * (kSplit / 2);
+  static constexpr size_t bytes = sc_bytes + uni_bytes + cnt_bytes;
 };
 
 struct Shared {
   float wmax[kWaves][8];
-  float lsum[8];
-  double Z[8], Olo[8], Ohi[8], rs[8], usys[8];
-  int klo[8], ncand[8], npts[8];
-  uint32_t bits[kSplit / 32];  // keys of the split chosen by any head
-  int wcount[kWaves];
-  int n_distinct;
-  int last;
+  uint32_t epoch;
   int next_item;
   // Bernoulli mode
   float A[8];
+  int wcount[kWaves];
   int nu;
 };
 
@@ -185,41 +186,53 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
 // Sampling helpers.
 //
 // Masses are fixed-point integers in units of 2^-31 of a split's largest
-// weight: w = exp(s - m) in (0, 1] becomes q = trunc(w * 2^31), the local CDF
-// c_j = q_0 + ... + q_j is an exact integer (stored as an fp32 value, which
-// keeps it nondecreasing), and the split masses merged across the group are
-// integers too, so split offsets O_s are exact, nondecreasing and identical
-// in every workgroup.  In global units the right edge of key j of split s is
-// x_j = O_s + r_s c_j with r_s = exp(m_s - M); the edges are clamped to the
-// split's range [O_s, O_{s+1}], so the keys of all splits tile [0, Z)
-// without gaps or overlaps.  A point t selects the key whose interval holds
-// t Z (the inverse CDF, with the half-open convention x_{j-1} <= t Z < x_j).
-// The local CDF is accumulated in doubles holding integers (exact sums).
+// weight: w = exp(s - m) in (0, 1] becomes q = trunc(w * 2^31), and the local
+// CDF c_j = q_0 + ... + q_j is an exact integer (held in doubles, whose sums
+// of such integers are exact and so independent of the order of additions).
+// The split masses merged across the group are integers too, so the split
+// offsets O_s are exact, nondecreasing and identical in every workgroup.  In
+// global units the right edge of key j of split s is
+//   X_j = min(O_s + r_s c_j, O_{s+1}),  r_s = exp(m_s - M),
+// and the last key of a split ends exactly at O_{s+1}, so the keys of all
+// splits tile [0, Z) without gaps or overlaps.  A point t selects the key
+// whose interval [X_{j-1}, X_j) holds t Z (the inverse CDF, half-open).
 // ---------------------------------------------------------------------------
 constexpr float kFix = 2147483648.0f;  // 2^31
 
-// First key j in [0, len) whose local CDF value c_j exceeds tau, else
-// len - 1.  tau = (t Z - O_s) / r_s is the point in the split's own units, so
-// the probes are plain fp32 compares; a monotone rule inside the split keeps
-// the keys of all splits a partition of [0, Z).  Four-way search: three
-// independent probes per round (one LDS latency), then the last <= 4
-// candidates counted at once.
+// Orders this wave's LDS accesses: a wave's LDS operations complete in
+// program order, so after this point every lane reads what any lane of the
+// same wave wrote before it (the fence keeps the compiler from moving LDS
+// accesses across it).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t u, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Number of keys j < len with c_j <= tau (c nondecreasing): the first key
+// whose CDF value exceeds tau, clamped to len - 1.  Branch-free binary search
+// over the split's 1024 slots (ten dependent LDS reads).
 __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
-  int lo = 0, hi = len;  // the answer lies in [lo, hi]
-  while (hi - lo > 4) {
-    const int q = (hi - lo) >> 2;
-    const int m1 = lo + q, m2 = lo + 2 * q, m3 = lo + 3 * q;
-    const bool b1 = c[lidx(m1)] > tau;
-    const bool b2 = c[lidx(m2)] > tau;
-    const bool b3 = c[lidx(m3)] > tau;
-    lo = b1 ? lo : (b2 ? m1 + 1 : (b3 ? m2 + 1 : m3 + 1));
-    hi = b1 ? m1 : (b2 ? m2 : (b3 ? m3 : hi));
-  }
-  int below = 0;  // values <= tau among the last candidates (the values are nondecreasing)
+  int lo = 0;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) below += (lo + x < hi && c[lidx(min(lo + x, len - 1))] <= tau) ? 1 : 0;
-  const int j = lo + below;
-  return j < len ? j : len - 1;
+  for (int step = kSplit / 2; step >= 1; step >>= 1) {
+    const int probe = lo + step - 1;
+    const float v = c[lidx(probe)];
+    lo = (probe < len && v <= tau) ? lo + step : lo;
+  }
+  return lo < len ? lo : len - 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -233,34 +246,26 @@ template <int D, int G, bool BERN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G>;
-  float* cdf = (float*)smem;                                   // [G][kPad] scores, then local CDF
-  uint32_t* cnt = (uint32_t*)(smem + L::cdf_bytes);             // [G][kSplit] points per key
-  unsigned char* aux = smem + L::cdf_bytes + L::cnt_bytes;
-  uint32_t* uni = (uint32_t*)aux;   // [G][kMaxS] 24-bit uniforms (stratified, i.i.d.)
-  float* red = (float*)aux;         // [kWaves][G*D] gather reduction
-  uint32_t* list = (uint32_t*)aux;  // [kSplit] distinct selected keys
+  float* sc = (float*)smem;                                       // [G][kPad]
+  uint32_t* uni = (uint32_t*)(smem + L::sc_bytes);                 // [G][kMaxS]
+  uint32_t* cntw = (uint32_t*)(smem + L::sc_bytes + L::uni_bytes);  // [G][kSplit / 2]
   __shared__ Shared sh;
-  __shared__ uint32_t binfo[128];   // Bernoulli kept-feature union
+  __shared__ uint32_t binfo[128];  // Bernoulli kept-feature union
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
-  int item = blockIdx.x;
-  // Launch tag of the statistics slots: the workspace's launch number + 1.
-  // Every workgroup reads the number before any workgroup of this launch can
-  // advance it (that happens when the last one exits), so all agree, and a
-  // slot left by an earlier launch (or an earlier replay of a captured graph)
-  // never carries this tag.
-  // (the load is issued here and first waited for when a slot is written)
-  const uint32_t ep_base = load_dev(p.ws.epoch);
-  auto launch_tag = [&]() -> uint32_t { return ep_base + 1u == 0u ? 1u : ep_base + 1u; };
-  // Each workgroup, once its read of the launch number has completed, counts
-  // itself in; the last one counted advances the number for the next launch
-  // (at its exit), when every workgroup of this launch has read it.  The
-  // count is taken after the first item's output adds are issued (the read
-  // was consumed when the slots were written), so its round trip overlaps
-  // theirs.
-  uint32_t entered = 0xffffffffu;
+  // Launch tag of the statistics slots: the workspace's launch number + 1
+  // (never 0).  Thread 0 reads the number here; it is advanced only by the
+  // last workgroup of this launch to count itself in (at its exit), and a
+  // workgroup counts itself in only once its read has completed, so every
+  // workgroup of the launch sees the same number, and a slot left by an
+  // earlier launch (or an earlier replay of a captured graph) never carries
+  // this tag.
+  const uint32_t ep_loaded = tid == 0 ? load_dev(p.ws.epoch) : 0u;
+  auto tag_of = [](uint32_t e) -> uint32_t { return e + 1u == 0u ? 1u : e + 1u; };
+  uint32_t entered = 0xffffffffu;  // thread 0: this workgroup's place in the count
 
+  int item = blockIdx.x;
   while (item < p.total_items) {
     const int group = item / p.ns, s = item % p.ns;
     const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
@@ -278,299 +283,285 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       const int k0 = s * kSplit;
       const int len = min(kSplit, n - k0);
       const bool is_last = (s == nsg - 1);
-      float mx[G];
-      // split 0 clears the group's output rows; every split adds into them
-      // only after all splits (split 0 included) have published statistics
-      if (s == 0)
-        for (int i = tid; i < G * D; i += kThreads) store_dev(p.out + (size_t)(b * p.Hq + h0) * D + i, 0.f);
-      // per-key counts, the key bitmap and per-head point counts start at 0
-      // (done here, while the first K loads are in flight)
-      for (int i = tid; i < G * kSplit / 4; i += kThreads) ((uint4*)cnt)[i] = make_uint4(0, 0, 0, 0);
-      if (tid < G) sh.npts[tid] = 0;
-      if (tid < kSplit / 32) sh.bits[tid] = 0u;
-      if (tid < G && p.mode == 2)
-        sh.usys[tid] = uniform_f64(stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + tid), kTagSystematic, 0u).x);
 
       // ---- score stage: all keys of the split, G query heads ----------------
+      float mx[G];
       if constexpr (BERN) {
         bernoulli_setup<D, G>(p, b, hk, p.kept_out != nullptr && s == 0, sh, binfo);
-        score_bernoulli<D, G>(p, b, hk, k0, len, cdf, mx, sh, binfo);
+        score_bernoulli<D, G>(p, b, hk, k0, len, sc, mx, sh, binfo);
       } else {
-        score_rowmajor<D, G>(p, b, hk, k0, len, cdf, mx);
+        score_rowmajor<D, G>(p, b, hk, k0, len, sc, mx);
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float m = wave_max(mx[g]);
         if (lane == 0) sh.wmax[w][g] = m;
       }
+      if (tid == 0 && entered == 0xffffffffu) sh.epoch = ep_loaded;
       __syncthreads();
+      if (tid == 0 && entered == 0xffffffffu) entered = atomic_add_dev(p.ws.exits, 1u);  // read has completed
+      const uint32_t tag = tag_of(sh.epoch);
       if (p.scores_out) {
-        write_scores<G>(p, b, hk, k0, len, cdf);
+        write_scores<G>(p, b, hk, k0, len, sc);
         __syncthreads();
       }
+      uint64_t* slots = p.ws.stats + (size_t)group * p.ns * G * 2;  // [split][head][2]
 
-      // ---- local CDF in fixed point, one wave per head ----------------------
+      // ---- from here on, wave g owns query head g ----------------------------
       for (int g = w; g < G; g += kWaves) {
+        const uint32_t row = (uint32_t)(b * p.Hq + h0 + g);
+        float* orow = p.out + (size_t)row * D;
+        float* cg = sc + g * kPad;
         float m = sh.wmax[0][g];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[x][g]);
-        float* cg = cdf + g * kPad;
-        double run[kPer];  // integer-valued: every sum below is exact
+
+        // 1. fixed-point weights of keys lane*kPer .. lane*kPer+kPer-1
+        double run[kPer];  // exact running sums inside the lane
         double acc = 0.0;
-        float sv[kPer];
+        {
+          float sv[kPer];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) sv[i] = cg[lidx(lane * kPer + i)];  // all reads issued together
+          for (int i = 0; i < kPer; ++i) sv[i] = cg[lidx(lane * kPer + i)];
 #pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const double q = trunc((double)expf(sv[i] - m) * kFix);
-          acc += lane * kPer + i < len ? q : 0.0;
-          run[i] = acc;
-        }
-        const double excl = wave_incl_scan_exact(acc) - acc;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          const int j = lane * kPer + i;
-          if (j < len) {
-            const float cv = (float)(excl + run[i]);
-            cg[lidx(j)] = cv;
-            if (j == len - 1) sh.lsum[g] = cv;
+          for (int i = 0; i < kPer; ++i) {
+            // rows past the split's end hold unrelated LDS contents: weight
+            // exp(-inf) = 0 (the argument is selected, so exp is branch-free)
+            const float wv = expf(lane * kPer + i < len ? sv[i] - m : -INFINITY);
+            const uint32_t q = (uint32_t)(wv * kFix);  // trunc(w * 2^31), exact: w <= 1
+            acc += (double)q;
+            run[i] = acc;
           }
         }
-        if (lane == 0) sh.wmax[0][g] = m;
-      }
-      __syncthreads();
+        const double incl = wave_incl_scan_exact(acc);
+        const double excl = incl - acc;  // exact: all values are integers below 2^53
+        const double total = readlane_f64(incl, 63);
 
-      // ---- publish (split max, split mass); the slot doubles as the flag ----
-      // each half of a slot carries the launch tag, so a reader accepts it
-      // only when both halves were written by this launch
-      uint64_t* slots = p.ws.stats + (size_t)group * p.ns * G * 2;  // [split][head][2]
-      if (tid < G) {
-        const uint64_t tag = (uint64_t)launch_tag() << 32;
-        if (s == 0) wait_memory();  // the cleared output rows are visible first
-        store_dev(slots + (s * G + tid) * 2, tag | __float_as_uint(sh.wmax[0][tid]));
-        store_dev(slots + (s * G + tid) * 2 + 1, tag | __float_as_uint(sh.lsum[tid]));
-      }
-
-      // while the other splits finish: uniforms of the points
-      if (p.mode != 2) {
-        const int nb = (S + 3) >> 2;
-        const uint32_t tag = p.mode == 1 ? kTagStratified : kTagIid;
-        for (int t = tid; t < G * nb; t += kThreads) {
-          const int g = t / nb, kb = t % nb;
-          const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hq + h0 + g), tag, (uint32_t)kb);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (kb * 4 + e < S) uni[g * kMaxS + kb * 4 + e] = uniform_bits(word_of(blk, e));
-        }
-        __syncthreads();
-      }
-
-      // ---- wait for every split of the group, merge (one wave per head) -----
-      const uint32_t ep = launch_tag();
-      for (int g = w; g < G; g += kWaves) {
-        float2 v0 = make_float2(-INFINITY, 0.f);  // (split max, split mass) of lane's split, chunk 0
-        auto read_slot = [&](int x, bool& ok) -> float2 {
-          const uint64_t a = load_dev(slots + (x * G + g) * 2);
-          const uint64_t c = load_dev(slots + (x * G + g) * 2 + 1);
-          ok = (uint32_t)(a >> 32) == ep && (uint32_t)(c >> 32) == ep;
-          return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
-        };
-        for (int c0 = 0; c0 < nsg; c0 += 64) {  // poll every chunk of 64 splits
-          const int x = c0 + lane;
-          uint32_t spins = 0;
-          while (true) {
-            bool ok = true;
-            float2 v = make_float2(-INFINITY, 0.f);
-            if (x < nsg) v = read_slot(x, ok);
-            if (c0 == 0) v0 = v;
-            if (__ballot(!ok) == 0ull) break;
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kSpinLimit) {
-              if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
-              break;
-            }
-          }
-        }
-        auto slot_value = [&](int c0, int x) -> float2 {
-          bool ok;
-          return c0 == 0 ? v0 : (x < nsg ? read_slot(x, ok) : make_float2(-INFINITY, 0.f));
-        };
-        float Mloc = -INFINITY;
-        for (int c0 = 0; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, slot_value(c0, c0 + lane).x);
-        const float M = wave_max(Mloc);
-        uint64_t carry = 0;
-        for (int c0 = 0; c0 < nsg; c0 += 64) {
-          const int x = c0 + lane;
-          const float2 v = slot_value(c0, x);
-          const float r = x < nsg ? expf(v.x - M) : 0.f;
-          const uint64_t Q = x < nsg ? (uint64_t)((double)v.y * (double)r) : 0ull;
-          const uint64_t incl = wave_incl_scan_u64(Q) + carry;
-          if (x == s) {
-            sh.Olo[g] = (double)(incl - Q);
-            sh.Ohi[g] = (double)incl;
-            sh.rs[g] = (double)r;
-          }
-          carry = wave_bcast_u64(incl, 63);
+        // 2. publish (split max, split mass); each half of the 16-byte slot
+        // carries the launch tag, so a reader accepts it only when both halves
+        // were written by this launch.  Split 0 first clears the output row:
+        // every split adds into it only after it has seen all slots.
+        if (s == 0) {
+          for (int i = lane; i < D; i += 64) store_dev(orow + i, 0.f);
+          wait_memory();
         }
         if (lane == 0) {
-          // candidate points of this split: systematic and stratified points
-          // are ordered by k, so only a short range of k can fall in this
-          // split's probability range (one extra point on each side is
-          // tested exactly below); i.i.d. points are all tested
-          const double Z = (double)carry;
-          sh.Z[g] = Z;
-          const double lo = sh.Olo[g] / Z * (double)S, hi = sh.Ohi[g] / Z * (double)S;
-          int klo = 0, khi = S - 1;
+          const uint64_t t = (uint64_t)tag << 32;
+          store_dev(slots + (s * G + g) * 2, t | __float_as_uint(m));
+          store_dev(slots + (s * G + g) * 2 + 1, t | __float_as_uint((float)total));
+        }
+
+        // while the other splits finish: the points' uniforms, and for i.i.d.
+        // draws the fp32 local CDF to search and cleared counters
+        uint32_t* ug = uni + g * kMaxS;
+        uint32_t* cw = cntw + g * (kSplit / 2);
+        if (p.mode != 2) {
+          const uint32_t stag = p.mode == 1 ? kTagStratified : kTagIid;
+          const int nb = (S + 3) >> 2;
+          for (int kb = lane; kb < nb; kb += 64) {
+            const uint4 blk = stream_block(p.seed, row, stag, (uint32_t)kb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kb * 4 + e < S) ug[kb * 4 + e] = uniform_bits(word_of(blk, e));
+          }
+        }
+        if (p.mode == 0) {
+#pragma unroll
+          for (int i = 0; i < kPer; ++i)
+            if (lane * kPer + i < len) cg[lidx(lane * kPer + i)] = (float)(excl + run[i]);  // nondecreasing
+          for (int i = lane; i < kSplit / 2; i += 64) cw[i] = 0u;
+        }
+        const double usys = p.mode == 2 ? uniform_f64(stream_block(p.seed, row, kTagSystematic, 0u).x) : 0.0;
+        wave_lds_sync();
+
+        // 3. wait for every split of the group, merge
+        double Z = 0.0, Olo = 0.0, Ohi = 0.0, rs = 0.0;
+        {
+          float2 v0 = make_float2(-INFINITY, 0.f);  // (split max, split mass) of lane's split, chunk 0
+          auto read_slot = [&](int x, bool& ok) -> float2 {
+            const uint64_t a = load_dev(slots + (x * G + g) * 2);
+            const uint64_t c = load_dev(slots + (x * G + g) * 2 + 1);
+            ok = (uint32_t)(a >> 32) == tag && (uint32_t)(c >> 32) == tag;
+            return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
+          };
+          for (int c0 = 0; c0 < nsg; c0 += 64) {  // poll every chunk of 64 splits
+            const int x = c0 + lane;
+            uint32_t spins = 0;
+            while (true) {
+              bool ok = true;
+              float2 v = make_float2(-INFINITY, 0.f);
+              if (x < nsg) v = read_slot(x, ok);
+              if (c0 == 0) v0 = v;
+              if (__ballot(!ok) == 0ull) break;
+              __builtin_amdgcn_s_sleep(1);
+              if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
+                break;
+              }
+            }
+          }
+          auto slot_value = [&](int c0, int x) -> float2 {
+            bool ok;
+            return c0 == 0 ? v0 : (x < nsg ? read_slot(x, ok) : make_float2(-INFINITY, 0.f));
+          };
+          float Mloc = -INFINITY;
+          for (int c0 = 0; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, slot_value(c0, c0 + lane).x);
+          const float M = wave_max(Mloc);
+          uint64_t carry = 0;
+          for (int c0 = 0; c0 < nsg; c0 += 64) {
+            const int x = c0 + lane;
+            const float2 v = slot_value(c0, x);
+            const float r = x < nsg ? expf(v.x - M) : 0.f;
+            const uint64_t Q = x < nsg ? (uint64_t)((double)v.y * (double)r) : 0ull;  // integer split mass
+            const uint64_t inc = wave_incl_scan_u64(Q) + carry;
+            if (s >= c0 && s < c0 + 64) {
+              Olo = (double)readlane_u64(inc - Q, s - c0);
+              Ohi = (double)readlane_u64(inc, s - c0);
+              rs = (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), s - c0));
+            }
+            carry = readlane_u64(inc, 63);
+          }
+          Z = (double)carry;
+        }
+
+        // 4. points per key of this lane: cnt[i] for key lane*kPer+i; the
+        // lane's points are numbers nstart .. nstart + sum(cnt) - 1 in the
+        // ascending order of the S points
+        int cnt[kPer];
+        int nstart = 0;
+        if (p.mode == 0) {
+          // i.i.d.: the points in [Olo, Ohi) (the last split: [Olo, Z)) are
+          // searched one by one; earlier points are counted for the numbering
+          int before = 0;
+          for (int k = lane; k < S; k += 64) {
+            const double tz = (double)ug[k] * 0x1.0p-24 * Z;
+            if (tz < Olo) {
+              ++before;
+              continue;
+            }
+            if (!is_last && tz >= Ohi) continue;
+            const int j = key_of(cg, len, (float)((tz - Olo) / rs));
+            atomicAdd(&cw[j >> 1], 1u << ((j & 1) * 16));
+          }
+          wave_lds_sync();
+          int lsum = 0;
+#pragma unroll
+          for (int i = 0; i < kPer / 2; ++i) {
+            const uint32_t word = cw[lane * (kPer / 2) + i];
+            cnt[2 * i] = (int)(word & 0xffffu);
+            cnt[2 * i + 1] = (int)(word >> 16);
+            lsum += cnt[2 * i] + cnt[2 * i + 1];
+          }
+          const int bsum = __builtin_amdgcn_readlane(wave_incl_scan_dpp(before), 63);
+          nstart = bsum + wave_incl_scan_dpp(lsum) - lsum;
+        } else {
+          // systematic / stratified: the number of points below an edge X is a
+          // closed-form function of y = X S / Z; a key's count is the
+          // difference at its two edges.  The edges are the same doubles in
+          // the neighbouring lane or split, so every point is counted once.
+          const double inv = (double)S / Z;
+          double X[kPer + 1];
+          X[0] = lane * kPer - 1 >= len - 1 ? Ohi : fmin(Olo + rs * excl, Ohi);
+#pragma unroll
+          for (int i = 0; i < kPer; ++i)
+            X[i + 1] = lane * kPer + i >= len - 1 ? Ohi : fmin(Olo + rs * (excl + run[i]), Ohi);
+          int N[kPer + 1];
           if (p.mode == 2) {
-            klo = max(0, (int)ceil(lo - sh.usys[g]) - 1);
-            if (!is_last) khi = min(S - 1, (int)ceil(hi - sh.usys[g]) + 1);
-          } else if (p.mode == 1) {
-            klo = max(0, (int)floor(lo) - 1);
-            if (!is_last) khi = min(S - 1, (int)ceil(hi) + 1);
+            // t_k = (k + u) / S:  #{k : t_k Z < X} = ceil(y - u), clamped to [0, S]
+#pragma unroll
+            for (int i = 0; i <= kPer; ++i) N[i] = (int)fmin(fmax(ceil(X[i] * inv - usys), 0.0), (double)S);
+          } else {
+            // t_k = (k + u_k) / S:  #{k : t_k Z < X} = f + [u_f < y - f], f = floor(y)
+            double y[kPer + 1], f[kPer + 1];
+            uint32_t uf[kPer + 1];
+#pragma unroll
+            for (int i = 0; i <= kPer; ++i) {
+              y[i] = X[i] * inv;
+              f[i] = fmin(floor(y[i]), (double)S);
+              uf[i] = ug[min((int)f[i], S - 1)];
+            }
+#pragma unroll
+            for (int i = 0; i <= kPer; ++i)
+              N[i] = (int)f[i] + ((f[i] < (double)S && (double)uf[i] * 0x1.0p-24 < y[i] - f[i]) ? 1 : 0);
           }
-          sh.klo[g] = klo;
-          sh.ncand[g] = max(0, khi - klo + 1);
+          if (is_last) {  // the last key of the sequence ends at t = 1
+#pragma unroll
+            for (int i = 0; i <= kPer; ++i)
+              if (lane * kPer + i - 1 >= len - 1) N[i] = S;
+          }
+          nstart = N[0];
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) cnt[i] = N[i + 1] - N[i];
         }
-      }
-      __syncthreads();
 
-      // ---- stratum points in this split's range, CDF search -------------------
-      // one candidate point per thread; the per-head constants are read once
-      // into registers and selected with compare chains (no LDS round trips)
-      {
-        double Zh[G], Ol[G], Oh[G], Rs[G], Us[G];
-        int Kl[G], first[G + 1];
-        first[0] = 0;
+        // sampled indices (optional output), ascending
+        if (p.idx_out) {
+          int* ix = p.idx_out + (size_t)row * S;
+          int k = nstart;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          Zh[g] = sh.Z[g];
-          Ol[g] = sh.Olo[g];
-          Oh[g] = sh.Ohi[g];
-          Rs[g] = sh.rs[g];
-          Us[g] = sh.usys[g];
-          Kl[g] = sh.klo[g];
-          first[g + 1] = first[g] + sh.ncand[g];
+          for (int i = 0; i < kPer; ++i)
+            for (int c = 0; c < cnt[i] && k < S; ++c) ix[k++] = k0 + lane * kPer + i;
         }
-        for (int pi = tid; pi < first[G]; pi += kThreads) {
-          int g = 0;
+
+        // 5. gather-add: the selected keys (key | count << 16) listed in key
+        // order in the head's uniform area, each value row read once and
+        // weighted by its count (count * v is exact in fp32)
+        uint32_t sel = 0;
 #pragma unroll
-          for (int x = 1; x < G; ++x) g = pi >= first[x] ? x : g;
-          double Z = Zh[0], O = Ol[0], Ohg = Oh[0], r = Rs[0], u = Us[0];
-          int k = pi - first[0] + Kl[0];
+        for (int i = 0; i < kPer; ++i) sel |= (cnt[i] > 0 ? 1u : 0u) << i;
+        const int nl = __popc(sel);
+        const int incl_n = wave_incl_scan_dpp(nl);
+        const int nsel = __builtin_amdgcn_readlane(incl_n, 63);
+        if (nsel > 0) {
+          uint32_t* list = ug;
+          wave_lds_sync();  // every lane is done with the uniforms
+          int pos = incl_n - nl;
 #pragma unroll
-          for (int x = 1; x < G; ++x) {
-            if (g == x) {
-              Z = Zh[x];
-              O = Ol[x];
-              Ohg = Oh[x];
-              r = Rs[x];
-              u = Us[x];
-              k = pi - first[x] + Kl[x];
+          for (int i = 0; i < kPer; ++i)
+            if (cnt[i] > 0) list[pos++] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
+          wave_lds_sync();
+          constexpr int LPR = D / 8, RPW = 64 / LPR, UNR = 4;
+          static_assert(RPW * D <= kSplit / 2 && D % 64 == 0, "row-slot sums fit the head's counter area");
+          const int r = lane / LPR, c = lane % LPR;
+          const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D + c * 8;
+          float a8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a8[e] = 0.f;
+          for (int i0 = 0; i0 < nsel; i0 += RPW * UNR) {
+            uint4 vv[UNR];
+            uint32_t ee[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+              const int i = i0 + u * RPW + r;
+              ee[u] = i < nsel ? list[i] : 0u;
+              vv[u] = i < nsel ? *(const uint4*)(Vb + (size_t)(ee[u] & 0xffffu) * D) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+              const float cf = (float)(ee[u] >> 16);
+              float f8[8];
+              unpack8(vv[u], f8);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) a8[e] = fmaf(cf, f8[e], a8[e]);
             }
           }
-          const uint32_t* ug = uni + g * kMaxS;
-          double t;
-          if (p.mode == 2) t = ((double)k + u) / (double)S;
-          else if (p.mode == 1) t = ((double)k + (double)ug[k] * 0x1.0p-24) / (double)S;
-          else t = (double)ug[k] * 0x1.0p-24;
-          const double tz = t * Z;
-          if (tz < O || (!is_last && tz >= Ohg)) continue;
-          const int j = key_of(cdf + g * kPad, len, (float)((tz - O) / r));
-          atomicAdd(&cnt[g * kSplit + j], 1u);
-          atomicAdd(&sh.npts[g], 1);
-          atomicOr(&sh.bits[j >> 5], 1u << (j & 31));
-          if (p.idx_out) {
-            int pos = k;
-            if (p.mode == 0) {  // rank among the S uniforms, ties by stream index
-              pos = 0;
-              for (int x = 0; x < S; ++x) pos += (ug[x] < ug[k]) || (ug[x] == ug[k] && x < k);
-            }
-            p.idx_out[(size_t)(b * p.Hq + h0 + g) * S + pos] = k0 + j;
+          // sum the RPW row slots through LDS (the i.i.d. counter area of the
+          // head, free by now) so that lane l ends with features l, l + 64, ...:
+          // each atomic instruction then covers 64 consecutive floats
+          float* part = (float*)cw;  // [RPW][D]
+          wave_lds_sync();
+          *(float4*)(part + r * D + c * 8) = make_float4(a8[0], a8[1], a8[2], a8[3]);
+          *(float4*)(part + r * D + c * 8 + 4) = make_float4(a8[4], a8[5], a8[6], a8[7]);
+          wave_lds_sync();
+#pragma unroll
+          for (int f = 0; f < D / 64; ++f) {
+            float v = 0.f;
+#pragma unroll
+            for (int x = 0; x < RPW; ++x) v += part[x * D + f * 64 + lane];
+            atomic_add_dev(orow + f * 64 + lane, v / (float)S);
           }
         }
       }
-      __syncthreads();
-
-      // ---- distinct selected keys, in key order (one wave) -------------------
-      if (w == 0) {
-        uint32_t v = (sh.bits[lane >> 1] >> ((lane & 1) * 16)) & 0xFFFFu;  // keys 16*lane .. +15
-        const int nb = __popc(v);
-        const int incl = wave_incl_scan_dpp(nb);
-        int pos = incl - nb;
-        while (v) {
-          const int bit = __ffs(v) - 1;
-          v &= v - 1;
-          list[pos++] = (uint32_t)(lane * 16 + bit);
-        }
-        if (lane == 63) sh.n_distinct = incl;
-      }
-      __syncthreads();
-
-      // ---- gather-add: each distinct row once, added `count` times ---------
-      // A row is spread over LPR lanes (8 features each) and replicated for
-      // GH heads, so a lane accumulates its own head(s) over the rows of its
-      // wave and no cross-lane sum is needed unless a wave holds RG > 1 rows.
-      {
-        constexpr int LPR = D / 8;
-        constexpr int GH = (G * LPR <= 64) ? G : 64 / LPR;  // heads per row copy
-        constexpr int HPL = G / GH;                          // heads per lane
-        constexpr int RG = 64 / (LPR * GH);                  // rows per wave instruction
-        constexpr int UNR = 4;                               // rows in flight per lane
-        const int rg = lane / (LPR * GH), gh = (lane / LPR) % GH, c = lane % LPR;
-        const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
-        float acc[HPL][8];
-#pragma unroll
-        for (int x = 0; x < HPL; ++x)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[x][e] = 0.f;
-        const int nd = sh.n_distinct;
-        for (int i0 = 0; i0 < nd; i0 += kWaves * RG * UNR) {
-          uint4 vv[UNR];
-          int jj[UNR];
-#pragma unroll
-          for (int u = 0; u < UNR; ++u) {
-            const int i = i0 + (u * kWaves + w) * RG + rg;
-            jj[u] = i < nd ? (int)list[i] : -1;
-            vv[u] = *(const uint4*)(Vb + (size_t)max(jj[u], 0) * D + c * 8);  // key 0 of the split when idle
-          }
-#pragma unroll
-          for (int u = 0; u < UNR; ++u) {
-            if (jj[u] < 0) continue;
-            float f[8];
-            unpack8(vv[u], f);
-#pragma unroll
-            for (int x = 0; x < HPL; ++x) {
-              const float cf = (float)cnt[(gh + GH * x) * kSplit + jj[u]];  // count * v is exact
-#pragma unroll
-              for (int e = 0; e < 8; ++e) acc[x][e] = fmaf(cf, f[e], acc[x][e]);
-            }
-          }
-        }
-        if constexpr (RG > 1) {
-#pragma unroll
-          for (int x = 0; x < HPL; ++x)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              for (int m = LPR * GH; m < 64; m <<= 1) acc[x][e] += __shfl_xor(acc[x][e], m, 64);
-        }
-        __syncthreads();  // `list` aliases `red`
-        if (rg == 0) {
-#pragma unroll
-          for (int x = 0; x < HPL; ++x)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[w * G * D + (gh + GH * x) * D + c * 8 + e] = acc[x][e];
-        }
-      }
-      __syncthreads();
-      // ---- add this split's share into the output rows ----------------------
-      for (int i = tid; i < G * D; i += kThreads) {
-        if (sh.npts[i / D] == 0) continue;  // no point of this head fell here
-        float v = red[i];
-#pragma unroll
-        for (int x = 1; x < kWaves; ++x) v += red[x * G * D + i];
-        atomic_add_dev(p.out + (size_t)(b * p.Hq + h0) * D + i, v / (float)S);
-      }
-      if (tid == 0 && entered == 0xffffffffu) entered = atomic_add_dev(p.ws.exits, 1u);
     }
 
     // ---- next work item ----------------------------------------------------
@@ -584,14 +575,14 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     __syncthreads();
     item = sh.next_item;
   }
-  // ---- the last workgroup to exit advances the launch number ---------------
-  if (tid == 0 && entered == 0xffffffffu) {  // a workgroup that published nothing
+  // ---- the last workgroup counted in advances the launch number -------------
+  if (tid == 0 && entered == 0xffffffffu) {  // a workgroup that scored nothing
     wait_memory();                            // its read of the launch number is complete
     entered = atomic_add_dev(p.ws.exits, 1u);
   }
   if (tid == 0 && entered == (uint32_t)(p.grid - 1)) {
     store_dev(p.ws.exits, 0u);
-    store_dev(p.ws.epoch, launch_tag());
+    store_dev(p.ws.epoch, tag_of(ep_loaded));
   }
 }
 

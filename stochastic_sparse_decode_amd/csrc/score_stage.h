@@ -8,7 +8,7 @@
 namespace santa {
 
 constexpr int kPer = kSplit / 64;                // CDF elements per lane in the scan
-constexpr int kPad = kSplit + kSplit / 16;       // padded LDS row of one head's CDF
+constexpr int kPad = kSplit + kSplit / 16 + 16;  // padded LDS row of one head (= 16 mod 32 banks)
 __device__ __forceinline__ int lidx(int j) { return j + (j >> 4); }  // bank-spread index
 
 template <int D, int G>
