@@ -43,10 +43,13 @@
  *
  *  Workspace: a 256-byte aligned device buffer of at least
  *  santa_workspace_bytes(problem) bytes, zero-filled by the caller once
- *  before first use.  The first 256 bytes hold the error bits; partial
- *  results follow them; the arrival flags sit at the end of the buffer.
- *  Kernels leave every flag at zero when they finish, so one buffer serves
- *  any sequence of calls whose problems each fit in it.  Calls that share one
+ *  before first use.  The first 256 bytes hold the error bits and the
+ *  counters; partial results follow them; the per-split statistics slots and
+ *  arrival flags sit at the end of the buffer.  Statistics slots are tagged
+ *  with a launch number taken from a counter that every sampling call
+ *  advances, and the arrival flags return to zero when a call finishes, so
+ *  one buffer serves any sequence of calls whose problems each fit in it
+ *  (including replays of a captured HIP graph).  Calls that share one
  *  workspace must not run concurrently.  After a call that reported a device
  *  error (santa_workspace_error != 0) the workspace must be zero-filled again.
  *

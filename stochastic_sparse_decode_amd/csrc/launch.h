@@ -13,6 +13,7 @@ constexpr int kSplit = 1024;    // keys per work item (one split of one KV head)
 constexpr int kMaxS = 1024;     // largest sample count
 constexpr int kTile = 64;       // keys per feature-major tile (Bernoulli mode)
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait: ~1 s, then error flag
+constexpr uint64_t kLaunchUnit = 1ull << 20;  // launch counter increment per launch (> any grid)
 
 // Error bits written by kernels into the workspace header.
 constexpr uint32_t kErrSpinTimeout = 1u;
@@ -21,8 +22,7 @@ constexpr uint32_t kErrSpinTimeout = 1u;
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
-  uint32_t* epoch;      // launch number: read by every workgroup at start, advanced at kernel end
-  uint32_t* exits;      // workgroups of this launch that have read `epoch`; back to 0 at kernel end
+  uint64_t* launches;   // launch counter of the sampling kernel: kLaunchUnit added per launch
   uint32_t* bar_done;   // [groups] arrivals of split partial outputs (dense), back to 0 at kernel end
   uint64_t* stats;      // [groups][ns][G][2] (epoch:32 | split max bits, epoch:32 | split mass bits)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)

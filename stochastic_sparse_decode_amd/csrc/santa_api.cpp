@@ -68,8 +68,7 @@ Workspace carve(void* base, size_t bytes, const santa_problem* p) {
   Workspace w;
   w.err = (uint32_t*)b;
   w.work_ctr = (uint32_t*)b + 1;
-  w.epoch = (uint32_t*)b + 2;
-  w.exits = (uint32_t*)b + 3;
+  w.launches = (uint64_t*)(b + 8);
   w.partial = (float*)(b + kAlign);
   w.bar_done = (uint32_t*)done;
   w.stats = (uint64_t*)stats;

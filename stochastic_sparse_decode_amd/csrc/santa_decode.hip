@@ -44,23 +44,25 @@ namespace santa {
 
 namespace {
 
+constexpr int kUniRow = kMaxS + 64;  // per-head uniform / list row (+ one spare slot per lane)
+
 // Dynamic LDS of one workgroup:
 //   sc  [G][kPad]        fp32 scores; the i.i.d. scheme overwrites a head's
 //                        scores with its local CDF once the weights are known
-//   uni [G][kMaxS]       24-bit uniforms of the points (stratified, i.i.d.);
+//   uni [G][kUniRow]     24-bit uniforms of the points (stratified, i.i.d.);
 //                        afterwards the head's list of selected keys
 //   cnt [G][kSplit / 2]  i.i.d. points per key, two 16-bit counters a word
 template <int D, int G>
 struct Lds {
   static constexpr size_t sc_bytes = sizeof(float) * G * kPad;
-  static constexpr size_t uni_bytes = sizeof(uint32_t) * G * kMaxS;
+  static constexpr size_t uni_bytes = sizeof(uint32_t) * G * kUniRow;
   static constexpr size_t cnt_bytes = sizeof(uint32_t) * G * (kSplit / 2);
   static constexpr size_t bytes = sc_bytes + uni_bytes + cnt_bytes;
 };
 
 struct Shared {
   float wmax[kWaves][8];
-  uint32_t epoch;
+  uint32_t epoch;  // launch tag of this launch
   int next_item;
   // Bernoulli mode
   float A[8];
@@ -198,6 +200,22 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
 // whose interval [X_{j-1}, X_j) holds t Z (the inverse CDF, half-open).
 // ---------------------------------------------------------------------------
 constexpr float kFix = 2147483648.0f;  // 2^31
+constexpr int kPollSleep = 4;          // s_sleep argument between poll rounds (64 clocks each)
+
+// e^x for x <= 0 (x finite, or a large negative stand-in for a masked key),
+// within about 2 ulp: the hardware base-2 exponential of t = fl(x log2 e),
+// corrected to first order by the rounding residual of that product (the
+// residual is below half an ulp of t, so the dropped second-order term is far
+// below fp32 resolution).  Branch-free, 8 instructions.
+__device__ __forceinline__ float exp_nonpos(float x) {
+  constexpr float kLog2e = 1.44269502162933349609375f;  // log2(e) rounded to fp32
+  constexpr float kLog2eLo = 1.925963033500011e-08f;    // log2(e) - kLog2e
+  constexpr float kLn2 = 0.693147180559945309f;
+  const float t = x * kLog2e;
+  const float r = fmaf(x, kLog2e, -t) + x * kLog2eLo;   // x log2(e) - t
+  const float p = __builtin_amdgcn_exp2f(t);
+  return fmaf(p, r * kLn2, p);
+}
 
 // Orders this wave's LDS accesses: a wave's LDS operations complete in
 // program order, so after this point every lane reads what any lane of the
@@ -247,23 +265,28 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G>;
   float* sc = (float*)smem;                                       // [G][kPad]
-  uint32_t* uni = (uint32_t*)(smem + L::sc_bytes);                 // [G][kMaxS]
+  uint32_t* uni = (uint32_t*)(smem + L::sc_bytes);                 // [G][kUniRow]
   uint32_t* cntw = (uint32_t*)(smem + L::sc_bytes + L::uni_bytes);  // [G][kSplit / 2]
   __shared__ Shared sh;
   __shared__ uint32_t binfo[128];  // Bernoulli kept-feature union
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
-  // Launch tag of the statistics slots: the workspace's launch number + 1
-  // (never 0).  Thread 0 reads the number here; it is advanced only by the
-  // last workgroup of this launch to count itself in (at its exit), and a
-  // workgroup counts itself in only once its read has completed, so every
-  // workgroup of the launch sees the same number, and a slot left by an
-  // earlier launch (or an earlier replay of a captured graph) never carries
-  // this tag.
-  const uint32_t ep_loaded = tid == 0 ? load_dev(p.ws.epoch) : 0u;
-  auto tag_of = [](uint32_t e) -> uint32_t { return e + 1u == 0u ? 1u : e + 1u; };
-  uint32_t entered = 0xffffffffu;  // thread 0: this workgroup's place in the count
+  // Launch tag of the statistics slots.  Every launch adds exactly
+  // kLaunchUnit to the workspace's 64-bit launch counter: workgroup 0 adds
+  // kLaunchUnit - (grid - 1), every other workgroup 1, each only after its own
+  // read of the counter has completed.  So every read made during launch L
+  // returns a value in [L kLaunchUnit, (L + 1) kLaunchUnit), all workgroups of
+  // a launch derive the same launch number, and a slot left by an earlier
+  // launch (or an earlier replay of a captured graph) never carries this
+  // launch's tag.  No workgroup waits for the add.
+  const uint64_t lc = tid == 0 ? load_dev(p.ws.launches) : 0ull;
+  auto tag_of = [](uint64_t c) -> uint32_t {
+    const uint32_t t = (uint32_t)(c / kLaunchUnit) + 1u;
+    return t == 0u ? 1u : t;
+  };
+  const uint64_t my_add = blockIdx.x == 0 ? kLaunchUnit - (uint64_t)(p.grid - 1) : 1ull;
+  bool counted = false;  // thread 0: this workgroup's add has been issued
 
   int item = blockIdx.x;
   while (item < p.total_items) {
@@ -297,10 +320,13 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         const float m = wave_max(mx[g]);
         if (lane == 0) sh.wmax[w][g] = m;
       }
-      if (tid == 0 && entered == 0xffffffffu) sh.epoch = ep_loaded;
+      if (tid == 0 && !counted) sh.epoch = tag_of(lc);
       __syncthreads();
-      if (tid == 0 && entered == 0xffffffffu) entered = atomic_add_dev(p.ws.exits, 1u);  // read has completed
-      const uint32_t tag = tag_of(sh.epoch);
+      if (tid == 0 && !counted) {  // the read has completed: its value is in LDS
+        atomic_add_noret(p.ws.launches, my_add);
+        counted = true;
+      }
+      const uint32_t tag = sh.epoch;
       if (p.scores_out) {
         write_scores<G>(p, b, hk, k0, len, sc);
         __syncthreads();
@@ -325,9 +351,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           for (int i = 0; i < kPer; ++i) sv[i] = cg[lidx(lane * kPer + i)];
 #pragma unroll
           for (int i = 0; i < kPer; ++i) {
-            // rows past the split's end hold unrelated LDS contents: weight
-            // exp(-inf) = 0 (the argument is selected, so exp is branch-free)
-            const float wv = expf(lane * kPer + i < len ? sv[i] - m : -INFINITY);
+            // rows past the split's end hold unrelated LDS contents: their
+            // argument is replaced by -1000, whose exponential is 0 in fp32
+            const float wv = exp_nonpos(lane * kPer + i < len ? sv[i] - m : -1000.f);
             const uint32_t q = (uint32_t)(wv * kFix);  // trunc(w * 2^31), exact: w <= 1
             acc += (double)q;
             run[i] = acc;
@@ -353,7 +379,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 
         // while the other splits finish: the points' uniforms, and for i.i.d.
         // draws the fp32 local CDF to search and cleared counters
-        uint32_t* ug = uni + g * kMaxS;
+        uint32_t* ug = uni + g * kUniRow;
         uint32_t* cw = cntw + g * (kSplit / 2);
         if (p.mode != 2) {
           const uint32_t stag = p.mode == 1 ? kTagStratified : kTagIid;
@@ -384,16 +410,27 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             ok = (uint32_t)(a >> 32) == tag && (uint32_t)(c >> 32) == tag;
             return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
           };
-          for (int c0 = 0; c0 < nsg; c0 += 64) {  // poll every chunk of 64 splits
+          // Poll every chunk of 64 splits.  kPollDepth rounds of slot reads are
+          // in flight at once: each round checks the oldest outstanding read of
+          // a lane's slot and issues a new one in its register, so a slot
+          // written at time t is seen about one device-scope load latency after
+          // t (with one read in flight at a time it could take two).  A lane
+          // stops reading once its slot carries this launch's tag.
+          // Poll every chunk of 64 splits.  A lane stops reading once its slot
+          // carries this launch's tag, and the wave sleeps between rounds, so
+          // waiting waves add little traffic to the memory channels that the
+          // splits still streaming K are using.
+          for (int c0 = 0; c0 < nsg; c0 += 64) {
             const int x = c0 + lane;
+            bool ok = x >= nsg;
             uint32_t spins = 0;
             while (true) {
-              bool ok = true;
-              float2 v = make_float2(-INFINITY, 0.f);
-              if (x < nsg) v = read_slot(x, ok);
-              if (c0 == 0) v0 = v;
+              if (!ok) {
+                const float2 v = read_slot(x, ok);
+                if (c0 == 0) v0 = v;
+              }
               if (__ballot(!ok) == 0ull) break;
-              __builtin_amdgcn_s_sleep(1);
+              __builtin_amdgcn_s_sleep(kPollSleep);
               if (++spins > kSpinLimit) {
                 if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
                 break;
@@ -515,10 +552,15 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         if (nsel > 0) {
           uint32_t* list = ug;
           wave_lds_sync();  // every lane is done with the uniforms
+          // every key is written; an unselected one goes to the lane's own
+          // slot past the list (no branches, no two lanes on one address)
           int pos = incl_n - nl;
 #pragma unroll
-          for (int i = 0; i < kPer; ++i)
-            if (cnt[i] > 0) list[pos++] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
+          for (int i = 0; i < kPer; ++i) {
+            const bool on = cnt[i] > 0;
+            list[on ? pos : kMaxS + lane] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
+            pos += on ? 1 : 0;
+          }
           wave_lds_sync();
           constexpr int LPR = D / 8, RPW = 64 / LPR, UNR = 4;
           static_assert(RPW * D <= kSplit / 2 && D % 64 == 0, "row-slot sums fit the head's counter area");
@@ -575,15 +617,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     __syncthreads();
     item = sh.next_item;
   }
-  // ---- the last workgroup counted in advances the launch number -------------
-  if (tid == 0 && entered == 0xffffffffu) {  // a workgroup that scored nothing
-    wait_memory();                            // its read of the launch number is complete
-    entered = atomic_add_dev(p.ws.exits, 1u);
-  }
-  if (tid == 0 && entered == (uint32_t)(p.grid - 1)) {
-    store_dev(p.ws.exits, 0u);
-    store_dev(p.ws.epoch, tag_of(ep_loaded));
-  }
+  // ---- a workgroup that scored nothing still adds its share ----------------
+  // (the amount is computed from the value read, so the add follows the read)
+  if (tid == 0 && !counted) atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
 }
 
 template <int D, int G>
