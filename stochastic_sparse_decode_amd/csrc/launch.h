@@ -28,24 +28,36 @@ struct Workspace {
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
 };
 
+// Kernel arguments.  The fields a workgroup needs before its first K load
+// (where its split lies, and the query) fill the first 64-byte line, so the
+// kernel reads them with one scalar-cache fetch.
 struct DecodeParams {
-  const void* q;        // [B][Hq][D] fp16
+  // ---- first 64 bytes ----
   const void* K;        // [B][Hkv][max_n_k][D] fp16 (row-major) or feature-major tiles
-  const void* V;        // [B][Hkv][max_n_k][D] fp16
   const int32_t* n_k;   // [B]
+  const void* q;        // [B][Hq][D] fp16
+  int ns;               // splits per group = ceil(max_n_k / kSplit)
+  int max_n_k;
+  int Hkv;
+  int total_items;      // B * Hkv * ns
+  int grid;             // persistent workgroups
+  int Hq;
+  float scale;
+  int S;
+  int mode;
+  int B;
+  // ---- the rest ----
+  const void* V;        // [B][Hkv][max_n_k][D] fp16
   float* out;           // [B][Hq][D]
   int32_t* idx_out;     // [B][Hq][S] or null
   float* scores_out;    // [B][Hq][max_n_k] or null
   uint8_t* kept_out;    // [B][Hq][D] or null (Bernoulli)
-  int B, Hq, Hkv, D, G, max_n_k, S, mode;
   uint64_t seed;
-  float scale;
-  int ns;               // splits per group = ceil(max_n_k / kSplit)
-  int total_items;      // B * Hkv * ns
-  int grid;             // persistent workgroups
-  int occ;              // decode kernel variant: register budget for 1 or 2 workgroups per CU
+  int D, G;
+  int occ;              // sampling kernel variant: 1 = one item per workgroup, 2 = items taken in turn
   Workspace ws;
 };
+static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");
 
 enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2 };
 

@@ -136,19 +136,18 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
 
 // grid = all items if they fit the resident capacity, else the capacity (and
 // then a group's splits must fit in it, for the cross-workgroup waits).  The
-// sampling kernel comes in two register budgets: one workgroup per CU when
-// every item gets its own workgroup, two per CU when workgroups take items in
-// turn (one streams while the other waits in its sampling tail).
+// sampling kernel comes in two variants: one workgroup per CU and one item per
+// workgroup when every item fits (no item loop), else two workgroups per CU
+// that take items in turn (one streams while the other waits in its sampling
+// tail).
 int choose_grid(DecodeParams& d, int kind) {
   d.occ = 1;
   int cap = capacity(d.D, d.G, kind, 1);
   if (cap <= 0) return SANTA_ERR_HIP;
   if (kind != santa::kOpDense && d.total_items > cap) {
-    const int cap2 = capacity(d.D, d.G, kind, 2);
-    if (cap2 > cap) {
-      d.occ = 2;
-      cap = cap2;
-    }
+    d.occ = 2;
+    cap = capacity(d.D, d.G, kind, 2);
+    if (cap <= 0) return SANTA_ERR_HIP;
   }
   d.grid = d.total_items < cap ? d.total_items : cap;
   if (kind != santa::kOpDense && d.grid < d.total_items && d.ns > d.grid) return SANTA_ERR_UNSUPPORTED;

@@ -256,10 +256,11 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 // ---------------------------------------------------------------------------
 // The fused kernel.
 // ---------------------------------------------------------------------------
-// OCC = workgroups per CU the register budget is sized for: 1 when every work
-// item has its own workgroup (no item waits behind another), 2 when
-// workgroups take several items in turn, so that one workgroup streams K
-// while the other is in the latency-bound sampling tail of its item.
+// OCC = workgroups per CU the register budget is sized for.  OCC = 1: every
+// work item has its own workgroup (grid = total_items, launched only then),
+// so no item waits behind another and the kernel has no item loop.  OCC = 2:
+// workgroups take items in turn from a counter, and two share a CU so that
+// one streams K while the other is in the latency-bound sampling tail.
 template <int D, int G, bool BERN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -280,7 +281,18 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   // a launch derive the same launch number, and a slot left by an earlier
   // launch (or an earlier replay of a captured graph) never carries this
   // launch's tag.  No workgroup waits for the add.
-  const uint64_t lc = tid == 0 ? load_dev(p.ws.launches) : 0ull;
+  uint64_t lc = 0ull;  // thread 0: the counter value read (issued with the first item)
+  // One field of each 64-byte line of the arguments is fetched here, so all
+  // lines arrive in one scalar round trip instead of one after another where
+  // their fields are first used (the first K load waits for them).
+  {
+    const void* k_ptr = p.K;
+    const int32_t* nk_ptr = p.n_k;
+    const void* v_ptr = p.V;
+    const uint32_t* err_ptr = p.ws.err;
+    const int ns_ = p.ns, mnk = p.max_n_k, hkv = p.Hkv, items = p.total_items;
+    asm volatile("" ::"s"(k_ptr), "s"(nk_ptr), "s"(v_ptr), "s"(err_ptr), "s"(ns_), "s"(mnk), "s"(hkv), "s"(items));
+  }
   auto tag_of = [](uint64_t c) -> uint32_t {
     const uint32_t t = (uint32_t)(c / kLaunchUnit) + 1u;
     return t == 0u ? 1u : t;
@@ -293,6 +305,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     const int group = item / p.ns, s = item % p.ns;
     const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
     const int n = p.n_k[b];
+    // the counter read is issued after the length read, so waiting for the
+    // length does not wait for it; it is first needed after the score stage
+    if (tid == 0 && !counted) lc = load_dev(p.ws.launches);
     const bool valid = n >= 1 && n <= p.max_n_k;
     const int nsg = valid ? (n + kSplit - 1) / kSplit : 0;
 
@@ -320,7 +335,11 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         const float m = wave_max(mx[g]);
         if (lane == 0) sh.wmax[w][g] = m;
       }
-      if (tid == 0 && !counted) sh.epoch = tag_of(lc);
+      if (tid == 0 && !counted) {
+        uint64_t c = lc;
+        asm volatile("" : "+v"(c));  // keeps the wait for the counter read here, after the stream
+        sh.epoch = tag_of(c);
+      }
       __syncthreads();
       if (tid == 0 && !counted) {  // the read has completed: its value is in LDS
         atomic_add_noret(p.ws.launches, my_add);
@@ -607,7 +626,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     }
 
     // ---- next work item ----------------------------------------------------
-    if (p.grid >= p.total_items) break;
+    // (with one item per workgroup the loop body runs once and the compiler
+    // drops the loop, so nothing is hoisted ahead of the first K loads)
+    if (OCC == 1 || p.grid >= p.total_items) break;
     __syncthreads();
     if (tid == 0) {
       const uint32_t t = atomic_add_dev(p.ws.work_ctr, 1u);
@@ -619,7 +640,10 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   }
   // ---- a workgroup that scored nothing still adds its share ----------------
   // (the amount is computed from the value read, so the add follows the read)
-  if (tid == 0 && !counted) atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
+  if (tid == 0 && !counted) {
+    if (p.total_items <= (int)blockIdx.x) lc = load_dev(p.ws.launches);  // it took no item at all
+    atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
+  }
 }
 
 template <int D, int G>
