@@ -24,7 +24,7 @@ struct Workspace {
   uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
   uint64_t* launches;   // launch counter of the sampling kernel: kLaunchUnit added per launch
   uint32_t* bar_done;   // [groups] arrivals of split partial outputs (dense), back to 0 at kernel end
-  uint64_t* stats;      // [groups][ns][G][2] (epoch:32 | split max bits, epoch:32 | split mass bits)
+  uint64_t* stats;      // [groups][ns][G][2] (tag:32 | split max bits, tag:32 | split mass bits)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
 };
 

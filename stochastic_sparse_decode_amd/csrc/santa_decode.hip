@@ -322,6 +322,14 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       const int len = min(kSplit, n - k0);
       const bool is_last = (s == nsg - 1);
 
+      // split 0 clears the group's output rows, each wave the rows of the
+      // heads it owns after the score stage (its own wait before publishing
+      // covers them); every split adds into a row only after it has seen
+      // split 0's statistics for that head
+      if (s == 0)
+        for (int g = w; g < G; g += kWaves)
+          for (int i = lane; i < D; i += 64) store_dev(p.out + (size_t)(b * p.Hq + h0 + g) * D + i, 0.f);
+
       // ---- score stage: all keys of the split, G query heads ----------------
       float mx[G];
       if constexpr (BERN) {
@@ -341,10 +349,6 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         sh.epoch = tag_of(c);
       }
       __syncthreads();
-      if (tid == 0 && !counted) {  // the read has completed: its value is in LDS
-        atomic_add_noret(p.ws.launches, my_add);
-        counted = true;
-      }
       const uint32_t tag = sh.epoch;
       if (p.scores_out) {
         write_scores<G>(p, b, hk, k0, len, sc);
@@ -384,16 +388,21 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 
         // 2. publish (split max, split mass); each half of the 16-byte slot
         // carries the launch tag, so a reader accepts it only when both halves
-        // were written by this launch.  Split 0 first clears the output row:
-        // every split adds into it only after it has seen all slots.
-        if (s == 0) {
-          for (int i = lane; i < D; i += 64) store_dev(orow + i, 0.f);
-          wait_memory();
-        }
+        // were written by this launch.  Split 0 cleared the output rows before
+        // its score stage; the wait makes sure those stores have completed
+        // (they have, long ago) before any split can see its slot and add.
+        if (s == 0) wait_memory();
         if (lane == 0) {
           const uint64_t t = (uint64_t)tag << 32;
           store_dev(slots + (s * G + g) * 2, t | __float_as_uint(m));
           store_dev(slots + (s * G + g) * 2 + 1, t | __float_as_uint((float)total));
+        }
+        // this workgroup's share of the launch counter (its read has completed:
+        // the value is in LDS); issued after the publish so that no wait before
+        // a publish covers its round trip
+        if (tid == 0 && !counted) {
+          atomic_add_noret(p.ws.launches, my_add);
+          counted = true;
         }
 
         // while the other splits finish: the points' uniforms, and for i.i.d.
@@ -429,12 +438,6 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             ok = (uint32_t)(a >> 32) == tag && (uint32_t)(c >> 32) == tag;
             return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
           };
-          // Poll every chunk of 64 splits.  kPollDepth rounds of slot reads are
-          // in flight at once: each round checks the oldest outstanding read of
-          // a lane's slot and issues a new one in its register, so a slot
-          // written at time t is seen about one device-scope load latency after
-          // t (with one read in flight at a time it could take two).  A lane
-          // stops reading once its slot carries this launch's tag.
           // Poll every chunk of 64 splits.  A lane stops reading once its slot
           // carries this launch's tag, and the wave sleeps between rounds, so
           // waiting waves add little traffic to the memory channels that the
