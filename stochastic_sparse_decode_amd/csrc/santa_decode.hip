@@ -47,21 +47,22 @@ namespace {
 constexpr int kUniRow = kMaxS + 64;  // per-head uniform / list row (+ one spare slot per lane)
 
 // Dynamic LDS of one workgroup:
-//   sc  [G][kPad]        fp32 scores; the i.i.d. scheme overwrites a head's
+//   sc  [nbuf][G][kPad]  fp32 scores; the i.i.d. scheme overwrites a head's
 //                        scores with its local CDF once the weights are known
 //   uni [G][kUniRow]     24-bit uniforms of the points (stratified, i.i.d.);
 //                        afterwards the head's list of selected keys
 //   cnt [G][kSplit / 2]  i.i.d. points per key, two 16-bit counters a word
-template <int D, int G>
+template <int D, int G, int OCC>
 struct Lds {
+  static constexpr int nbuf = OCC == 1 ? 1 : 2;  // score buffers: the pipelined variant keeps two items
   static constexpr size_t sc_bytes = sizeof(float) * G * kPad;
   static constexpr size_t uni_bytes = sizeof(uint32_t) * G * kUniRow;
   static constexpr size_t cnt_bytes = sizeof(uint32_t) * G * (kSplit / 2);
-  static constexpr size_t bytes = sc_bytes + uni_bytes + cnt_bytes;
+  static constexpr size_t bytes = nbuf * sc_bytes + uni_bytes + cnt_bytes;
 };
 
 struct Shared {
-  float wmax[kWaves][8];
+  float wmax[2][kWaves][8];  // per score buffer: split maximum of each head, per wave
   uint32_t epoch;  // launch tag of this launch
   int next_item;
   // Bernoulli mode
@@ -256,18 +257,23 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 // ---------------------------------------------------------------------------
 // The fused kernel.
 // ---------------------------------------------------------------------------
-// OCC = workgroups per CU the register budget is sized for.  OCC = 1: every
-// work item has its own workgroup (grid = total_items, launched only then),
-// so no item waits behind another and the kernel has no item loop.  OCC = 2:
-// workgroups take items in turn from a counter, and two share a CU so that
-// one streams K while the other is in the latency-bound sampling tail.
+// OCC = workgroups per CU the register budget is sized for.
+//  OCC = 1: every work item has its own workgroup (grid = total_items,
+//  launched only then): stream the split, publish, wait, finish; no item loop.
+//  OCC = 2: workgroups take items in turn from a counter, two per CU, and
+//  pipeline them: stream item k and publish its statistics, then finish item
+//  k - 1 (whose group has normally published everything by then), so the
+//  sampling tail of one item never stalls the K stream of the next.  Every
+//  workgroup publishes its current item before it waits for anything, so the
+//  waits end as long as a group has no more splits than there are
+//  workgroups.
 template <int D, int G, bool BERN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  using L = Lds<D, G>;
-  float* sc = (float*)smem;                                       // [G][kPad]
-  uint32_t* uni = (uint32_t*)(smem + L::sc_bytes);                 // [G][kUniRow]
-  uint32_t* cntw = (uint32_t*)(smem + L::sc_bytes + L::uni_bytes);  // [G][kSplit / 2]
+  using L = Lds<D, G, OCC>;
+  uint32_t* uni = (uint32_t*)(smem + L::nbuf * L::sc_bytes);                  // [G][kUniRow]
+  uint32_t* cntw = (uint32_t*)(smem + L::nbuf * L::sc_bytes + L::uni_bytes);  // [G][kSplit / 2]
+  auto score_buf = [&](int i) -> float* { return (float*)(smem + (size_t)i * L::sc_bytes); };  // [G][kPad]
   __shared__ Shared sh;
   __shared__ uint32_t binfo[128];  // Bernoulli kept-feature union
 
@@ -300,70 +306,44 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   const uint64_t my_add = blockIdx.x == 0 ? kLaunchUnit - (uint64_t)(p.grid - 1) : 1ull;
   bool counted = false;  // thread 0: this workgroup's add has been issued
 
-  int item = blockIdx.x;
-  while (item < p.total_items) {
-    const int group = item / p.ns, s = item % p.ns;
-    const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
-    const int n = p.n_k[b];
+  // ---- one work item: (sequence b, KV head hk, split s) ---------------------
+  struct ItemCtx {
+    int group, s, b, hk, h0, nsg, k0, len;
+    bool valid, active, is_last;
+  };
+  auto describe = [&](int item) -> ItemCtx {
+    ItemCtx it;
+    it.group = item / p.ns;
+    it.s = item % p.ns;
+    it.b = it.group / p.Hkv;
+    it.hk = it.group % p.Hkv;
+    it.h0 = it.hk * G;
+    const int n = p.n_k[it.b];
     // the counter read is issued after the length read, so waiting for the
     // length does not wait for it; it is first needed after the score stage
     if (tid == 0 && !counted) lc = load_dev(p.ws.launches);
-    const bool valid = n >= 1 && n <= p.max_n_k;
-    const int nsg = valid ? (n + kSplit - 1) / kSplit : 0;
+    it.valid = n >= 1 && n <= p.max_n_k;
+    it.nsg = it.valid ? (n + kSplit - 1) / kSplit : 0;
+    it.active = it.valid && it.s < it.nsg;
+    it.k0 = it.s * kSplit;
+    it.len = it.active ? min(kSplit, n - it.k0) : 0;
+    it.is_last = it.s == it.nsg - 1;
+    return it;
+  };
 
-    if (!valid) {
-      if (s == 0) {  // invalid sequence length: NaN output, indices -1
-        for (int i = tid; i < G * D; i += kThreads) p.out[(size_t)(b * p.Hq + h0) * D + i] = __builtin_nanf("");
-        if (p.idx_out)
-          for (int i = tid; i < G * S; i += kThreads) p.idx_out[(size_t)(b * p.Hq + h0) * S + i] = -1;
-      }
-    } else if (s < nsg) {
-      const int k0 = s * kSplit;
-      const int len = min(kSplit, n - k0);
-      const bool is_last = (s == nsg - 1);
-
-      // split 0 clears the group's output rows, each wave the rows of the
-      // heads it owns after the score stage (its own wait before publishing
-      // covers them); every split adds into a row only after it has seen
-      // split 0's statistics for that head
-      if (s == 0)
-        for (int g = w; g < G; g += kWaves)
-          for (int i = lane; i < D; i += 64) store_dev(p.out + (size_t)(b * p.Hq + h0 + g) * D + i, 0.f);
-
-      // ---- score stage: all keys of the split, G query heads ----------------
-      float mx[G];
-      if constexpr (BERN) {
-        bernoulli_setup<D, G>(p, b, hk, p.kept_out != nullptr && s == 0, sh, binfo);
-        score_bernoulli<D, G>(p, b, hk, k0, len, sc, mx, sh, binfo);
-      } else {
-        score_rowmajor<D, G>(p, b, hk, k0, len, sc, mx);
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float m = wave_max(mx[g]);
-        if (lane == 0) sh.wmax[w][g] = m;
-      }
-      if (tid == 0 && !counted) {
-        uint64_t c = lc;
-        asm volatile("" : "+v"(c));  // keeps the wait for the counter read here, after the stream
-        sh.epoch = tag_of(c);
-      }
-      __syncthreads();
-      const uint32_t tag = sh.epoch;
-      if (p.scores_out) {
-        write_scores<G>(p, b, hk, k0, len, sc);
-        __syncthreads();
-      }
-      uint64_t* slots = p.ws.stats + (size_t)group * p.ns * G * 2;  // [split][head][2]
-
-      // ---- from here on, wave g owns query head g ----------------------------
-      for (int g = w; g < G; g += kWaves) {
+  // ---- per query head (wave g owns head g): weights, then publish and/or
+  // the sampling tail ----------------------------------------------------------
+  auto head = [&](const ItemCtx& it, int g, float* scb, int wb, bool do_publish, bool do_finish) {
+        const int s = it.s, len = it.len, k0 = it.k0, nsg = it.nsg, b = it.b, hk = it.hk, h0 = it.h0;
+        const bool is_last = it.is_last;
+        const uint32_t tag = sh.epoch;
+        uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
         const uint32_t row = (uint32_t)(b * p.Hq + h0 + g);
         float* orow = p.out + (size_t)row * D;
-        float* cg = sc + g * kPad;
-        float m = sh.wmax[0][g];
+        float* cg = scb + g * kPad;
+        float m = sh.wmax[wb][0][g];
 #pragma unroll
-        for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[x][g]);
+        for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[wb][x][g]);
 
         // 1. fixed-point weights of keys lane*kPer .. lane*kPer+kPer-1
         double run[kPer];  // exact running sums inside the lane
@@ -391,6 +371,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         // were written by this launch.  Split 0 cleared the output rows before
         // its score stage; the wait makes sure those stores have completed
         // (they have, long ago) before any split can see its slot and add.
+        if (do_publish) {
         if (s == 0) wait_memory();
         if (lane == 0) {
           const uint64_t t = (uint64_t)tag << 32;
@@ -404,6 +385,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           atomic_add_noret(p.ws.launches, my_add);
           counted = true;
         }
+        }
+        if (!do_finish) return;
 
         // while the other splits finish: the points' uniforms, and for i.i.d.
         // draws the fp32 local CDF to search and cleared counters
@@ -625,21 +608,82 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             atomic_add_dev(orow + f * 64 + lane, v / (float)S);
           }
         }
-      }
-    }
+  };
 
-    // ---- next work item ----------------------------------------------------
-    // (with one item per workgroup the loop body runs once and the compiler
-    // drops the loop, so nothing is hoisted ahead of the first K loads)
-    if (OCC == 1 || p.grid >= p.total_items) break;
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t t = atomic_add_dev(p.ws.work_ctr, 1u);
-      sh.next_item = p.grid + (int)t;
-      if (t == (uint32_t)(p.total_items - 1)) store_dev(p.ws.work_ctr, 0u);  // last grab of the launch
+  // ---- stream one split, publish its statistics (all waves) -----------------
+  auto start_item = [&](const ItemCtx& it, float* scb, int wb, bool finish_now) {
+    if (!it.valid) {
+      if (it.s == 0) {  // invalid sequence length: NaN output, indices -1
+        for (int i = tid; i < G * D; i += kThreads) p.out[(size_t)(it.b * p.Hq + it.h0) * D + i] = __builtin_nanf("");
+        if (p.idx_out)
+          for (int i = tid; i < G * S; i += kThreads) p.idx_out[(size_t)(it.b * p.Hq + it.h0) * S + i] = -1;
+      }
+      return;
+    }
+    if (!it.active) return;
+    // split 0 clears the group's output rows, each wave the rows of the
+    // heads it owns after the score stage (its own wait before publishing
+    // covers them); every split adds into a row only after it has seen
+    // split 0's statistics for that head
+    if (it.s == 0)
+      for (int g = w; g < G; g += kWaves)
+        for (int i = lane; i < D; i += 64) store_dev(p.out + (size_t)(it.b * p.Hq + it.h0 + g) * D + i, 0.f);
+
+    // ---- score stage: all keys of the split, G query heads ----------------
+    float mx[G];
+    if constexpr (BERN) {
+      bernoulli_setup<D, G>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo);
+      score_bernoulli<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo);
+    } else {
+      score_rowmajor<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float m = wave_max(mx[g]);
+      if (lane == 0) sh.wmax[wb][w][g] = m;
+    }
+    if (tid == 0 && !counted) {
+      uint64_t c = lc;
+      asm volatile("" : "+v"(c));  // keeps the wait for the counter read here, after the stream
+      sh.epoch = tag_of(c);
     }
     __syncthreads();
-    item = sh.next_item;
+    if (p.scores_out) {
+      write_scores<G>(p, it.b, it.hk, it.k0, it.len, scb);
+      __syncthreads();
+    }
+    // ---- from here on, wave g owns query head g ----------------------------
+    for (int g = w; g < G; g += kWaves) head(it, g, scb, wb, true, finish_now);
+  };
+
+  if constexpr (OCC == 1) {
+    start_item(describe(blockIdx.x), score_buf(0), 0, true);
+  } else {
+    ItemCtx prev{};  // nothing to finish yet (active = false)
+    int item = blockIdx.x, cb = 0;
+    while (true) {
+      const bool have = item < p.total_items;
+      ItemCtx cur = prev;
+      cur.active = false;
+      if (have) {
+        cur = describe(item);
+        start_item(cur, score_buf(cb), cb, false);
+      }
+      if (prev.active)  // the previous item's statistics are published by now, or soon
+        for (int g = w; g < G; g += kWaves) head(prev, g, score_buf(cb ^ 1), cb ^ 1, false, true);
+      if (!have) break;
+      // ---- next work item ------------------------------------------------
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t t = atomic_add_dev(p.ws.work_ctr, 1u);
+        sh.next_item = p.grid + (int)t;
+        if (t == (uint32_t)(p.total_items - 1)) store_dev(p.ws.work_ctr, 0u);  // last grab of the launch
+      }
+      __syncthreads();
+      item = sh.next_item;
+      prev = cur;
+      cb ^= 1;
+    }
   }
   // ---- a workgroup that scored nothing still adds its share ----------------
   // (the amount is computed from the value read, so the add follows the read)
@@ -649,8 +693,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int G>
-size_t lds_bytes() { return Lds<D, G>::bytes; }
+template <int D, int G, int OCC>
+size_t lds_bytes() { return Lds<D, G, OCC>::bytes; }
 
 template <int D, int G, bool BERN, int OCC>
 int capacity_t() {
@@ -658,7 +702,7 @@ int capacity_t() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   auto fn = decode_kernel<D, G, BERN, OCC>;
-  const size_t lds = lds_bytes<D, G>();
+  const size_t lds = lds_bytes<D, G, OCC>();
   (void)hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess) return 0;
   return per_cu * cus;
@@ -666,7 +710,7 @@ int capacity_t() {
 
 template <int D, int G, bool BERN, int OCC>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const size_t lds = lds_bytes<D, G>();
+  const size_t lds = lds_bytes<D, G, OCC>();
   hipLaunchKernelGGL((decode_kernel<D, G, BERN, OCC>), dim3(p.grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
