@@ -260,13 +260,10 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 // OCC = workgroups per CU the register budget is sized for.
 //  OCC = 1: every work item has its own workgroup (grid = total_items,
 //  launched only then): stream the split, publish, wait, finish; no item loop.
-//  OCC = 2: workgroups take items in turn from a counter, two per CU, and
+//  OCC = 2: two workgroups per CU take the valid splits round-robin and
 //  pipeline them: stream item k and publish its statistics, then finish item
 //  k - 1 (whose group has normally published everything by then), so the
-//  sampling tail of one item never stalls the K stream of the next.  Every
-//  workgroup publishes its current item before it waits for anything, so the
-//  waits end as long as a group has no more splits than there are
-//  workgroups.
+//  sampling tail of one item never stalls the K stream of the next.
 template <int D, int G, bool BERN, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -659,38 +656,72 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   if constexpr (OCC == 1) {
     start_item(describe(blockIdx.x), score_buf(0), 0, true);
   } else {
-    ItemCtx prev{};  // nothing to finish yet (active = false)
-    int item = blockIdx.x, cb = 0;
-    while (true) {
-      const bool have = item < p.total_items;
-      ItemCtx cur = prev;
-      cur.active = false;
-      if (have) {
-        cur = describe(item);
-        start_item(cur, score_buf(cb), cb, false);
+    // Only valid splits are items, numbered sequence by sequence: sequence b
+    // has H_kv * nsg_b of them (nsg_b = ceil(n_k[b] / kSplit) for a valid
+    // length, none otherwise).  Workgroup x takes items x, x + grid,
+    // x + 2 grid, ... (no shared counter, no skipped splits).  The splits of
+    // a group are consecutive items, so with nsg <= grid they fall in at most
+    // two consecutive rounds; every workgroup publishes its item of round r
+    // before it waits for any item of round r or later, so the waits end.
+    if (tid == 0 && !counted) lc = load_dev(p.ws.launches);
+    // sequences with an invalid length: NaN outputs, indices -1
+    for (int bq = blockIdx.x; bq < p.B; bq += p.grid) {
+      const int n = p.n_k[bq];
+      if (n >= 1 && n <= p.max_n_k) continue;
+      for (int i = tid; i < p.Hq * D; i += kThreads) p.out[(size_t)bq * p.Hq * D + i] = __builtin_nanf("");
+      if (p.idx_out)
+        for (int i = tid; i < p.Hq * S; i += kThreads) p.idx_out[(size_t)bq * p.Hq * S + i] = -1;
+    }
+    // lane l of every wave keeps the length of sequence l of the first 64
+    const int nk0 = lane < p.B ? p.n_k[lane] : 0;
+    // item t -> (sequence, KV head, split); false when t is past the last item
+    auto find = [&](int t, ItemCtx& it) -> bool {
+      int carry = 0;
+      for (int c0 = 0; c0 < p.B; c0 += 64) {
+        const int bq = c0 + lane;
+        const int n = c0 == 0 ? nk0 : (bq < p.B ? p.n_k[bq] : 0);
+        const int nsgq = (n >= 1 && n <= p.max_n_k) ? (n + kSplit - 1) / kSplit : 0;
+        const int cnt = nsgq * p.Hkv;
+        const int incl = wave_incl_scan_dpp(cnt) + carry;
+        const uint64_t hit = __ballot(incl > t);
+        if (hit != 0ull) {
+          const int l = __ffsll((unsigned long long)hit) - 1;
+          const int j = t - __builtin_amdgcn_readlane(incl - cnt, l);
+          const int nb = __builtin_amdgcn_readlane(n, l), nsgb = __builtin_amdgcn_readlane(nsgq, l);
+          it.b = c0 + l;
+          it.hk = j / nsgb;
+          it.s = j % nsgb;
+          it.h0 = it.hk * G;
+          it.group = it.b * p.Hkv + it.hk;
+          it.valid = true;
+          it.active = true;
+          it.nsg = nsgb;
+          it.k0 = it.s * kSplit;
+          it.len = min(kSplit, nb - it.k0);
+          it.is_last = it.s == nsgb - 1;
+          return true;
+        }
+        carry = __builtin_amdgcn_readlane(incl, 63);
       }
+      return false;
+    };
+    ItemCtx prev{};  // nothing to finish yet (active = false)
+    int cb = 0;
+    for (int t = blockIdx.x;; t += p.grid) {
+      ItemCtx cur{};
+      const bool have = find(t, cur);
+      if (have) start_item(cur, score_buf(cb), cb, false);
       if (prev.active)  // the previous item's statistics are published by now, or soon
         for (int g = w; g < G; g += kWaves) head(prev, g, score_buf(cb ^ 1), cb ^ 1, false, true);
       if (!have) break;
-      // ---- next work item ------------------------------------------------
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t t = atomic_add_dev(p.ws.work_ctr, 1u);
-        sh.next_item = p.grid + (int)t;
-        if (t == (uint32_t)(p.total_items - 1)) store_dev(p.ws.work_ctr, 0u);  // last grab of the launch
-      }
-      __syncthreads();
-      item = sh.next_item;
+      __syncthreads();  // every wave is done with the buffer the next item overwrites
       prev = cur;
       cb ^= 1;
     }
   }
   // ---- a workgroup that scored nothing still adds its share ----------------
   // (the amount is computed from the value read, so the add follows the read)
-  if (tid == 0 && !counted) {
-    if (p.total_items <= (int)blockIdx.x) lc = load_dev(p.ws.launches);  // it took no item at all
-    atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
-  }
+  if (tid == 0 && !counted) atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
 }
 
 template <int D, int G, int OCC>

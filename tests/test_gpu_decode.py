@@ -8,6 +8,8 @@ oracle's estimate on the GPU's index list, and against the oracle's own output
 for every head without a flip.
 """
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -116,6 +118,42 @@ def test_invalid_sequence_lengths():
     assert np.isnan(out[2]).all() and (idx[2] == -1).all()
     assert not np.isnan(out[1]).any()
     check_parity(wl, 16, 2, 3, "invalid-n_k")
+
+
+# --------------------------------------------------------------------------
+# more items than one workgroup per CU: the persistent, pipelined variant
+# (workgroups take the valid splits round-robin); ragged and invalid lengths,
+# and more than 64 sequences (several chunks of the per-sequence item count)
+# --------------------------------------------------------------------------
+
+PERSISTENT = [
+    # B, Hq, Hkv, d, max_n_k, invalid sequences (n_k set to 0 or max_n_k + 1);
+    # over 2048 items, more than any number of resident one-item workgroups
+    (20, 32, 8, 128, 16384, (3, 11)),
+    (70, 1, 1, 64, 32768, (0, 65, 69)),
+]
+
+
+@functools.lru_cache(maxsize=2)
+def persistent_case(case):
+    B, Hq, Hkv, d, max_n_k, bad = case
+    rng = np.random.default_rng(B + d)
+    n_k = rng.integers(1, max_n_k + 1, size=B).astype(np.int32)
+    for i, bi in enumerate(bad):
+        n_k[bi] = 0 if i % 2 == 0 else max_n_k + 1
+    return W.random_case(B, Hq, Hkv, d, n_k, max_n_k=max_n_k, seed=B + 7, planted=True,
+                         pad_value=np.float16(np.nan))
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "B%d_Hq%d_Hkv%d_d%d" % c[:4])
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_persistent_ragged_invalid_parity(case, mode):
+    wl = persistent_case(case)
+    assert wl.B * wl.Hkv * ((wl.max_n_k + 1023) // 1024) > 2048
+    out, idx, _ = run_decode(wl, 32, mode, 17, with_scores=False)
+    for bi in case[5]:
+        assert np.isnan(out[bi]).all() and (idx[bi] == -1).all()
+    check_parity(wl, 32, mode, 17, "persistent")
 
 
 # --------------------------------------------------------------------------
