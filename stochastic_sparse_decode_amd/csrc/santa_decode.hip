@@ -411,26 +411,62 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         // 3. wait for every split of the group, merge
         double Z = 0.0, Olo = 0.0, Ohi = 0.0, rs = 0.0;
         {
-          float2 v0 = make_float2(-INFINITY, 0.f);  // (split max, split mass) of lane's split, chunk 0
+          // The slots of the first kRegChunks * 64 splits are read together
+          // and kept in registers (one round trip however many splits there
+          // are up to that bound); splits beyond it are polled and re-read a
+          // chunk of 64 at a time.
+          constexpr int kRegChunks = 4;
           auto read_slot = [&](int x, bool& ok) -> float2 {
             const uint64_t a = load_dev(slots + (x * G + g) * 2);
             const uint64_t c = load_dev(slots + (x * G + g) * 2 + 1);
             ok = (uint32_t)(a >> 32) == tag && (uint32_t)(c >> 32) == tag;
             return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
           };
-          // Poll every chunk of 64 splits.  A lane stops reading once its slot
+          float2 v[kRegChunks];
+          {
+            // every round re-reads all of the lane's slots, issuing every load
+            // before the first test so that one round is one round trip; a
+            // lane past the last split reads the last split's slot and ignores it
+            uint32_t spins = 0;
+            while (true) {
+              uint64_t ra[kRegChunks], rc[kRegChunks];
+#pragma unroll
+              for (int c = 0; c < kRegChunks; ++c) {
+                ra[c] = rc[c] = 0ull;
+                if (c * 64 < nsg) {  // the same in every lane
+                  const int x = min(c * 64 + lane, nsg - 1);
+                  ra[c] = load_dev(slots + (x * G + g) * 2);
+                  rc[c] = load_dev(slots + (x * G + g) * 2 + 1);
+                }
+              }
+              bool all = true;
+#pragma unroll
+              for (int c = 0; c < kRegChunks; ++c) {
+                v[c] = make_float2(__uint_as_float((uint32_t)ra[c]), __uint_as_float((uint32_t)rc[c]));
+                const bool ok = (uint32_t)(ra[c] >> 32) == tag && (uint32_t)(rc[c] >> 32) == tag;
+                all = all && (ok || c * 64 + lane >= nsg);
+              }
+              if (__ballot(!all) == 0ull) break;
+              __builtin_amdgcn_s_sleep(kPollSleep);
+              if (++spins > kSpinLimit) {
+                if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
+                break;
+              }
+            }
+#pragma unroll
+            for (int c = 0; c < kRegChunks; ++c)
+              if (c * 64 + lane >= nsg) v[c] = make_float2(-INFINITY, 0.f);
+          }
+          // Beyond the register chunks: a lane stops reading once its slot
           // carries this launch's tag, and the wave sleeps between rounds, so
           // waiting waves add little traffic to the memory channels that the
           // splits still streaming K are using.
-          for (int c0 = 0; c0 < nsg; c0 += 64) {
+          for (int c0 = kRegChunks * 64; c0 < nsg; c0 += 64) {
             const int x = c0 + lane;
             bool ok = x >= nsg;
             uint32_t spins = 0;
             while (true) {
-              if (!ok) {
-                const float2 v = read_slot(x, ok);
-                if (c0 == 0) v0 = v;
-              }
+              if (!ok) (void)read_slot(x, ok);
               if (__ballot(!ok) == 0ull) break;
               __builtin_amdgcn_s_sleep(kPollSleep);
               if (++spins > kSpinLimit) {
@@ -439,19 +475,20 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
               }
             }
           }
-          auto slot_value = [&](int c0, int x) -> float2 {
+          auto far_slot = [&](int x) -> float2 {
             bool ok;
-            return c0 == 0 ? v0 : (x < nsg ? read_slot(x, ok) : make_float2(-INFINITY, 0.f));
+            return x < nsg ? read_slot(x, ok) : make_float2(-INFINITY, 0.f);
           };
           float Mloc = -INFINITY;
-          for (int c0 = 0; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, slot_value(c0, c0 + lane).x);
+#pragma unroll
+          for (int c = 0; c < kRegChunks; ++c) Mloc = fmaxf(Mloc, v[c].x);
+          for (int c0 = kRegChunks * 64; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, far_slot(c0 + lane).x);
           const float M = wave_max(Mloc);
           uint64_t carry = 0;
-          for (int c0 = 0; c0 < nsg; c0 += 64) {
+          auto merge_chunk = [&](int c0, float2 sv) {
             const int x = c0 + lane;
-            const float2 v = slot_value(c0, x);
-            const float r = x < nsg ? expf(v.x - M) : 0.f;
-            const uint64_t Q = x < nsg ? (uint64_t)((double)v.y * (double)r) : 0ull;  // integer split mass
+            const float r = x < nsg ? expf(sv.x - M) : 0.f;
+            const uint64_t Q = x < nsg ? (uint64_t)((double)sv.y * (double)r) : 0ull;  // integer split mass
             const uint64_t inc = wave_incl_scan_u64(Q) + carry;
             if (s >= c0 && s < c0 + 64) {
               Olo = (double)readlane_u64(inc - Q, s - c0);
@@ -459,7 +496,11 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
               rs = (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), s - c0));
             }
             carry = readlane_u64(inc, 63);
-          }
+          };
+#pragma unroll
+          for (int c = 0; c < kRegChunks; ++c)
+            if (c * 64 < nsg) merge_chunk(c * 64, v[c]);
+          for (int c0 = kRegChunks * 64; c0 < nsg; c0 += 64) merge_chunk(c0, far_slot(c0 + lane));
           Z = (double)carry;
         }
 
@@ -632,7 +673,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       bernoulli_setup<D, G>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo);
       score_bernoulli<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo);
     } else {
-      score_rowmajor<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+      // two workgroups per CU: half the loads per buffer (the CU still has
+      // 16 KiB per wave in flight, and the registers saved avoid spills)
+      score_rowmajor<D, G, OCC == 2 ? 8 : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {

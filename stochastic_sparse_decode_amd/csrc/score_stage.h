@@ -11,13 +11,14 @@ constexpr int kPer = kSplit / 64;                // CDF elements per lane in the
 constexpr int kPad = kSplit + kSplit / 16 + 16;  // padded LDS row of one head (= 16 mod 32 banks)
 __device__ __forceinline__ int lidx(int j) { return j + (j >> 4); }  // bank-spread index
 
-template <int D, int G>
+// LB = wave-wide 16-byte loads per register buffer (two buffers in flight)
+template <int D, int G, int LB = 16>
 struct Geo {
   static constexpr int LPR = D / 8;        // lanes per key row (16 B each)
   static constexpr int RPW = 64 / LPR;     // key rows per wave-wide load
   static constexpr int U = LPR / G;        // wave-wide loads per reduction block
   static constexpr int BR = U * RPW;       // key rows per block
-  static constexpr int NB = (16 / U) > 0 ? (16 / U) : 1;   // blocks in flight per wave
+  static constexpr int NB = (LB / U) > 0 ? (LB / U) : 1;   // blocks per buffer
   static constexpr int ROWS_IT = NB * kWaves * BR;          // rows per workgroup iteration
   static_assert(U * G == LPR, "group size must divide the row width");
   static_assert(kSplit % ROWS_IT == 0, "an iteration never crosses the split end");
@@ -28,10 +29,10 @@ struct Geo {
 // lanes per row, U rows per lane per block so that the U*G partial dot
 // products of a lane reduce-scatter to exactly one (row, head) score per lane.
 // ---------------------------------------------------------------------------
-template <int D, int G>
+template <int D, int G, int LB = 16>
 __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int hk, int k0, int len,
                                                float* cdf, float* mx) {
-  using Gm = Geo<D, G>;
+  using Gm = Geo<D, G, LB>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / Gm::LPR, c = lane % Gm::LPR;
   const _Float16* Kb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
