@@ -294,6 +294,13 @@ __device__ __forceinline__ float2 load_dev(const float2* p) {
 __device__ __forceinline__ void store_dev(float2* p, float2 v) {
   __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Workgroup barrier that orders LDS accesses only: global loads and stores
+// in flight stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 // Wait until every memory operation this wave has issued has completed.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -328,22 +328,22 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     return it;
   };
 
-  // ---- per query head (wave g owns head g): weights, then publish and/or
-  // the sampling tail ----------------------------------------------------------
-  auto head = [&](const ItemCtx& it, int g, float* scb, int wb, bool do_publish, bool do_finish) {
-        const int s = it.s, len = it.len, k0 = it.k0, nsg = it.nsg, b = it.b, hk = it.hk, h0 = it.h0;
-        const bool is_last = it.is_last;
-        const uint32_t tag = sh.epoch;
-        uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
-        const uint32_t row = (uint32_t)(b * p.Hq + h0 + g);
-        float* orow = p.out + (size_t)row * D;
-        float* cg = scb + g * kPad;
+  // ---- per query head (wave g owns head g) ---------------------------------
+  // Fixed-point weights q of the keys lane*kPer .. lane*kPer+kPer-1 of head
+  // g, the lane's exclusive prefix and the split total (integers below 2^53
+  // held in doubles, so every partial sum is exact in any order).
+  struct Weights {
+    uint32_t q[kPer];
+    double excl, total;
+    float m;
+  };
+  auto weights = [&](const ItemCtx& it, int g, const float* scb, int wb, Weights& wt) {
+        const int len = it.len;
+        const float* cg = scb + g * kPad;
         float m = sh.wmax[wb][0][g];
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[wb][x][g]);
 
-        // 1. fixed-point weights of keys lane*kPer .. lane*kPer+kPer-1
-        double run[kPer];  // exact running sums inside the lane
         double acc = 0.0;
         {
           float sv[kPer];
@@ -356,24 +356,29 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             const float wv = exp_nonpos(lane * kPer + i < len ? sv[i] - m : -1000.f);
             const uint32_t q = (uint32_t)(wv * kFix);  // trunc(w * 2^31), exact: w <= 1
             acc += (double)q;
-            run[i] = acc;
+            wt.q[i] = q;
           }
         }
         const double incl = wave_incl_scan_exact(acc);
-        const double excl = incl - acc;  // exact: all values are integers below 2^53
-        const double total = readlane_f64(incl, 63);
+        wt.excl = incl - acc;  // exact: all values are integers below 2^53
+        wt.total = readlane_f64(incl, 63);
+        wt.m = m;
+  };
 
-        // 2. publish (split max, split mass); each half of the 16-byte slot
-        // carries the launch tag, so a reader accepts it only when both halves
-        // were written by this launch.  Split 0 cleared the output rows before
-        // its score stage; the wait makes sure those stores have completed
-        // (they have, long ago) before any split can see its slot and add.
-        if (do_publish) {
-        if (s == 0) wait_memory();
+  // Publish head g's (split max, split mass).
+  auto publish = [&](const ItemCtx& it, int g, const Weights& wt) {
+        const uint32_t tag = sh.epoch;
+        uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
+        // Each half of the 16-byte slot carries the launch tag, so a reader
+        // accepts it only when both halves were written by this launch.  Split
+        // 0 cleared the output rows before its score stage; the wait makes
+        // sure those stores have completed (they have, long ago) before any
+        // split can see its slot and add.
+        if (it.s == 0) wait_memory();
         if (lane == 0) {
           const uint64_t t = (uint64_t)tag << 32;
-          store_dev(slots + (s * G + g) * 2, t | __float_as_uint(m));
-          store_dev(slots + (s * G + g) * 2 + 1, t | __float_as_uint((float)total));
+          store_dev(slots + (it.s * G + g) * 2, t | __float_as_uint(wt.m));
+          store_dev(slots + (it.s * G + g) * 2 + 1, t | __float_as_uint((float)wt.total));
         }
         // this workgroup's share of the launch counter (its read has completed:
         // the value is in LDS); issued after the publish so that no wait before
@@ -382,9 +387,44 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           atomic_add_noret(p.ws.launches, my_add);
           counted = true;
         }
-        }
-        if (!do_finish) return;
+  };
 
+  // The sampling tail of head g in two halves: tail_a waits for the group's
+  // statistics, places the points and issues the first value loads; tail_b
+  // adds the value rows into the output.
+  constexpr int kVU = 4;  // value loads per lane per round of the gather
+  constexpr int LPR = D / 8, RPW = 64 / LPR;
+  static_assert(RPW * D <= kSplit / 2 && D % 64 == 0, "row-slot sums fit the head's counter area");
+  struct Gather {
+    int nsel;
+    uint32_t ee[kVU];
+    uint4 vv[kVU];
+  };
+  // One round of reads of head g's statistics slots: the first kRegChunks * 64
+  // splits, issued together (so a round is one round trip) and kept in
+  // registers; a lane past the last split reads the last split's slot.  The
+  // reads are unconditional, so the compiler knows exactly how many loads
+  // are younger than any earlier one it waits for.
+  constexpr int kRegChunks = 4;
+  struct Poll {
+    uint64_t ra[kRegChunks], rc[kRegChunks];
+  };
+  auto poll_issue = [&](const ItemCtx& it, int g, Poll& pl) {
+    const uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c) {
+      const int x = min(c * 64 + lane, it.nsg - 1);
+      pl.ra[c] = load_dev(slots + (x * G + g) * 2);
+      pl.rc[c] = load_dev(slots + (x * G + g) * 2 + 1);
+    }
+  };
+  auto tail_a = [&](const ItemCtx& it, int g, float* scb, const Weights& wt, Gather& gt) {
+        const int s = it.s, len = it.len, k0 = it.k0, nsg = it.nsg, b = it.b, hk = it.hk, h0 = it.h0;
+        const bool is_last = it.is_last;
+        const uint32_t tag = sh.epoch;
+        const uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
+        const uint32_t row = (uint32_t)(b * p.Hq + h0 + g);
+        float* cg = scb + g * kPad;
         // while the other splits finish: the points' uniforms, and for i.i.d.
         // draws the fp32 local CDF to search and cleared counters
         uint32_t* ug = uni + g * kUniRow;
@@ -400,9 +440,12 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           }
         }
         if (p.mode == 0) {
+          double cum = wt.excl;
 #pragma unroll
-          for (int i = 0; i < kPer; ++i)
-            if (lane * kPer + i < len) cg[lidx(lane * kPer + i)] = (float)(excl + run[i]);  // nondecreasing
+          for (int i = 0; i < kPer; ++i) {
+            cum += (double)wt.q[i];
+            if (lane * kPer + i < len) cg[lidx(lane * kPer + i)] = (float)cum;  // nondecreasing
+          }
           for (int i = lane; i < kSplit / 2; i += 64) cw[i] = 0u;
         }
         const double usys = p.mode == 2 ? uniform_f64(stream_block(p.seed, row, kTagSystematic, 0u).x) : 0.0;
@@ -415,7 +458,6 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           // and kept in registers (one round trip however many splits there
           // are up to that bound); splits beyond it are polled and re-read a
           // chunk of 64 at a time.
-          constexpr int kRegChunks = 4;
           auto read_slot = [&](int x, bool& ok) -> float2 {
             const uint64_t a = load_dev(slots + (x * G + g) * 2);
             const uint64_t c = load_dev(slots + (x * G + g) * 2 + 1);
@@ -424,33 +466,28 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           };
           float2 v[kRegChunks];
           {
-            // every round re-reads all of the lane's slots, issuing every load
-            // before the first test so that one round is one round trip; a
-            // lane past the last split reads the last split's slot and ignores it
-            uint32_t spins = 0;
-            while (true) {
-              uint64_t ra[kRegChunks], rc[kRegChunks];
-#pragma unroll
-              for (int c = 0; c < kRegChunks; ++c) {
-                ra[c] = rc[c] = 0ull;
-                if (c * 64 < nsg) {  // the same in every lane
-                  const int x = min(c * 64 + lane, nsg - 1);
-                  ra[c] = load_dev(slots + (x * G + g) * 2);
-                  rc[c] = load_dev(slots + (x * G + g) * 2 + 1);
-                }
-              }
+            Poll pl;
+            auto test = [&]() -> bool {
               bool all = true;
 #pragma unroll
               for (int c = 0; c < kRegChunks; ++c) {
-                v[c] = make_float2(__uint_as_float((uint32_t)ra[c]), __uint_as_float((uint32_t)rc[c]));
-                const bool ok = (uint32_t)(ra[c] >> 32) == tag && (uint32_t)(rc[c] >> 32) == tag;
+                v[c] = make_float2(__uint_as_float((uint32_t)pl.ra[c]), __uint_as_float((uint32_t)pl.rc[c]));
+                const bool ok = (uint32_t)(pl.ra[c] >> 32) == tag && (uint32_t)(pl.rc[c] >> 32) == tag;
                 all = all && (ok || c * 64 + lane >= nsg);
               }
-              if (__ballot(!all) == 0ull) break;
-              __builtin_amdgcn_s_sleep(kPollSleep);
-              if (++spins > kSpinLimit) {
-                if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
-                break;
+              return __ballot(!all) == 0ull;
+            };
+            poll_issue(it, g, pl);
+            if (!test()) {
+              uint32_t spins = 0;
+              while (true) {
+                __builtin_amdgcn_s_sleep(kPollSleep);
+                if (++spins > kSpinLimit) {
+                  if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
+                  break;
+                }
+                poll_issue(it, g, pl);
+                if (test()) break;
               }
             }
 #pragma unroll
@@ -540,38 +577,40 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           // difference at its two edges.  The edges are the same doubles in
           // the neighbouring lane or split, so every point is counted once.
           const double inv = (double)S / Z;
-          double X[kPer + 1];
-          X[0] = lane * kPer - 1 >= len - 1 ? Ohi : fmin(Olo + rs * excl, Ohi);
+          // edge e is the right edge of the lane's key e - 1 (e = 0: the
+          // lane's left edge); cum is the exact local CDF value there.  The
+          // last key of the sequence ends at t = 1.
+          auto edge = [&](int e, double cum) -> double {
+            return lane * kPer + e - 1 >= len - 1 ? Ohi : fmin(Olo + rs * cum, Ohi);
+          };
+          auto at_end = [&](int e, int n) -> int { return is_last && lane * kPer + e - 1 >= len - 1 ? S : n; };
+          // counts from the points below consecutive edges, one edge at a time
+          auto roll = [&](const auto& below) {
+            double cum = wt.excl;
+            int prev_n = below(0, cum);
+            nstart = prev_n;
 #pragma unroll
-          for (int i = 0; i < kPer; ++i)
-            X[i + 1] = lane * kPer + i >= len - 1 ? Ohi : fmin(Olo + rs * (excl + run[i]), Ohi);
-          int N[kPer + 1];
+            for (int i = 0; i < kPer; ++i) {
+              cum += (double)wt.q[i];
+              const int n = below(i + 1, cum);
+              cnt[i] = n - prev_n;
+              prev_n = n;
+            }
+          };
           if (p.mode == 2) {
             // t_k = (k + u) / S:  #{k : t_k Z < X} = ceil(y - u), clamped to [0, S]
-#pragma unroll
-            for (int i = 0; i <= kPer; ++i) N[i] = (int)fmin(fmax(ceil(X[i] * inv - usys), 0.0), (double)S);
+            roll([&](int e, double cum) {
+              return at_end(e, (int)fmin(fmax(ceil(edge(e, cum) * inv - usys), 0.0), (double)S));
+            });
           } else {
             // t_k = (k + u_k) / S:  #{k : t_k Z < X} = f + [u_f < y - f], f = floor(y)
-            double y[kPer + 1], f[kPer + 1];
-            uint32_t uf[kPer + 1];
-#pragma unroll
-            for (int i = 0; i <= kPer; ++i) {
-              y[i] = X[i] * inv;
-              f[i] = fmin(floor(y[i]), (double)S);
-              uf[i] = ug[min((int)f[i], S - 1)];
-            }
-#pragma unroll
-            for (int i = 0; i <= kPer; ++i)
-              N[i] = (int)f[i] + ((f[i] < (double)S && (double)uf[i] * 0x1.0p-24 < y[i] - f[i]) ? 1 : 0);
+            roll([&](int e, double cum) {
+              const double y = edge(e, cum) * inv;
+              const double f = fmin(floor(y), (double)S);
+              const uint32_t uf = ug[min((int)f, S - 1)];
+              return at_end(e, (int)f + ((f < (double)S && (double)uf * 0x1.0p-24 < y - f) ? 1 : 0));
+            });
           }
-          if (is_last) {  // the last key of the sequence ends at t = 1
-#pragma unroll
-            for (int i = 0; i <= kPer; ++i)
-              if (lane * kPer + i - 1 >= len - 1) N[i] = S;
-          }
-          nstart = N[0];
-#pragma unroll
-          for (int i = 0; i < kPer; ++i) cnt[i] = N[i + 1] - N[i];
         }
 
         // sampled indices (optional output), ascending
@@ -583,15 +622,17 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             for (int c = 0; c < cnt[i] && k < S; ++c) ix[k++] = k0 + lane * kPer + i;
         }
 
-        // 5. gather-add: the selected keys (key | count << 16) listed in key
-        // order in the head's uniform area, each value row read once and
-        // weighted by its count (count * v is exact in fp32)
+        // 5. gather: the selected keys (key | count << 16) listed in key order
+        // in the head's uniform area (each value row is read once and weighted
+        // by its count, an exact product in fp32); the first kVU rows per
+        // lane are requested here
         uint32_t sel = 0;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) sel |= (cnt[i] > 0 ? 1u : 0u) << i;
         const int nl = __popc(sel);
         const int incl_n = wave_incl_scan_dpp(nl);
         const int nsel = __builtin_amdgcn_readlane(incl_n, 63);
+        gt.nsel = nsel;
         if (nsel > 0) {
           uint32_t* list = ug;
           wave_lds_sync();  // every lane is done with the uniforms
@@ -605,30 +646,51 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             pos += on ? 1 : 0;
           }
           wave_lds_sync();
-          constexpr int LPR = D / 8, RPW = 64 / LPR, UNR = 4;
-          static_assert(RPW * D <= kSplit / 2 && D % 64 == 0, "row-slot sums fit the head's counter area");
+          const int r = lane / LPR, c = lane % LPR;
+          const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D + c * 8;
+#pragma unroll
+          for (int u = 0; u < kVU; ++u) {
+            const int i = u * RPW + r;
+            gt.ee[u] = i < nsel ? list[i] : 0u;
+            gt.vv[u] = i < nsel ? *(const uint4*)(Vb + (size_t)(gt.ee[u] & 0xffffu) * D) : make_uint4(0, 0, 0, 0);
+          }
+        }
+  };
+  auto tail_b = [&](const ItemCtx& it, int g, const Gather& gt) {
+        const int nsel = gt.nsel;
+        if (nsel == 0) return;
+        const int b = it.b, hk = it.hk, k0 = it.k0;
+        const uint32_t row = (uint32_t)(b * p.Hq + it.h0 + g);
+        float* orow = p.out + (size_t)row * D;
+        const uint32_t* list = uni + g * kUniRow;
+        uint32_t* cw = cntw + g * (kSplit / 2);
+        {
           const int r = lane / LPR, c = lane % LPR;
           const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D + c * 8;
           float a8[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) a8[e] = 0.f;
-          for (int i0 = 0; i0 < nsel; i0 += RPW * UNR) {
-            uint4 vv[UNR];
-            uint32_t ee[UNR];
+          auto add_rows = [&](const uint4 (&vv)[kVU], const uint32_t (&ee)[kVU]) {
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-              const int i = i0 + u * RPW + r;
-              ee[u] = i < nsel ? list[i] : 0u;
-              vv[u] = i < nsel ? *(const uint4*)(Vb + (size_t)(ee[u] & 0xffffu) * D) : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
+            for (int u = 0; u < kVU; ++u) {
               const float cf = (float)(ee[u] >> 16);
               float f8[8];
               unpack8(vv[u], f8);
 #pragma unroll
               for (int e = 0; e < 8; ++e) a8[e] = fmaf(cf, f8[e], a8[e]);
             }
+          };
+          add_rows(gt.vv, gt.ee);
+          for (int i0 = RPW * kVU; i0 < nsel; i0 += RPW * kVU) {
+            uint4 vv[kVU];
+            uint32_t ee[kVU];
+#pragma unroll
+            for (int u = 0; u < kVU; ++u) {
+              const int i = i0 + u * RPW + r;
+              ee[u] = i < nsel ? list[i] : 0u;
+              vv[u] = i < nsel ? *(const uint4*)(Vb + (size_t)(ee[u] & 0xffffu) * D) : make_uint4(0, 0, 0, 0);
+            }
+            add_rows(vv, ee);
           }
           // sum the RPW row slots through LDS (the i.i.d. counter area of the
           // head, free by now) so that lane l ends with features l, l + 64, ...:
@@ -675,7 +737,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     } else {
       // two workgroups per CU: half the loads per buffer (the CU still has
       // 16 KiB per wave in flight, and the registers saved avoid spills)
-      score_rowmajor<D, G, OCC == 2 ? 8 : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+      score_rowmajor<D, G, OCC == 2 ? (G > kWaves ? 4 : 8) : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -687,13 +749,22 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       asm volatile("" : "+v"(c));  // keeps the wait for the counter read here, after the stream
       sh.epoch = tag_of(c);
     }
-    __syncthreads();
+    lds_barrier();
     if (p.scores_out) {
       write_scores<G>(p, it.b, it.hk, it.k0, it.len, scb);
       __syncthreads();
     }
     // ---- from here on, wave g owns query head g ----------------------------
-    for (int g = w; g < G; g += kWaves) head(it, g, scb, wb, true, finish_now);
+    for (int g = w; g < G; g += kWaves) {
+      Weights wt;
+      weights(it, g, scb, wb, wt);
+      publish(it, g, wt);
+      if (finish_now) {
+        Gather gt;
+        tail_a(it, g, scb, wt, gt);
+        tail_b(it, g, gt);
+      }
+    }
   };
 
   if constexpr (OCC == 1) {
@@ -755,9 +826,15 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       const bool have = find(t, cur);
       if (have) start_item(cur, score_buf(cb), cb, false);
       if (prev.active)  // the previous item's statistics are published by now, or soon
-        for (int g = w; g < G; g += kWaves) head(prev, g, score_buf(cb ^ 1), cb ^ 1, false, true);
+        for (int g = w; g < G; g += kWaves) {
+          Weights wt;
+          Gather gt;
+          weights(prev, g, score_buf(cb ^ 1), cb ^ 1, wt);
+          tail_a(prev, g, score_buf(cb ^ 1), wt, gt);
+          tail_b(prev, g, gt);
+        }
       if (!have) break;
-      __syncthreads();  // every wave is done with the buffer the next item overwrites
+      lds_barrier();  // every wave is done with the buffer the next item overwrites
       prev = cur;
       cb ^= 1;
     }
