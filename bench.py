@@ -90,6 +90,16 @@ def make_workload(name):
     return W.bernoulli(B=8, n_k=32768, seed=1004), "Bernoulli case B=8, n_k=32768, 32q/8kv, d=128"
 
 
+def bernoulli_bytes(kept, wl, S):
+    """Bytes a Bernoulli step must read: for each (sequence, KV head) the
+    union of its G heads' kept features over all n_k keys (2 bytes each),
+    plus S value rows per KV head."""
+    G = wl.Hq // wl.Hkv
+    union = kept.view(wl.B, wl.Hkv, G, wl.d).bool().any(dim=2).sum(dim=2).cpu().numpy()  # [B][H_kv]
+    k_bytes = int((union.astype("int64") * wl.n_k.astype("int64")[:, None]).sum()) * 2
+    return k_bytes + wl.B * wl.Hkv * S * wl.d * 2
+
+
 def algorithmic_bytes(wl, S, dense=False):
     k_bytes = int(wl.n_k.astype("int64").sum()) * wl.Hkv * wl.d * 2
     if dense:
@@ -132,8 +142,10 @@ def timed(fn, sets, steps, warmup, graph=True):
     return start.elapsed_time(stop) / steps  # ms per step (= per launch: one launch per step)
 
 
-def cpu_baseline(wl, S, mode, seconds):
-    """Time the fp64 oracle on whole decode steps of the same workload (bounded)."""
+def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False):
+    """Time the fp64 oracle on whole decode steps of the same workload (bounded);
+    nbytes = the step's algorithmic bytes (the Bernoulli steps use seed 1, as
+    the timed GPU steps do, so their kept features and bytes are the same)."""
     from oracle import santa as O
     try:
         from threadpoolctl import threadpool_info
@@ -143,12 +155,15 @@ def cpu_baseline(wl, S, mode, seconds):
     t0 = time.perf_counter()
     n = 0
     while True:
-        O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, n, wl.scale)
+        if bernoulli:
+            O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, 1, wl.scale)
+        else:
+            O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, n, wl.scale)
         n += 1
         if time.perf_counter() - t0 >= seconds:
             break
     per_step = (time.perf_counter() - t0) / n
-    tbs = algorithmic_bytes(wl, S) / per_step / 1e12
+    tbs = nbytes / per_step / 1e12
     return {"value": tbs, "unit": "TB/s", "cores": threads, "kind": "oracle",
             "sample": "%d full decode step(s) of the same workload, %.2f s per step" % (n, per_step)}
 
@@ -203,7 +218,15 @@ def main():
     # outputs agree up to the order of the fp32 adds of the splits' shares
     assert (last - out).abs().max().item() <= 1e-5, "graph replay differs from eager launch"
     eager_ms = timed(step, sets, min(args.steps, 50), 2, graph=False) if not args.eager else ms
-    nbytes = algorithmic_bytes(wl, S)
+    if args.workload == "bernoulli":
+        # the kept features of the timed steps (every step uses seed 1)
+        kept = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        santa.santa_bernoulli_qk(q, sets[0][0], sets[0][1], nk, S, mode, 1, wl.scale, out=out, kept=kept,
+                                 workspace=ws)
+        torch.cuda.synchronize()
+        nbytes = bernoulli_bytes(kept, wl, S)
+    else:
+        nbytes = algorithmic_bytes(wl, S)
     gbs = nbytes / (ms * 1e-3) / 1e9
 
     dense_ms = None
@@ -242,7 +265,7 @@ def main():
                         "pct_hbm_peak": 100.0 * dbytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         res["speedup_vs_dense"] = dense_ms / ms
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, S, mode, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(wl, S, mode, args.cpu_seconds, nbytes, args.workload == "bernoulli")
     print(json.dumps(res))
 
 

@@ -78,9 +78,12 @@ struct Shared {
 // kept feature of a tile is one contiguous 128-byte row; only the union of
 // the group's kept features is read, and each contributes by add/subtract.
 // ---------------------------------------------------------------------------
+// info[j] = (feature index << 16) | keep/sign bits of the j-th kept feature of
+// the union; wt[j] = its fp16 query weight (+1, -1 or 0) for each head, and
+// zero for every j past the union (so padded steps add nothing).
 template <int D, int G>
 __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, int hk, bool write_kept,
-                                                Shared& sh, uint32_t* info) {
+                                                Shared& sh, uint32_t* info, uint4* wt) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
   // A_g = max |q_g| : wave g-loop over features
@@ -96,6 +99,7 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
   __syncthreads();
   bool any = false;
   uint32_t bits = 0;
+  uint32_t hw[4] = {0u, 0u, 0u, 0u};  // fp16 weights of the G heads, two per word
   if (tid < D) {
     const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hkv + hk), kTagBernoulli, (uint32_t)(tid >> 2));
     const double ub = (double)uniform_bits(word_of(blk, tid & 3));
@@ -105,6 +109,8 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
       // u * A < |q|  <=>  (x >> 8) * A < |q| * 2^24, exact in fp64
       const bool keep = ub * (double)sh.A[g] < (double)fabsf(qi) * 16777216.0;
       if (keep) bits |= (1u << (2 * g)) | ((qi < 0.f ? 1u : 0u) << (2 * g + 1));
+      const uint32_t h16 = keep ? (qi < 0.f ? 0xBC00u : 0x3C00u) : 0u;  // -1, +1 or 0 in fp16
+      hw[g >> 1] |= h16 << (16 * (g & 1));
       any |= keep;
       if (write_kept) p.kept_out[(size_t)(b * p.Hq + hk * G + g) * D + tid] = keep ? 1 : 0;
     }
@@ -114,17 +120,21 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
   const int before = __popcll(bal & ((1ull << lane) - 1ull));
   if (lane == 0 && w < 2) sh.wcount[w] = __popcll(bal);
   __syncthreads();
+  const int nu = (D > 64) ? sh.wcount[0] + sh.wcount[1] : sh.wcount[0];
   if (any) {
     const int pos = before + (w == 1 ? sh.wcount[0] : 0);
     info[pos] = ((uint32_t)tid << 16) | bits;
+    wt[pos] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
   }
-  if (tid == 0) sh.nu = (D > 64) ? sh.wcount[0] + sh.wcount[1] : sh.wcount[0];
+  for (int j = nu + tid; j < 128; j += kThreads) wt[j] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) sh.nu = nu;
   __syncthreads();
 }
 
 template <int D, int G>
 __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, int hk, int k0, int len,
-                                                float* cdf, float* mx, const Shared& sh, const uint32_t* info) {
+                                                float* cdf, float* mx, const Shared& sh, const uint32_t* info,
+                                                const uint4* wt) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, t4 = (lane >> 3) & 3, ko = lane & 7;
   const int ti = w * 4 + t4;  // tile of this lane inside the split (16 tiles)
@@ -139,31 +149,38 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
 
-  constexpr int UNR = 8;
+  // A lane takes the kept features j = 2 x + half of the list, two steps at a
+  // time: the two features' values of a key form one fp16 pair, and so do the
+  // head's weights for them, so one v_dot2 (fp32 accumulate) adds both.
+  constexpr int UNR = 8;  // steps (loads) per iteration, an even number
   const int steps = (nu + 1) / 2;
   for (int f0 = 0; f0 < steps; f0 += UNR) {
     uint4 kv[UNR];
-    uint32_t inf[UNR];
 #pragma unroll
     for (int x = 0; x < UNR; ++x) {
       const int fi = 2 * (f0 + x) + half;
-      const bool ok = fi < nu;
-      const uint32_t e = info[ok ? fi : 0];       // nu >= 1 here
-      inf[x] = ok ? e : (e & 0xffff0000u);          // past the list: keep nothing
+      const uint32_t e = info[fi < nu ? fi : 0];  // past the list: a kept row, weighted 0
       kv[x] = load_nt((const uint4*)(tb + (size_t)(e >> 16) * kTile + ko * 8));
     }
 #pragma unroll
-    for (int x = 0; x < UNR; ++x) {
-      float f[8];
-      unpack8(kv[x], f);
+    for (int x = 0; x < UNR; x += 2) {
+      const int j0 = 2 * (f0 + x) + half;  // j0 + 2 < 128: the table holds 128 entries
+      const uint4 wa = wt[j0], wc = wt[j0 + 2];
+      uint32_t wp[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const bool keep = (inf[x] >> (2 * g)) & 1u;
-        const bool neg = (inf[x] >> (2 * g + 1)) & 1u;
+        const uint32_t a = word_of(wa, g >> 1), c = word_of(wc, g >> 1);
+        wp[g] = __builtin_amdgcn_perm(c, a, (g & 1) ? 0x07060302u : 0x05040100u);
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = neg ? -f[e] : f[e];
-          acc[g][e] += keep ? t : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = word_of(kv[x], i), c = word_of(kv[x + 1], i);
+        const uint32_t klo = __builtin_amdgcn_perm(c, a, 0x05040100u);  // key 2i: (feature j0, j0 + 2)
+        const uint32_t khi = __builtin_amdgcn_perm(c, a, 0x07060302u);  // key 2i + 1
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          acc[g][2 * i] = __builtin_amdgcn_fdot2(as_h2(wp[g]), as_h2(klo), acc[g][2 * i], false);
+          acc[g][2 * i + 1] = __builtin_amdgcn_fdot2(as_h2(wp[g]), as_h2(khi), acc[g][2 * i + 1], false);
         }
       }
     }
@@ -272,7 +289,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   uint32_t* cntw = (uint32_t*)(smem + L::nbuf * L::sc_bytes + L::uni_bytes);  // [G][kSplit / 2]
   auto score_buf = [&](int i) -> float* { return (float*)(smem + (size_t)i * L::sc_bytes); };  // [G][kPad]
   __shared__ Shared sh;
-  __shared__ uint32_t binfo[128];  // Bernoulli kept-feature union
+  __shared__ uint32_t binfo[BERN ? 128 : 1];  // Bernoulli kept-feature union
+  __shared__ uint4 bwt[BERN ? 128 : 1];       // and its per-head fp16 weights
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
@@ -732,8 +750,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     // ---- score stage: all keys of the split, G query heads ----------------
     float mx[G];
     if constexpr (BERN) {
-      bernoulli_setup<D, G>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo);
-      score_bernoulli<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo);
+      bernoulli_setup<D, G>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo, bwt);
+      score_bernoulli<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt);
     } else {
       // two workgroups per CU: half the loads per buffer (the CU still has
       // 16 KiB per wave in flight, and the registers saved avoid spills)
