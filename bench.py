@@ -202,6 +202,7 @@ def main():
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     S = args.S
 
+    rm_sets = sets  # row-major K
     if args.workload == "bernoulli":
         sets = [(santa.santa_pack_k_feature_major(k), v) for k, v in sets]
         step = lambda kv: santa.santa_bernoulli_qk(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa
@@ -229,6 +230,12 @@ def main():
         nbytes = algorithmic_bytes(wl, S)
     gbs = nbytes / (ms * 1e-3) / 1e9
 
+    exact_ms = None
+    if args.workload == "bernoulli" and not args.no_dense:
+        # the same step with exact scores (all of K, row-major) for comparison
+        estep = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
+                                              workspace=ws)
+        exact_ms = timed(estep, rm_sets, args.steps, args.warmup, graph=not args.eager)
     dense_ms = None
     if not args.no_dense and args.workload != "bernoulli":
         dstep = lambda kv: santa.santa_dense_decode(q, kv[0], kv[1], nk, wl.scale, out=out, workspace=ws)  # noqa
@@ -259,6 +266,10 @@ def main():
                      "traffic": measured_traffic() if args.workload == "llama32k" and args.mode == "systematic"
                      and S == 128 else None},
     }
+    if exact_ms is not None:
+        res["exact_santa"] = {"us_per_step": exact_ms * 1000.0,
+                              "effective_GBs": algorithmic_bytes(wl, S) / (exact_ms * 1e-3) / 1e9}
+        res["speedup_vs_exact_santa"] = exact_ms / ms
     if dense_ms is not None:
         dbytes = algorithmic_bytes(wl, S, dense=True)
         res["dense"] = {"us_per_step": dense_ms * 1000.0, "effective_GBs": dbytes / (dense_ms * 1e-3) / 1e9,
