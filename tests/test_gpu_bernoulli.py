@@ -1,5 +1,7 @@
 """GPU parity of santa_bernoulli_qk and of the feature-major packing kernel."""
 
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -80,3 +82,37 @@ def test_bernoulli_equal_magnitudes_match_plain_decode():
     torch.cuda.synchronize()
     # same scores up to fp32 summation order, so indices agree except at boundaries
     assert (idx.cpu().numpy() != idx_b).mean() < 0.01
+
+
+# more items than resident one-item workgroups: the persistent Bernoulli
+# variant, with ragged and invalid lengths (n_k = 0 and n_k > max_n_k)
+@functools.lru_cache(maxsize=1)
+def persistent_case():
+    B, max_n_k = 36, 8192
+    rng = np.random.default_rng(77)
+    n_k = rng.integers(1, max_n_k + 1, size=B).astype(np.int32)
+    n_k[5], n_k[30] = 0, max_n_k + 1
+    return W.random_case(B, 32, 8, 128, n_k, max_n_k=max_n_k, seed=78, pad_value=np.float16(np.nan))
+
+
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_bernoulli_persistent_parity(mode):
+    wl = persistent_case()
+    assert wl.B * wl.Hkv * (wl.max_n_k // 1024) > 2048
+    S, seed = 64, 31 + mode
+    print("[bernoulli] persistent mode=%d B=%d n_k=%s" % (mode, wl.B, list(wl.n_k)[:6]), flush=True)
+    out_g, idx_g, sc_g, kept_g = run_bernoulli(wl, S, mode, seed)
+    valid = (wl.n_k >= 1) & (wl.n_k <= wl.max_n_k)
+    assert np.isnan(out_g[~valid]).all() and (idx_g[~valid] == -1).all()
+    out_o, idx_o, kept_o, det = O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, seed, wl.scale,
+                                                   return_detail=True)
+    assert np.array_equal(kept_g[valid], kept_o[valid])
+    rep = P.compare_indices(idx_g, idx_o, det, P.BAND)
+    print("   %s" % rep, flush=True)
+    assert rep.bad == 0
+    est = P.oracle_estimate_from_indices(wl.V, idx_g, wl.n_k, wl.Hq, S)
+    assert np.abs(out_g[valid] - est[valid]).max() <= P.OUT_TOL
+    q_t, _, _ = O.bernoulli_queries(wl.q, wl.Hkv, seed)
+    s_o = O.all_scores(q_t, wl.K, wl.n_k, wl.scale)
+    m = ~np.isnan(s_o)
+    assert np.abs(sc_g[m] - s_o[m]).max() <= 1e-4 * max(1.0, np.abs(s_o[m]).max())
