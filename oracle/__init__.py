@@ -8,9 +8,10 @@ it, and there is no CPU fallback that routes through it.
 The oracle is a plain, slow, obviously correct fp64 NumPy implementation of
 what the method computes, written from the abstract "Stochastic Sparse
 Attention for Memory-Bound Inference" (arXiv 2605.01910; both versions of the
-abstract) plus the readings that abstract leaves open, which are listed in
-the design doc of this repository.  It shares no code, tables or constants with the
-HIP path; the only thing both sides share is the seeded input generator module
+abstract) plus the readings of what that abstract leaves open, each stated in
+the docstring of the function that depends on it.  It shares no code, tables
+or constants with the HIP path; the only thing both sides share is the seeded
+input generator module
 ``stochastic_sparse_decode_amd.workloads``, which contains none of the
 method's arithmetic.
 

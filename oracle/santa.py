@@ -15,10 +15,12 @@ Source: "Stochastic Sparse Attention for Memory-Bound Inference"
 * Bernoulli qK^T sampling uses stochastic ternary queries to read fewer key
   features in the score stage (the sentence introducing it).
 
-Everything below that the abstract leaves open follows the readings listed in
-the design doc (scale argument, inverse-CDF sampling, equal-probability strata,
-weights 1/S, duplicates counted, half-open CDF intervals, key-index CDF order,
-the Philox stream layout, keep probability |q_i| / max|q|).
+Where the abstract leaves a step open, the functions below take these
+readings: an explicit softmax scale argument; i.i.d. draws by the inverse CDF
+of sorted uniforms; equal-probability strata [k/S, (k+1)/S); weights 1/S with
+duplicates counted; half-open CDF intervals (a point on F_j selects j + 1);
+the CDF in key-index order; the Philox stream layout of ``philox``; keep
+probability |q_i| / max|q| for the ternary queries.
 
 Per-head functions take 1-D / 2-D float64 arrays and are written to be read
 against those statements; the batched drivers only loop over (b, h).
