@@ -22,10 +22,11 @@ philox   Philox4x32-10 counter-based generator (Salmon et al., SC'11) and the
 santa    scores, softmax distribution, stratum points, inverse-CDF search,
          gather-average estimate, dense attention and the Bernoulli qK^T mode.
 moments  exact first and second moments of the three estimators.
+fp8      exact decoding of the OCP E4M3 bytes of the fp8 key cache.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against something other than itself (known-answer vectors, a library
 routine, closed forms, brute-force enumeration or fine-grid integration).
 """
 
-from . import philox, santa, moments  # noqa: F401
+from . import fp8, philox, santa, moments  # noqa: F401

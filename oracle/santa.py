@@ -31,7 +31,7 @@ Mode numbers: 0 = i.i.d. multinomial, 1 = stratified, 2 = systematic.
 
 import numpy as np
 
-from . import philox
+from . import fp8, philox
 
 IID = 0
 STRATIFIED = 1
@@ -260,6 +260,16 @@ def bernoulli_decode(q, K, V, n_k, S, mode, seed, scale, return_detail=False):
         return out, idx, kept, detail
     out, idx = res
     return out, idx, kept
+
+
+def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, score_override=None,
+                      return_detail=False):
+    """SANTA decode step on an fp8 key cache: the keys are
+    K = k_scale[b, h_kv] * decode(K8) (OCP E4M3 bytes, decoded exactly into
+    fp64 by ``fp8.dequantize``); every later step is ``santa_decode``'s."""
+    K = fp8.dequantize(K8, k_scale)
+    return santa_decode(q, K, V, n_k, S, mode, seed, scale, score_override=score_override,
+                        return_detail=return_detail)
 
 
 def all_scores(q, K, n_k, scale):

@@ -191,3 +191,29 @@ def feature_major(K, tile=64):
     if n % tile:
         raise ValueError("max_n_k must be a multiple of %d" % tile)
     return np.ascontiguousarray(K.reshape(B, Hkv, n // tile, tile, d).transpose(0, 1, 2, 4, 3))
+
+
+def quantize_keys_fp8(K, n_k):
+    """fp8 key cache for K (B, H_kv, max_n_k, d) fp16: (K8 uint8, k_scale).
+
+    One fp32 scale per (sequence, KV head), k_scale = max |K| / 448 over the
+    sequence's valid rows (1 when that maximum is 0 or the length is invalid),
+    and K8 = the OCP E4M3 bytes of K / k_scale, rounded to nearest even (by
+    torch's float8_e4m3fn conversion); so the cache holds
+    K ~ k_scale * decode(K8).  Rows past n_k keep whatever K / k_scale gives
+    (NaN padding stays NaN).  This is input preparation, as when a serving
+    system writes its cache; the decode step only reads K8 and k_scale.
+    """
+    import torch
+
+    B, Hkv, max_n_k, d = K.shape
+    k_scale = np.ones((B, Hkv), dtype=np.float32)
+    for b in range(B):
+        n = int(n_k[b])
+        if not 1 <= n <= max_n_k:
+            continue
+        amax = np.abs(K[b, :, :n].astype(np.float32)).max(axis=(1, 2))
+        k_scale[b] = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    x = torch.from_numpy(K.astype(np.float32) / k_scale[:, :, None, None])
+    K8 = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return K8, k_scale
