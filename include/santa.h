@@ -15,6 +15,8 @@
  *   - santa_dense_decode: the exact softmax(scale q K^T) V, reading all of K
  *     and V, split over the key sequence (FlashDecoding style; the baseline
  *     the abstract compares against).
+ *   - santa_decode_fp8k: santa_decode on a key cache stored as 8-bit floats
+ *     (OCP E4M3) with one scale per (sequence, KV head).
  *   - santa_bernoulli_qk: the abstract's Bernoulli qK^T sampling, which
  *     replaces each query by a stochastic ternary vector so that only the kept
  *     key features are read in the score stage, followed by the SANTA value
@@ -134,6 +136,24 @@ int santa_decode(const santa_problem* problem, const void* q, const void* K, con
                  const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
                  int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/* SANTA decode step on an fp8 key cache (the same estimator as santa_decode;
+ * the abstract calls SANTA complementary to quantization, and keys are almost
+ * all of its bytes).
+ *   K8      [B][H_kv][max_n_k][d] bytes, each an OCP 8-bit floating point
+ *           number in the E4M3 encoding (sign, 4 exponent bits with bias 7, 3
+ *           mantissa bits; S.1111.111 is NaN; largest finite magnitude 448)
+ *   k_scale [B][H_kv] fp32, device memory: the cache holds
+ *           K[b][h][j][i] = k_scale[b][h] * E4M3(K8[b][h][j][i])
+ * Scores are scale * k_scale[b][h/G] * <q, decoded K8 row>, the E4M3 values
+ * converted exactly to fp16 and accumulated in fp32.  V stays fp16 and every
+ * other argument, output and error is as for santa_decode.  d = 64 supports
+ * G <= 4 (SANTA_ERR_UNSUPPORTED for G = 8); k_scale must be 4-byte aligned and
+ * K8 16-byte aligned. */
+int santa_decode_fp8k(const santa_problem* problem, const void* q, const void* K8, const float* k_scale,
+                      const void* V, const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
+                      int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* Exact decode attention: out[b][h] = softmax(scale q K^T) V over j < n_k[b]
  * (the FlashDecoding-style baseline named in the abstract's fifth sentence). */

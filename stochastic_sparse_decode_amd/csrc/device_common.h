@@ -104,11 +104,12 @@ __device__ __forceinline__ float dpp(float x) {
 // Reduce-scatter across the LPR lanes of a key row.  On entry every lane holds
 // NV = LPR partial sums v[0..NV); on exit lane (lane % LPR) holds in v[0] the
 // full sum of combination index (lane % LPR).  Partner lanes are paired with
-// the masks 8, 7, 2, 1 (LPR = 16) or 7, 2, 1 (LPR = 8); the half kept by a lane
-// is chosen by one bit of its lane id that differs between partners.
+// the masks 8, 7, 2, 1 (LPR = 16), 7, 2, 1 (LPR = 8) or 2, 1 (LPR = 4); the
+// half kept by a lane is chosen by one bit of its lane id that differs between
+// partners.
 template <int LPR>
 __device__ __forceinline__ void row_reduce_scatter(float* v, int lane) {
-  static_assert(LPR == 8 || LPR == 16, "row width");
+  static_assert(LPR == 4 || LPR == 8 || LPR == 16, "row width");
   if constexpr (LPR == 16) {
     const bool hi = (lane >> 3) & 1;
 #pragma unroll
@@ -118,7 +119,7 @@ __device__ __forceinline__ void row_reduce_scatter(float* v, int lane) {
       v[i] = keep + dpp<kDppRor8>(send);
     }
   }
-  {
+  if constexpr (LPR >= 8) {
     const bool hi = (lane >> 2) & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {

@@ -52,6 +52,7 @@ struct DecodeParams {
   int32_t* idx_out;     // [B][Hq][S] or null
   float* scores_out;    // [B][Hq][max_n_k] or null
   uint8_t* kept_out;    // [B][Hq][D] or null (Bernoulli)
+  const float* k_scale; // [B][Hkv] scales of an fp8 key cache (K = k_scale * decode(K8)), else null
   uint64_t seed;
   int D, G;
   int occ;              // sampling kernel variant: 1 = one item per workgroup, 2 = items taken in turn
@@ -59,13 +60,16 @@ struct DecodeParams {
 };
 static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");
 
-enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2 };
+enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2, kOpDecodeF8 = 3 };
+
+// Key cache kinds of the sampling kernel.
+enum KeyKind { kKeyF16 = 0, kKeyBernoulli = 1, kKeyF8 = 2 };
 
 // Resident-workgroup capacity of the current device for a kernel variant.
-int decode_capacity(int D, int G, bool bernoulli, int occ);
+int decode_capacity(int D, int G, int key_kind, int occ);
 int dense_capacity(int D, int G);
 
-hipError_t launch_decode(const DecodeParams& p, bool bernoulli, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int key_kind, hipStream_t stream);
 hipError_t launch_dense(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_pack_feature_major(const void* K, void* K_fm, int B, int Hkv, int max_n_k, int D,
                                      hipStream_t stream);

@@ -79,7 +79,7 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Resident-workgroup capacity per (device, kernel variant), computed once.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 3 /*kernel*/ * 2 /*workgroups per CU*/;
+constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 4 /*kernel*/ * 2 /*workgroups per CU*/;
 std::mutex g_cap_mutex;
 int g_cap[kMaxDevices][kVariants];
 
@@ -89,6 +89,10 @@ int variant_index(int D, int G, int kind, int occ) {
   return ((kind * 2 + di) * 4 + gi) * 2 + (occ == 2 ? 1 : 0);
 }
 
+int key_kind(int op) {
+  return op == santa::kOpBernoulli ? santa::kKeyBernoulli : op == santa::kOpDecodeF8 ? santa::kKeyF8 : santa::kKeyF16;
+}
+
 int capacity(int D, int G, int kind, int occ) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -96,7 +100,7 @@ int capacity(int D, int G, int kind, int occ) {
   int& slot = g_cap[dev][variant_index(D, G, kind, occ)];
   if (slot == 0) {
     slot = kind == santa::kOpDense ? santa::dense_capacity(D, G)
-                                   : santa::decode_capacity(D, G, kind == santa::kOpBernoulli, occ);
+                                   : santa::decode_capacity(D, G, key_kind(kind), occ);
   }
   return slot;
 }
@@ -156,9 +160,14 @@ int choose_grid(DecodeParams& d, int kind) {
 
 int sampled_step(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
-                 uint8_t* kept_out, void* ws, size_t ws_bytes, void* stream, int kind) {
+                 uint8_t* kept_out, const float* k_scale, void* ws, size_t ws_bytes, void* stream, int kind) {
   int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes);
   if (st != SANTA_OK) return st;
+  if (kind == santa::kOpDecodeF8) {
+    if (!k_scale) return SANTA_ERR_NULL;
+    if (!aligned(k_scale, 4)) return SANTA_ERR_ALIGN;
+    if (group_size(p) > p->head_dim / 16) return SANTA_ERR_UNSUPPORTED;  // d = 64 with G = 8
+  }
   if (S < 1 || S > SANTA_MAX_S) return SANTA_ERR_SHAPE;
   if (mode != SANTA_IID && mode != SANTA_STRATIFIED && mode != SANTA_SYSTEMATIC) return SANTA_ERR_MODE;
   if ((indices_out && !aligned(indices_out, 4)) || (scores_out && !aligned(scores_out, 4))) return SANTA_ERR_ALIGN;
@@ -167,12 +176,13 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   d.idx_out = indices_out;
   d.scores_out = scores_out;
   d.kept_out = kept_out;
+  d.k_scale = k_scale;
   d.S = S;
   d.mode = mode;
   d.seed = seed;
   st = choose_grid(d, kind);
   if (st != SANTA_OK) return st;
-  const hipError_t e = santa::launch_decode(d, kind == santa::kOpBernoulli, (hipStream_t)stream);
+  const hipError_t e = santa::launch_decode(d, key_kind(kind), (hipStream_t)stream);
   return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
 }
 
@@ -188,16 +198,24 @@ size_t santa_workspace_bytes(const santa_problem* problem) {
 int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, workspace,
-                      workspace_bytes, stream, santa::kOpDecode);
+  return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, nullptr,
+                      workspace, workspace_bytes, stream, santa::kOpDecode);
+}
+
+int santa_decode_fp8k(const santa_problem* problem, const void* q, const void* K8, const float* k_scale,
+                      const void* V, const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
+                      int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return sampled_step(problem, q, K8, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, k_scale,
+                      workspace, workspace_bytes, stream, santa::kOpDecodeF8);
 }
 
 int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* K_fm, const void* V,
                        const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
                        int32_t* indices_out, float* scores_out, uint8_t* kept_out, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  return sampled_step(problem, q, K_fm, V, n_k, S, mode, seed, out, indices_out, scores_out, kept_out, workspace,
-                      workspace_bytes, stream, santa::kOpBernoulli);
+  return sampled_step(problem, q, K_fm, V, n_k, S, mode, seed, out, indices_out, scores_out, kept_out, nullptr,
+                      workspace, workspace_bytes, stream, santa::kOpBernoulli);
 }
 
 int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,

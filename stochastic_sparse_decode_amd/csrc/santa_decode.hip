@@ -281,8 +281,9 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 //  pipeline them: stream item k and publish its statistics, then finish item
 //  k - 1 (whose group has normally published everything by then), so the
 //  sampling tail of one item never stalls the K stream of the next.
-template <int D, int G, bool BERN, int OCC>
+template <int D, int G, int KIND, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
+  constexpr bool BERN = KIND == kKeyBernoulli;
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G, OCC>;
   uint32_t* uni = (uint32_t*)(smem + L::nbuf * L::sc_bytes);                  // [G][kUniRow]
@@ -752,6 +753,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     if constexpr (BERN) {
       bernoulli_setup<D, G>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo, bwt);
       score_bernoulli<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt);
+    } else if constexpr (KIND == kKeyF8) {
+      score_rowmajor_f8<D, G, OCC == 2 ? (G > kWaves ? 4 : 8) : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     } else {
       // two workgroups per CU: half the loads per buffer (the CU still has
       // 16 KiB per wave in flight, and the registers saved avoid spills)
@@ -865,55 +868,74 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 template <int D, int G, int OCC>
 size_t lds_bytes() { return Lds<D, G, OCC>::bytes; }
 
-template <int D, int G, bool BERN, int OCC>
+template <int D, int G, int KIND, int OCC>
 int capacity_t() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  auto fn = decode_kernel<D, G, BERN, OCC>;
+  auto fn = decode_kernel<D, G, KIND, OCC>;
   const size_t lds = lds_bytes<D, G, OCC>();
   (void)hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess) return 0;
   return per_cu * cus;
 }
 
-template <int D, int G, bool BERN, int OCC>
+template <int D, int G, int KIND, int OCC>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const size_t lds = lds_bytes<D, G, OCC>();
-  hipLaunchKernelGGL((decode_kernel<D, G, BERN, OCC>), dim3(p.grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, G, KIND, OCC>), dim3(p.grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-template <bool BERN, int OCC>
+// (D, G, key kind) combinations that are built; the fp8 score stage needs
+// G <= D / 16
+template <int D, int G, int KIND>
+constexpr bool built() { return KIND != kKeyF8 || fp8_supported<D, G>(); }
+
+template <int KIND, int OCC>
 hipError_t dispatch(const DecodeParams& p, hipStream_t stream) {
-#define SANTA_CASE(DD, GG) \
-  if (p.D == DD && p.G == GG) return launch_t<DD, GG, BERN, OCC>(p, stream);
+#define SANTA_CASE(DD, GG)                                                                     \
+  if constexpr (built<DD, GG, KIND>())                                                         \
+    if (p.D == DD && p.G == GG) return launch_t<DD, GG, KIND, OCC>(p, stream);
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
   return hipErrorInvalidValue;
 }
 
-template <bool BERN, int OCC>
+template <int KIND, int OCC>
 int capacity(int D, int G) {
-#define SANTA_CASE(DD, GG) \
-  if (D == DD && G == GG) return capacity_t<DD, GG, BERN, OCC>();
+#define SANTA_CASE(DD, GG)                                                                     \
+  if constexpr (built<DD, GG, KIND>())                                                         \
+    if (D == DD && G == GG) return capacity_t<DD, GG, KIND, OCC>();
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
   return 0;
 }
 
-}  // namespace
-
-int decode_capacity(int D, int G, bool bernoulli, int occ) {
-  if (occ == 2) return bernoulli ? capacity<true, 2>(D, G) : capacity<false, 2>(D, G);
-  return bernoulli ? capacity<true, 1>(D, G) : capacity<false, 1>(D, G);
+template <int OCC>
+int capacity_kind(int D, int G, int key_kind) {
+  if (key_kind == kKeyBernoulli) return capacity<kKeyBernoulli, OCC>(D, G);
+  if (key_kind == kKeyF8) return capacity<kKeyF8, OCC>(D, G);
+  return capacity<kKeyF16, OCC>(D, G);
 }
 
-hipError_t launch_decode(const DecodeParams& p, bool bernoulli, hipStream_t stream) {
-  if (p.occ == 2) return bernoulli ? dispatch<true, 2>(p, stream) : dispatch<false, 2>(p, stream);
-  return bernoulli ? dispatch<true, 1>(p, stream) : dispatch<false, 1>(p, stream);
+template <int OCC>
+hipError_t dispatch_kind(const DecodeParams& p, int key_kind, hipStream_t stream) {
+  if (key_kind == kKeyBernoulli) return dispatch<kKeyBernoulli, OCC>(p, stream);
+  if (key_kind == kKeyF8) return dispatch<kKeyF8, OCC>(p, stream);
+  return dispatch<kKeyF16, OCC>(p, stream);
+}
+
+}  // namespace
+
+int decode_capacity(int D, int G, int key_kind, int occ) {
+  return occ == 2 ? capacity_kind<2>(D, G, key_kind) : capacity_kind<1>(D, G, key_kind);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int key_kind, hipStream_t stream) {
+  return p.occ == 2 ? dispatch_kind<2>(p, key_kind, stream) : dispatch_kind<1>(p, key_kind, stream);
 }
 
 }  // namespace santa

@@ -84,6 +84,96 @@ __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int
   for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Score stage, fp8 key cache: rows of D bytes (OCP E4M3), 16 bytes = 16
+// features per lane, LPR = D / 16 lanes per row.  Each 16-byte piece becomes
+// eight fp16 pairs (the E4M3 -> fp16 conversion is exact) that are dotted
+// with the query's fp16 pairs (v_dot2_f32_f16, fp32 accumulate); the sum is
+// scaled by scale * k_scale[b, h_kv] once.  Same schedule as the fp16 stage.
+// ---------------------------------------------------------------------------
+template <int D, int G, int LB = 16>
+struct GeoF8 {
+  static constexpr int LPR = D / 16;       // lanes per key row (16 B each)
+  static constexpr int RPW = 64 / LPR;     // key rows per wave-wide load
+  static constexpr int U = LPR / G;        // wave-wide loads per reduction block
+  static constexpr int BR = U * RPW;       // key rows per block
+  static constexpr int NB = (LB / U) > 0 ? (LB / U) : 1;   // blocks per buffer
+  static constexpr int ROWS_IT = NB * kWaves * BR;          // rows per workgroup iteration
+  static_assert(U >= 1 && U * G == LPR, "group size must divide the row width");
+  static_assert(kSplit % ROWS_IT == 0, "an iteration never crosses the split end");
+};
+
+template <int D, int G>
+constexpr bool fp8_supported() { return G <= D / 16; }
+
+template <int D, int G, int LB = 16>
+__device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, int hk, int k0, int len,
+                                                  float* cdf, float* mx) {
+  using Gm = GeoF8<D, G, LB>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane / Gm::LPR, c = lane % Gm::LPR;
+  const uint8_t* Kb = (const uint8_t*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
+  const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
+  uint4 qv[G][2];  // features c*16 .. c*16+15 of each head, as fp16 pairs
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qv[g][0] = *(const uint4*)(qb + g * D + c * 16);
+    qv[g][1] = *(const uint4*)(qb + g * D + c * 16 + 8);
+  }
+  const float sc = p.scale * p.k_scale[b * p.Hkv + hk];
+
+  const int my_u = c / G, my_g = c % G;
+  float m_run = -INFINITY;
+  constexpr int NIT = kSplit / Gm::ROWS_IT;
+  uint4 buf[2][Gm::NB][Gm::U];
+  auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb)
+#pragma unroll
+      for (int u = 0; u < Gm::U; ++u) {
+        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, len - 1);
+        bb[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 16));
+      }
+  };
+  issue(buf[0], 0);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int base = it * Gm::ROWS_IT;
+    if (it + 1 < NIT) issue(buf[(it + 1) & 1], base + Gm::ROWS_IT);
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb) {
+      float v[Gm::LPR];
+#pragma unroll
+      for (int u = 0; u < Gm::U; ++u) {
+        // fp16 pairs of features (2m, 2m+1) of the lane's 16
+        uint32_t kh[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wd = word_of(buf[it & 1][nb][u], i);
+          kh[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.0f, false));
+          kh[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.0f, true));
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            acc = __builtin_amdgcn_fdot2(as_h2(kh[m]), as_h2(word_of(qv[g][m >> 2], m & 3)), acc, false);
+          v[u * G + g] = acc;
+        }
+      }
+      row_reduce_scatter<Gm::LPR>(v, lane);
+      // rows < kSplit always; rows >= len land in unused LDS slots
+      const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
+      const float s = v[0] * sc;
+      cdf[my_g * kPad + lidx(row)] = s;
+      m_run = fmaxf(m_run, row < len ? s : -INFINITY);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+}
+
 // Copy the split's scores from LDS to scores_out (debug output), coalesced.
 template <int G>
 __device__ __forceinline__ void write_scores(const DecodeParams& p, int b, int hk, int k0, int len, const float* cdf) {

@@ -55,6 +55,8 @@ def library():
     lib.santa_workspace_bytes.restype = sz
     lib.santa_decode.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, sz, vp]
     lib.santa_decode.restype = ctypes.c_int
+    lib.santa_decode_fp8k.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, sz, vp]
+    lib.santa_decode_fp8k.restype = ctypes.c_int
     lib.santa_dense_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.santa_dense_decode.restype = ctypes.c_int
     lib.santa_bernoulli_qk.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, vp, sz, vp]
@@ -153,6 +155,41 @@ def santa_decode(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, sco
                                 int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
                                 _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "santa_decode")
+    return out
+
+
+def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
+                      workspace=None, stream=None):
+    """SANTA decode step on an fp8 key cache; returns ``out`` (B, H_q, d) fp32.
+
+    K8 (B, H_kv, max_n_k, d) uint8 holds OCP E4M3 bytes and k_scale (B, H_kv)
+    fp32 their scales (K = k_scale * decoded K8); q, V, n_k and the optional
+    outputs are as for ``santa_decode``.
+    """
+    dev = q.device
+    for t, nm in ((q, "q"), (V, "V")):
+        _expect(t, nm, torch.float16, dev)
+    _expect(K8, "K8", torch.uint8, dev, 4)
+    _expect(k_scale, "k_scale", torch.float32, dev, 2)
+    _expect(n_k, "n_k", torch.int32, dev, 1)
+    if tuple(V.shape) != tuple(K8.shape) or tuple(k_scale.shape) != tuple(K8.shape[:2]):
+        raise ValueError("K8 %s, V %s and k_scale %s do not match" % (tuple(K8.shape), tuple(V.shape),
+                                                                      tuple(k_scale.shape)))
+    prob = problem(q, K8, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.float32, dev)
+    if indices is not None:
+        _expect(indices, "indices", torch.int32, dev)
+    if scores is not None:
+        _expect(scores, "scores", torch.float32, dev)
+    if workspace is None:
+        workspace = new_workspace(prob, dev)
+    mode = MODES.get(mode, mode)
+    st = library().santa_decode_fp8k(ctypes.byref(prob), _ptr(q), _ptr(K8), _ptr(k_scale), _ptr(V), _ptr(n_k),
+                                     int(S), int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
+                                     _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "santa_decode_fp8k")
     return out
 
 

@@ -93,3 +93,19 @@ def test_binding_has_no_fallback(tmp_path, monkeypatch):
     monkeypatch.setattr(santa, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         santa.library()
+
+
+def test_fp8k_host_checks(lib):
+    vp = ctypes.c_void_p
+    p = _prob()
+    nb = santa.workspace_bytes(p)
+
+    def call(prob, k_scale, ws_bytes=nb):
+        return lib.santa_decode_fp8k(ctypes.byref(prob), vp(FAKE), vp(FAKE), vp(k_scale), vp(FAKE), vp(FAKE), 128,
+                                     2, 0, vp(FAKE), None, None, vp(FAKE), ws_bytes, None)
+
+    assert call(p, 0) == 1                     # k_scale missing
+    assert call(p, FAKE + 2) == 4              # k_scale not 4-byte aligned
+    p64 = _prob(head_dim=64, num_q_heads=64, num_kv_heads=8)
+    assert call(p64, FAKE, santa.workspace_bytes(p64)) == 3   # d = 64 with G = 8 is not built
+    assert call(p, FAKE, 16) == 5              # workspace too small
