@@ -65,7 +65,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama32k", choices=["llama32k", "batched", "sweep131k", "bernoulli"])
+    ap.add_argument("--workload", default="llama32k",
+                    choices=["llama32k", "batched", "sweep131k", "bernoulli", "llama32k-fp8k"])
     ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid"])
     ap.add_argument("--S", type=int, default=128)
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of distinct KV copies to rotate over")
@@ -82,6 +83,9 @@ def make_workload(name):
     from stochastic_sparse_decode_amd import workloads as W
     if name == "llama32k":
         return W.llama(B=1, n_k=32768, seed=1001), "Llama-3.1-8B decode layer, B=1, 32q/8kv, d=128, n_k=32768"
+    if name == "llama32k-fp8k":
+        return (W.llama(B=1, n_k=32768, seed=1001),
+                "Llama-3.1-8B decode layer, B=1, 32q/8kv, d=128, n_k=32768, fp8 (OCP E4M3) key cache")
     if name == "batched":
         return (W.llama(B=16, n_k_range=(8192, 32768), seed=1002),
                 "Llama-3.1-8B decode layer, B=16, n_k~U[8192,32768], 32q/8kv, d=128")
@@ -98,6 +102,12 @@ def bernoulli_bytes(kept, wl, S):
     union = kept.view(wl.B, wl.Hkv, G, wl.d).bool().any(dim=2).sum(dim=2).cpu().numpy()  # [B][H_kv]
     k_bytes = int((union.astype("int64") * wl.n_k.astype("int64")[:, None]).sum()) * 2
     return k_bytes + wl.B * wl.Hkv * S * wl.d * 2
+
+
+def fp8k_bytes(wl, S):
+    """Bytes of a step on an fp8 key cache: one byte per key element plus S
+    fp16 value rows per KV head (the per-head key scales are negligible)."""
+    return int(wl.n_k.astype("int64").sum()) * wl.Hkv * wl.d + wl.B * wl.Hkv * S * wl.d * 2
 
 
 def algorithmic_bytes(wl, S, dense=False):
@@ -142,7 +152,7 @@ def timed(fn, sets, steps, warmup, graph=True):
     return start.elapsed_time(stop) / steps  # ms per step (= per launch: one launch per step)
 
 
-def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False):
+def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False, fp8_cache=None):
     """Time the fp64 oracle on whole decode steps of the same workload (bounded);
     nbytes = the step's algorithmic bytes (the Bernoulli steps use seed 1, as
     the timed GPU steps do, so their kept features and bytes are the same)."""
@@ -157,6 +167,8 @@ def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False):
     while True:
         if bernoulli:
             O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, 1, wl.scale)
+        elif fp8_cache is not None:
+            O.santa_decode_fp8k(wl.q, fp8_cache[0], fp8_cache[1], wl.V, wl.n_k, S, mode, n, wl.scale)
         else:
             O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, n, wl.scale)
         n += 1
@@ -177,6 +189,7 @@ def main():
     import torch
 
     from stochastic_sparse_decode_amd import santa
+    from stochastic_sparse_decode_amd import workloads as W
 
     dev = torch.device("cuda:0")
     if args.copy_calibration:
@@ -202,8 +215,17 @@ def main():
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     S = args.S
 
-    rm_sets = sets  # row-major K
-    if args.workload == "bernoulli":
+    rm_sets = sets  # row-major fp16 K
+    fp8k = args.workload == "llama32k-fp8k"
+    if fp8k:
+        K8, ks = W.quantize_keys_fp8(wl.K, wl.n_k)
+        K80 = torch.from_numpy(K8).to(dev)
+        ks_d = torch.from_numpy(ks).to(dev)
+        R8 = max(1, int(math.ceil(args.rotate_bytes * (1 << 30) / (K80.numel() + V0.numel() * 2))))
+        sets = [(K80, V0)] + [(K80.clone(), V0.clone()) for _ in range(R8 - 1)]
+        step = lambda kv: santa.santa_decode_fp8k(q, kv[0], ks_d, kv[1], nk, S, mode, 1, wl.scale,  # noqa: E731
+                                                  out=out, workspace=ws)
+    elif args.workload == "bernoulli":
         sets = [(santa.santa_pack_k_feature_major(k), v) for k, v in sets]
         step = lambda kv: santa.santa_bernoulli_qk(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa
                                                    workspace=ws)
@@ -226,20 +248,22 @@ def main():
                                  workspace=ws)
         torch.cuda.synchronize()
         nbytes = bernoulli_bytes(kept, wl, S)
+    elif fp8k:
+        nbytes = fp8k_bytes(wl, S)
     else:
         nbytes = algorithmic_bytes(wl, S)
     gbs = nbytes / (ms * 1e-3) / 1e9
 
     exact_ms = None
-    if args.workload == "bernoulli" and not args.no_dense:
-        # the same step with exact scores (all of K, row-major) for comparison
+    if (args.workload == "bernoulli" or fp8k) and not args.no_dense:
+        # the same step with exact scores on the fp16 cache (all of K, row-major)
         estep = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
                                               workspace=ws)
         exact_ms = timed(estep, rm_sets, args.steps, args.warmup, graph=not args.eager)
     dense_ms = None
     if not args.no_dense and args.workload != "bernoulli":
         dstep = lambda kv: santa.santa_dense_decode(q, kv[0], kv[1], nk, wl.scale, out=out, workspace=ws)  # noqa
-        dense_ms = timed(dstep, sets, args.steps, args.warmup, graph=not args.eager)
+        dense_ms = timed(dstep, rm_sets, args.steps, args.warmup, graph=not args.eager)
 
     res = {
         "metric": "decode-attention us/step + effective HBM TB/s (% peak), Llama-3.1-8B shape @32k",
@@ -254,7 +278,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 in, f32 accumulate",
+        "dtype": "f8 (E4M3) keys, f16 q and values, f32 accumulate" if fp8k else "f16 in, f32 accumulate",
         "data": "synthetic (seeded; rotated over %d KV copies, %.2f GiB)" % (R, R * set_bytes / (1 << 30)),
         "config": {"workload": desc, "mode": args.mode, "S": S, "global_batch": wl.B, "seq_len": int(wl.n_k.max()),
                    "parallelism": "none (1 GPU)"},
@@ -267,16 +291,18 @@ def main():
                      and S == 128 else None},
     }
     if exact_ms is not None:
-        res["exact_santa"] = {"us_per_step": exact_ms * 1000.0,
-                              "effective_GBs": algorithmic_bytes(wl, S) / (exact_ms * 1e-3) / 1e9}
-        res["speedup_vs_exact_santa"] = exact_ms / ms
+        key = "fp16_santa" if fp8k else "exact_santa"
+        res[key] = {"us_per_step": exact_ms * 1000.0,
+                    "effective_GBs": algorithmic_bytes(wl, S) / (exact_ms * 1e-3) / 1e9}
+        res["speedup_vs_" + key] = exact_ms / ms
     if dense_ms is not None:
         dbytes = algorithmic_bytes(wl, S, dense=True)
         res["dense"] = {"us_per_step": dense_ms * 1000.0, "effective_GBs": dbytes / (dense_ms * 1e-3) / 1e9,
                         "pct_hbm_peak": 100.0 * dbytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         res["speedup_vs_dense"] = dense_ms / ms
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(wl, S, mode, args.cpu_seconds, nbytes, args.workload == "bernoulli")
+        res["cpu_baseline"] = cpu_baseline(wl, S, mode, args.cpu_seconds, nbytes, args.workload == "bernoulli",
+                                           (K8, ks) if fp8k else None)
     print(json.dumps(res))
 
 
