@@ -272,6 +272,46 @@ def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, score_overri
                         return_detail=return_detail)
 
 
+def gather_paged(cache, block_table, n_k, max_n_k):
+    """Contiguous (B, H_kv, max_n_k, d) view of a paged cache.
+
+    cache: (num_blocks, H_kv, P, d); block_table: (B, max_blocks) int; key j
+    of sequence b is row j % P of block block_table[b, j // P].  Rows at and
+    past n_k[b] are NaN (never read by the step).  A sequence with an invalid
+    length, or whose blocks below n_k are not all in [0, num_blocks), is left
+    entirely NaN.
+    """
+    num_blocks, Hkv, P, d = cache.shape
+    B = block_table.shape[0]
+    out = np.full((B, Hkv, max_n_k, d), np.nan)
+    for b in range(B):
+        n = int(n_k[b])
+        if not 1 <= n <= max_n_k:
+            continue
+        blocks = [int(block_table[b, j]) for j in range((n + P - 1) // P)]
+        if any(x < 0 or x >= num_blocks for x in blocks):
+            continue
+        for j in range(n):
+            out[b, :, j] = cache[blocks[j // P], :, j % P].astype(np.float64)
+    return out
+
+
+def santa_decode_paged(q, K_cache, V_cache, block_table, n_k, max_n_k, S, mode, seed, scale,
+                       score_override=None, return_detail=False):
+    """SANTA decode step on a paged KV cache: the keys and values of every
+    sequence are gathered through the block table (``gather_paged``), then
+    every step is ``santa_decode``'s.  A sequence with a block-table entry out
+    of range yields NaN outputs and indices -1, as an invalid length does."""
+    K = gather_paged(K_cache, block_table, n_k, max_n_k)
+    V = gather_paged(V_cache, block_table, n_k, max_n_k)
+    n_eff = np.asarray(n_k, dtype=np.int64).copy()
+    for b in range(len(n_eff)):
+        if np.isnan(K[b]).all():
+            n_eff[b] = 0  # invalid: NaN outputs
+    return santa_decode(q, K, V, n_eff, S, mode, seed, scale, score_override=score_override,
+                        return_detail=return_detail)
+
+
 def all_scores(q, K, n_k, scale):
     """Scores (B, H_q, max_n_k) fp64, NaN beyond n_k (for diagnostics)."""
     qf = _f64(q)

@@ -217,3 +217,36 @@ def quantize_keys_fp8(K, n_k):
     x = torch.from_numpy(K.astype(np.float32) / k_scale[:, :, None, None])
     K8 = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
     return K8, k_scale
+
+
+def paginate(K, V, n_k, block_size, seed=0, spare_blocks=3):
+    """Paged copy of a contiguous cache: (K_cache, V_cache, block_table, num_blocks).
+
+    Each sequence's rows below n_k are cut into blocks of ``block_size`` keys;
+    the blocks are placed at shuffled positions of a pool of num_blocks =
+    (blocks used) + spare_blocks; the rows of a last, partly used block past
+    n_k and the spare blocks are NaN (a read of them poisons the result).  K_cache, V_cache: (num_blocks, H_kv, block_size,
+    d) fp16; block_table: (B, max_blocks) int32, entries past a sequence's
+    blocks set to -1.  Sequences with an invalid n_k get no blocks.
+    """
+    B, Hkv, max_n_k, d = K.shape
+    P = int(block_size)
+    max_blocks = (max_n_k + P - 1) // P
+    rng = np.random.default_rng(seed)
+    owners = []
+    for b in range(B):
+        n = int(n_k[b])
+        if 1 <= n <= max_n_k:
+            owners += [(b, i) for i in range((n + P - 1) // P)]
+    num_blocks = len(owners) + spare_blocks
+    place = rng.permutation(num_blocks)[:len(owners)]
+    Kc = np.full((num_blocks, Hkv, P, d), np.nan, dtype=FP16)
+    Vc = np.full((num_blocks, Hkv, P, d), np.nan, dtype=FP16)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    for (b, i), pos in zip(owners, place):
+        n = int(n_k[b])
+        rows = min(P, n - i * P)
+        Kc[pos, :, :rows] = K[b, :, i * P:i * P + rows]
+        Vc[pos, :, :rows] = V[b, :, i * P:i * P + rows]
+        table[b, i] = pos
+    return Kc, Vc, table, num_blocks
