@@ -66,7 +66,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama32k",
-                    choices=["llama32k", "batched", "sweep131k", "bernoulli", "llama32k-fp8k"])
+                    choices=["llama32k", "batched", "sweep131k", "bernoulli", "llama32k-fp8k", "batched-paged"])
     ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid"])
     ap.add_argument("--S", type=int, default=128)
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of distinct KV copies to rotate over")
@@ -86,6 +86,10 @@ def make_workload(name):
     if name == "llama32k-fp8k":
         return (W.llama(B=1, n_k=32768, seed=1001),
                 "Llama-3.1-8B decode layer, B=1, 32q/8kv, d=128, n_k=32768, fp8 (OCP E4M3) key cache")
+    if name == "batched-paged":
+        return (W.llama(B=16, n_k_range=(8192, 32768), seed=1002),
+                "Llama-3.1-8B decode layer, B=16, n_k~U[8192,32768], 32q/8kv, d=128, paged cache (256-key blocks, "
+                "shuffled placement)")
     if name == "batched":
         return (W.llama(B=16, n_k_range=(8192, 32768), seed=1002),
                 "Llama-3.1-8B decode layer, B=16, n_k~U[8192,32768], 32q/8kv, d=128")
@@ -225,6 +229,14 @@ def main():
         sets = [(K80, V0)] + [(K80.clone(), V0.clone()) for _ in range(R8 - 1)]
         step = lambda kv: santa.santa_decode_fp8k(q, kv[0], ks_d, kv[1], nk, S, mode, 1, wl.scale,  # noqa: E731
                                                   out=out, workspace=ws)
+    elif args.workload == "batched-paged":
+        Kc, Vc, table, _ = W.paginate(wl.K, wl.V, wl.n_k, 256, seed=1)
+        Kc0, Vc0 = torch.from_numpy(Kc).to(dev), torch.from_numpy(Vc).to(dev)
+        tab = torch.from_numpy(table).to(dev)
+        Rp = max(1, int(math.ceil(args.rotate_bytes * (1 << 30) / (2 * Kc0.numel() * 2))))
+        sets = [(Kc0, Vc0)] + [(Kc0.clone(), Vc0.clone()) for _ in range(Rp - 1)]
+        step = lambda kv: santa.santa_decode_paged(q, kv[0], kv[1], tab, nk, S, mode, 1, wl.scale,  # noqa: E731
+                                                   out=out, workspace=ws)
     elif args.workload == "bernoulli":
         sets = [(santa.santa_pack_k_feature_major(k), v) for k, v in sets]
         step = lambda kv: santa.santa_bernoulli_qk(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa
@@ -255,7 +267,7 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
 
     exact_ms = None
-    if (args.workload == "bernoulli" or fp8k) and not args.no_dense:
+    if (args.workload in ("bernoulli", "batched-paged") or fp8k) and not args.no_dense:
         # the same step with exact scores on the fp16 cache (all of K, row-major)
         estep = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
                                               workspace=ws)
@@ -291,7 +303,7 @@ def main():
                      and S == 128 else None},
     }
     if exact_ms is not None:
-        key = "fp16_santa" if fp8k else "exact_santa"
+        key = {"llama32k-fp8k": "fp16_santa", "batched-paged": "contiguous_santa"}.get(args.workload, "exact_santa")
         res[key] = {"us_per_step": exact_ms * 1000.0,
                     "effective_GBs": algorithmic_bytes(wl, S) / (exact_ms * 1e-3) / 1e9}
         res["speedup_vs_" + key] = exact_ms / ms

@@ -17,6 +17,7 @@
  *     the abstract compares against).
  *   - santa_decode_fp8k: santa_decode on a key cache stored as 8-bit floats
  *     (OCP E4M3) with one scale per (sequence, KV head).
+ *   - santa_decode_paged: santa_decode on a paged KV cache (block table).
  *   - santa_bernoulli_qk: the abstract's Bernoulli qK^T sampling, which
  *     replaces each query by a stochastic ternary vector so that only the kept
  *     key features are read in the score stage, followed by the SANTA value
@@ -155,6 +156,25 @@ int santa_decode_fp8k(const santa_problem* problem, const void* q, const void* K
                       int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* SANTA decode step on a paged KV cache (the batched serving setting the
+ * pages evaluate in, without padding every sequence to max_n_k).
+ *   K_cache, V_cache [num_blocks][H_kv][block_size][d] fp16: a pool of
+ *            blocks; block p holds block_size consecutive keys (values) of
+ *            one sequence, for every KV head
+ *   block_table [B][max_n_k / block_size] int32, device memory: key j of
+ *            sequence b is row j % block_size of block
+ *            block_table[b][j / block_size] (entries past ceil(n_k[b] /
+ *            block_size) are not read)
+ * block_size: a power of two in [16, 1024] dividing problem->max_n_k (the
+ * longest sequence the table can describe).  Every other argument, output and
+ * error is as for santa_decode.  A block-table entry outside [0, num_blocks)
+ * is read as block 0 and sets bit 1 of the workspace error bits
+ * (santa_workspace_error); the results of that sequence are then unspecified. */
+int santa_decode_paged(const santa_problem* problem, const void* q, const void* K_cache, const void* V_cache,
+                       const int32_t* block_table, int32_t block_size, int32_t num_blocks, const int32_t* n_k,
+                       int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out,
+                       float* scores_out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Exact decode attention: out[b][h] = softmax(scale q K^T) V over j < n_k[b]
  * (the FlashDecoding-style baseline named in the abstract's fifth sentence). */
 int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,
@@ -180,7 +200,8 @@ int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* 
 int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void* K_fm, void* stream);
 
 /* Copy the device error bits of a workspace to *flags (synchronises `stream`).
- * Bit 0: a bounded cross-workgroup wait timed out (results invalid). */
+ * Bit 0: a bounded cross-workgroup wait timed out (results invalid).
+ * Bit 1: a block-table entry of santa_decode_paged was out of range. */
 int santa_workspace_error(const void* workspace, uint32_t* flags, void* stream);
 
 /* Human-readable name of a status code (static string). */

@@ -273,7 +273,7 @@ def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, score_overri
 
 
 def gather_paged(cache, block_table, n_k, max_n_k):
-    """Contiguous (B, H_kv, max_n_k, d) view of a paged cache.
+    """Contiguous (B, H_kv, max_n_k, d) copy of a paged cache (same dtype).
 
     cache: (num_blocks, H_kv, P, d); block_table: (B, max_blocks) int; key j
     of sequence b is row j % P of block block_table[b, j // P].  Rows at and
@@ -283,7 +283,7 @@ def gather_paged(cache, block_table, n_k, max_n_k):
     """
     num_blocks, Hkv, P, d = cache.shape
     B = block_table.shape[0]
-    out = np.full((B, Hkv, max_n_k, d), np.nan)
+    out = np.full((B, Hkv, max_n_k, d), np.nan, dtype=cache.dtype)  # exact copies of the stored values
     for b in range(B):
         n = int(n_k[b])
         if not 1 <= n <= max_n_k:
@@ -291,8 +291,9 @@ def gather_paged(cache, block_table, n_k, max_n_k):
         blocks = [int(block_table[b, j]) for j in range((n + P - 1) // P)]
         if any(x < 0 or x >= num_blocks for x in blocks):
             continue
-        for j in range(n):
-            out[b, :, j] = cache[blocks[j // P], :, j % P].astype(np.float64)
+        for i, blk in enumerate(blocks):  # keys i P .. i P + rows - 1 sit in block blk
+            rows = min(P, n - i * P)
+            out[b, :, i * P:i * P + rows] = cache[blk, :, :rows]
     return out
 
 

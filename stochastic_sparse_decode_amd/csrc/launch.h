@@ -17,6 +17,7 @@ constexpr uint64_t kLaunchUnit = 1ull << 20;  // launch counter increment per la
 
 // Error bits written by kernels into the workspace header.
 constexpr uint32_t kErrSpinTimeout = 1u;
+constexpr uint32_t kErrBlockTable = 2u;  // a block-table entry out of range (read as block 0)
 
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
@@ -53,6 +54,9 @@ struct DecodeParams {
   float* scores_out;    // [B][Hq][max_n_k] or null
   uint8_t* kept_out;    // [B][Hq][D] or null (Bernoulli)
   const float* k_scale; // [B][Hkv] scales of an fp8 key cache (K = k_scale * decode(K8)), else null
+  const int32_t* block_table;  // paged cache: [B][max_n_k / block_size] block of each key range, else null
+  int lg_block;         // paged cache: log2(block_size)
+  int num_blocks;       // paged cache: blocks in K and V, each [Hkv][block_size][D]
   uint64_t seed;
   int D, G;
   int occ;              // sampling kernel variant: 1 = one item per workgroup, 2 = items taken in turn
@@ -60,10 +64,11 @@ struct DecodeParams {
 };
 static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");
 
-enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2, kOpDecodeF8 = 3 };
+enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2, kOpDecodeF8 = 3, kOpDecodePaged = 4 };
 
 // Key cache kinds of the sampling kernel.
-enum KeyKind { kKeyF16 = 0, kKeyBernoulli = 1, kKeyF8 = 2 };
+enum KeyKind { kKeyF16 = 0, kKeyBernoulli = 1, kKeyF8 = 2, kKeyF16Paged = 3 };
+constexpr int kMaxBlocksPerSplit = kSplit / 16;  // smallest block: 16 keys
 
 // Resident-workgroup capacity of the current device for a kernel variant.
 int decode_capacity(int D, int G, int key_kind, int occ);

@@ -79,7 +79,7 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Resident-workgroup capacity per (device, kernel variant), computed once.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 4 /*kernel*/ * 2 /*workgroups per CU*/;
+constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 5 /*kernel*/ * 2 /*workgroups per CU*/;
 std::mutex g_cap_mutex;
 int g_cap[kMaxDevices][kVariants];
 
@@ -90,8 +90,18 @@ int variant_index(int D, int G, int kind, int occ) {
 }
 
 int key_kind(int op) {
-  return op == santa::kOpBernoulli ? santa::kKeyBernoulli : op == santa::kOpDecodeF8 ? santa::kKeyF8 : santa::kKeyF16;
+  switch (op) {
+    case santa::kOpBernoulli: return santa::kKeyBernoulli;
+    case santa::kOpDecodeF8: return santa::kKeyF8;
+    case santa::kOpDecodePaged: return santa::kKeyF16Paged;
+    default: return santa::kKeyF16;
+  }
 }
+
+struct Paging {
+  const int32_t* block_table = nullptr;
+  int lg_block = 0, num_blocks = 0;
+};
 
 int capacity(int D, int G, int kind, int occ) {
   int dev = 0;
@@ -160,7 +170,8 @@ int choose_grid(DecodeParams& d, int kind) {
 
 int sampled_step(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
-                 uint8_t* kept_out, const float* k_scale, void* ws, size_t ws_bytes, void* stream, int kind) {
+                 uint8_t* kept_out, const float* k_scale, const Paging& pg, void* ws, size_t ws_bytes, void* stream,
+                 int kind) {
   int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes);
   if (st != SANTA_OK) return st;
   if (kind == santa::kOpDecodeF8) {
@@ -177,6 +188,9 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   d.scores_out = scores_out;
   d.kept_out = kept_out;
   d.k_scale = k_scale;
+  d.block_table = pg.block_table;
+  d.lg_block = pg.lg_block;
+  d.num_blocks = pg.num_blocks;
   d.S = S;
   d.mode = mode;
   d.seed = seed;
@@ -198,8 +212,27 @@ size_t santa_workspace_bytes(const santa_problem* problem) {
 int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, nullptr,
+  return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, nullptr, Paging{},
                       workspace, workspace_bytes, stream, santa::kOpDecode);
+}
+
+int santa_decode_paged(const santa_problem* problem, const void* q, const void* K_cache, const void* V_cache,
+                       const int32_t* block_table, int32_t block_size, int32_t num_blocks, const int32_t* n_k,
+                       int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out,
+                       float* scores_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!problem) return SANTA_ERR_NULL;
+  if (!block_table) return SANTA_ERR_NULL;
+  if (!aligned(block_table, 4)) return SANTA_ERR_ALIGN;
+  int lg = 0;
+  while (lg < 11 && (1 << lg) < block_size) ++lg;
+  if (block_size < 16 || block_size > santa::kSplit || (1 << lg) != block_size) return SANTA_ERR_SHAPE;
+  if (problem->max_n_k % block_size != 0 || num_blocks < 1) return SANTA_ERR_SHAPE;
+  Paging pg;
+  pg.block_table = block_table;
+  pg.lg_block = lg;
+  pg.num_blocks = num_blocks;
+  return sampled_step(problem, q, K_cache, V_cache, n_k, S, mode, seed, out, indices_out, scores_out, nullptr,
+                      nullptr, pg, workspace, workspace_bytes, stream, santa::kOpDecodePaged);
 }
 
 int santa_decode_fp8k(const santa_problem* problem, const void* q, const void* K8, const float* k_scale,
@@ -207,7 +240,7 @@ int santa_decode_fp8k(const santa_problem* problem, const void* q, const void* K
                       int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
                       void* stream) {
   return sampled_step(problem, q, K8, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, k_scale,
-                      workspace, workspace_bytes, stream, santa::kOpDecodeF8);
+                      Paging{}, workspace, workspace_bytes, stream, santa::kOpDecodeF8);
 }
 
 int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* K_fm, const void* V,
@@ -215,7 +248,7 @@ int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* 
                        int32_t* indices_out, float* scores_out, uint8_t* kept_out, void* workspace,
                        size_t workspace_bytes, void* stream) {
   return sampled_step(problem, q, K_fm, V, n_k, S, mode, seed, out, indices_out, scores_out, kept_out, nullptr,
-                      workspace, workspace_bytes, stream, santa::kOpBernoulli);
+                      Paging{}, workspace, workspace_bytes, stream, santa::kOpBernoulli);
 }
 
 int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,

@@ -284,6 +284,7 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 template <int D, int G, int KIND, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   constexpr bool BERN = KIND == kKeyBernoulli;
+  constexpr bool PAGED = KIND == kKeyF16Paged;
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G, OCC>;
   uint32_t* uni = (uint32_t*)(smem + L::nbuf * L::sc_bytes);                  // [G][kUniRow]
@@ -292,6 +293,9 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   __shared__ Shared sh;
   __shared__ uint32_t binfo[BERN ? 128 : 1];  // Bernoulli kept-feature union
   __shared__ uint4 bwt[BERN ? 128 : 1];       // and its per-head fp16 weights
+  // paged cache: the block of each block-sized key range of the item in
+  // score buffer wb (validated; an out-of-range entry reads block 0)
+  __shared__ int pblk[PAGED ? 2 : 1][PAGED ? kMaxBlocksPerSplit : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
@@ -345,6 +349,18 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     it.len = it.active ? min(kSplit, n - it.k0) : 0;
     it.is_last = it.s == it.nsg - 1;
     return it;
+  };
+
+  // start of key (or value) row j of an item's split, for the KV head's
+  // contiguous block or through the block table
+  auto row_of = [&](const void* base, const ItemCtx& it, int wb, int j) -> const _Float16* {
+    if constexpr (PAGED) {
+      const int blk = pblk[wb][j >> p.lg_block];
+      const size_t slab = ((size_t)blk * p.Hkv + it.hk) << p.lg_block;  // first row of the (block, head) slab
+      return (const _Float16*)base + (slab + (size_t)(j & ((1 << p.lg_block) - 1))) * D;
+    } else {
+      return (const _Float16*)base + ((size_t)(it.b * p.Hkv + it.hk) * p.max_n_k + it.k0 + j) * D;
+    }
   };
 
   // ---- per query head (wave g owns head g) ---------------------------------
@@ -437,7 +453,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       pl.rc[c] = load_dev(slots + (x * G + g) * 2 + 1);
     }
   };
-  auto tail_a = [&](const ItemCtx& it, int g, float* scb, const Weights& wt, Gather& gt) {
+  auto tail_a = [&](const ItemCtx& it, int g, float* scb, int wb, const Weights& wt, Gather& gt) {
         const int s = it.s, len = it.len, k0 = it.k0, nsg = it.nsg, b = it.b, hk = it.hk, h0 = it.h0;
         const bool is_last = it.is_last;
         const uint32_t tag = sh.epoch;
@@ -666,16 +682,16 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           }
           wave_lds_sync();
           const int r = lane / LPR, c = lane % LPR;
-          const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D + c * 8;
 #pragma unroll
           for (int u = 0; u < kVU; ++u) {
             const int i = u * RPW + r;
             gt.ee[u] = i < nsel ? list[i] : 0u;
-            gt.vv[u] = i < nsel ? *(const uint4*)(Vb + (size_t)(gt.ee[u] & 0xffffu) * D) : make_uint4(0, 0, 0, 0);
+            gt.vv[u] = i < nsel ? *(const uint4*)(row_of(p.V, it, wb, (int)(gt.ee[u] & 0xffffu)) + c * 8)
+                                : make_uint4(0, 0, 0, 0);
           }
         }
   };
-  auto tail_b = [&](const ItemCtx& it, int g, const Gather& gt) {
+  auto tail_b = [&](const ItemCtx& it, int g, int wb, const Gather& gt) {
         const int nsel = gt.nsel;
         if (nsel == 0) return;
         const int b = it.b, hk = it.hk, k0 = it.k0;
@@ -685,7 +701,6 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         uint32_t* cw = cntw + g * (kSplit / 2);
         {
           const int r = lane / LPR, c = lane % LPR;
-          const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D + c * 8;
           float a8[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) a8[e] = 0.f;
@@ -707,7 +722,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             for (int u = 0; u < kVU; ++u) {
               const int i = i0 + u * RPW + r;
               ee[u] = i < nsel ? list[i] : 0u;
-              vv[u] = i < nsel ? *(const uint4*)(Vb + (size_t)(ee[u] & 0xffffu) * D) : make_uint4(0, 0, 0, 0);
+              vv[u] = i < nsel ? *(const uint4*)(row_of(p.V, it, wb, (int)(ee[u] & 0xffffu)) + c * 8)
+                               : make_uint4(0, 0, 0, 0);
             }
             add_rows(vv, ee);
           }
@@ -758,7 +774,24 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     } else {
       // two workgroups per CU: half the loads per buffer (the CU still has
       // 16 KiB per wave in flight, and the registers saved avoid spills)
-      score_rowmajor<D, G, OCC == 2 ? (G > kWaves ? 4 : 8) : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+      if constexpr (PAGED) {
+        // the split's block entries, checked against the pool
+        const int nbl = (it.len + (1 << p.lg_block) - 1) >> p.lg_block;
+        if (tid < nbl) {
+          int e = p.block_table[(size_t)it.b * (p.max_n_k >> p.lg_block) + (it.k0 >> p.lg_block) + tid];
+          if (e < 0 || e >= p.num_blocks) {
+            atomicOr(p.ws.err, kErrBlockTable);
+            e = 0;
+          }
+          pblk[wb][tid] = e;
+        }
+        lds_barrier();
+      }
+      constexpr int LB = OCC == 2 ? (G > kWaves ? 4 : 8) : 16;
+      if constexpr (PAGED)
+        score_rowmajor_rows<D, G, LB>(p, it.b, it.hk, it.len, scb, mx, [&](int j) { return row_of(p.K, it, wb, j); });
+      else
+        score_rowmajor<D, G, LB>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -782,8 +815,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       publish(it, g, wt);
       if (finish_now) {
         Gather gt;
-        tail_a(it, g, scb, wt, gt);
-        tail_b(it, g, gt);
+        tail_a(it, g, scb, wb, wt, gt);
+        tail_b(it, g, wb, gt);
       }
     }
   };
@@ -851,8 +884,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           Weights wt;
           Gather gt;
           weights(prev, g, score_buf(cb ^ 1), cb ^ 1, wt);
-          tail_a(prev, g, score_buf(cb ^ 1), wt, gt);
-          tail_b(prev, g, gt);
+          tail_a(prev, g, score_buf(cb ^ 1), cb ^ 1, wt, gt);
+          tail_b(prev, g, cb ^ 1, gt);
         }
       if (!have) break;
       lds_barrier();  // every wave is done with the buffer the next item overwrites
@@ -892,6 +925,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 template <int D, int G, int KIND>
 constexpr bool built() { return KIND != kKeyF8 || fp8_supported<D, G>(); }
 
+
 template <int KIND, int OCC>
 hipError_t dispatch(const DecodeParams& p, hipStream_t stream) {
 #define SANTA_CASE(DD, GG)                                                                     \
@@ -918,6 +952,7 @@ template <int OCC>
 int capacity_kind(int D, int G, int key_kind) {
   if (key_kind == kKeyBernoulli) return capacity<kKeyBernoulli, OCC>(D, G);
   if (key_kind == kKeyF8) return capacity<kKeyF8, OCC>(D, G);
+  if (key_kind == kKeyF16Paged) return capacity<kKeyF16Paged, OCC>(D, G);
   return capacity<kKeyF16, OCC>(D, G);
 }
 
@@ -925,6 +960,7 @@ template <int OCC>
 hipError_t dispatch_kind(const DecodeParams& p, int key_kind, hipStream_t stream) {
   if (key_kind == kKeyBernoulli) return dispatch<kKeyBernoulli, OCC>(p, stream);
   if (key_kind == kKeyF8) return dispatch<kKeyF8, OCC>(p, stream);
+  if (key_kind == kKeyF16Paged) return dispatch<kKeyF16Paged, OCC>(p, stream);
   return dispatch<kKeyF16, OCC>(p, stream);
 }
 

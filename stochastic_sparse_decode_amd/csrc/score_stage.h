@@ -84,6 +84,64 @@ __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int
   for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
 }
 
+// The same stage for a paged (block table) cache: row_ptr(j) points at key
+// row j (0 <= j < len) of the split.  (The contiguous stage above keeps its
+// own copy: routing it through a row-pointer functor made the compiler
+// schedule its loads worse.)
+template <int D, int G, int LB, typename RowPtr>
+__device__ __forceinline__ void score_rowmajor_rows(const DecodeParams& p, int b, int hk, int len, float* cdf,
+                                                    float* mx, const RowPtr& row_ptr) {
+  using Gm = Geo<D, G, LB>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane / Gm::LPR, c = lane % Gm::LPR;
+  const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
+  uint4 qv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qb + g * D + c * 8);
+
+  const int my_u = c / G, my_g = c % G;
+  float m_run = -INFINITY;
+
+  // A split is always streamed in NIT = kSplit / ROWS_IT fully unrolled
+  // iterations with two register buffers: the loads of iteration i+1 are in
+  // flight while iteration i is reduced.  Loads are unconditional (rows past
+  // the split's end re-read its last row, an L1 hit) so that the compiler
+  // counts outstanding loads exactly and never waits for the prefetch.
+  constexpr int NIT = kSplit / Gm::ROWS_IT;
+  uint4 buf[2][Gm::NB][Gm::U];
+  auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb)
+#pragma unroll
+      for (int u = 0; u < Gm::U; ++u) {
+        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, len - 1);
+        bb[nb][u] = load_nt((const uint4*)(row_ptr(row) + c * 8));
+      }
+  };
+  issue(buf[0], 0);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int base = it * Gm::ROWS_IT;
+    if (it + 1 < NIT) issue(buf[(it + 1) & 1], base + Gm::ROWS_IT);
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb) {
+      float v[Gm::LPR];
+#pragma unroll
+      for (int u = 0; u < Gm::U; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) v[u * G + g] = dot8(buf[it & 1][nb][u], qv[g]);
+      row_reduce_scatter<Gm::LPR>(v, lane);
+      // rows < kSplit always; rows >= len land in unused LDS slots
+      const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
+      const float s = v[0] * p.scale;
+      cdf[my_g * kPad + lidx(row)] = s;
+      m_run = fmaxf(m_run, row < len ? s : -INFINITY);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------
 // Score stage, fp8 key cache: rows of D bytes (OCP E4M3), 16 bytes = 16
 // features per lane, LPR = D / 16 lanes per row.  Each 16-byte piece becomes

@@ -57,6 +57,8 @@ def library():
     lib.santa_decode.restype = ctypes.c_int
     lib.santa_decode_fp8k.argtypes = [P, vp, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, sz, vp]
     lib.santa_decode_fp8k.restype = ctypes.c_int
+    lib.santa_decode_paged.argtypes = [P, vp, vp, vp, vp, i32, i32, vp, i32, i32, u64, vp, vp, vp, vp, sz, vp]
+    lib.santa_decode_paged.restype = ctypes.c_int
     lib.santa_dense_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.santa_dense_decode.restype = ctypes.c_int
     lib.santa_bernoulli_qk.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, vp, sz, vp]
@@ -190,6 +192,48 @@ def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, out=None, in
                                      int(S), int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
                                      _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "santa_decode_fp8k")
+    return out
+
+
+def problem_paged(q, K_cache, block_table, scale):
+    """santa_problem for q and a paged cache (num_blocks, H_kv, P, d) with a
+    block table (B, max_blocks): max_n_k = max_blocks * P."""
+    B, Hq, d = q.shape
+    return Problem(B, Hq, K_cache.shape[1], d, block_table.shape[1] * K_cache.shape[2], float(scale))
+
+
+def santa_decode_paged(q, K_cache, V_cache, block_table, n_k, S, mode, seed, scale, out=None, indices=None,
+                       scores=None, workspace=None, stream=None):
+    """SANTA decode step on a paged KV cache; returns ``out`` (B, H_q, d) fp32.
+
+    K_cache, V_cache (num_blocks, H_kv, block_size, d) fp16; block_table
+    (B, max_blocks) int32: key j of sequence b is row j % block_size of block
+    block_table[b, j // block_size].  The rest is as for ``santa_decode``.
+    """
+    dev = q.device
+    for t, nm in ((q, "q"), (K_cache, "K_cache"), (V_cache, "V_cache")):
+        _expect(t, nm, torch.float16, dev)
+    _expect(block_table, "block_table", torch.int32, dev, 2)
+    _expect(n_k, "n_k", torch.int32, dev, 1)
+    if K_cache.dim() != 4 or tuple(V_cache.shape) != tuple(K_cache.shape):
+        raise ValueError("K_cache %s and V_cache %s must be (num_blocks, H_kv, block_size, d)" % (
+            tuple(K_cache.shape), tuple(V_cache.shape)))
+    prob = problem_paged(q, K_cache, block_table, scale)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    _expect(out, "out", torch.float32, dev)
+    if indices is not None:
+        _expect(indices, "indices", torch.int32, dev)
+    if scores is not None:
+        _expect(scores, "scores", torch.float32, dev)
+    if workspace is None:
+        workspace = new_workspace(prob, dev)
+    mode = MODES.get(mode, mode)
+    st = library().santa_decode_paged(ctypes.byref(prob), _ptr(q), _ptr(K_cache), _ptr(V_cache), _ptr(block_table),
+                                      int(K_cache.shape[2]), int(K_cache.shape[0]), _ptr(n_k), int(S), int(mode),
+                                      int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
+                                      _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "santa_decode_paged")
     return out
 
 

@@ -109,3 +109,22 @@ def test_fp8k_host_checks(lib):
     p64 = _prob(head_dim=64, num_q_heads=64, num_kv_heads=8)
     assert call(p64, FAKE, santa.workspace_bytes(p64)) == 3   # d = 64 with G = 8 is not built
     assert call(p, FAKE, 16) == 5              # workspace too small
+
+
+def test_paged_host_checks(lib):
+    vp = ctypes.c_void_p
+    p = _prob(max_n_k=4096)
+    nb = santa.workspace_bytes(p)
+
+    def call(prob, table=FAKE, block=64, blocks=10, ws_bytes=nb):
+        return lib.santa_decode_paged(ctypes.byref(prob), vp(FAKE), vp(FAKE), vp(FAKE), vp(table), block, blocks,
+                                      vp(FAKE), 128, 2, 0, vp(FAKE), None, None, vp(FAKE), ws_bytes, None)
+
+    assert call(p, table=0) == 1          # block table missing
+    assert call(p, table=FAKE + 2) == 4   # block table not 4-byte aligned
+    assert call(p, block=48) == 2         # not a power of two
+    assert call(p, block=8) == 2          # below 16 keys
+    assert call(p, block=2048) == 2       # above one split
+    assert call(_prob(max_n_k=4000), block=64, ws_bytes=santa.workspace_bytes(_prob(max_n_k=4000))) == 2
+    assert call(p, blocks=0) == 2         # empty pool
+    assert call(p, ws_bytes=16) == 5
