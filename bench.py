@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--steps-model", type=int, default=10)
+    ap.add_argument("--model-step", action="store_true",
+                    help="only time a synthetic 32-layer Llama-3.1-8B decode step (B=1, 32k context): attention "
+                         "by SANTA or by the dense kernel, projections and MLP by torch matmuls on random weights")
     return ap.parse_args()
 
 
@@ -184,8 +188,101 @@ def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False, fp8_cache=None):
             "sample": "%d full decode step(s) of the same workload, %.2f s per step" % (n, per_step)}
 
 
+def model_step(args):
+    """Synthetic decode step of a 32-layer Llama-3.1-8B-shaped model at B=1
+    with a 32k context in every layer: per layer the fused QKV projection,
+    attention over that layer's own KV cache (SANTA systematic S=128, or the
+    dense kernel), the output projection and the gated MLP (torch matmuls,
+    random fp16 weights; norms, rotary embedding and the cache append are left
+    out: they move a few KiB).  Reports the token latency with each attention
+    and the share attention takes of it."""
+    import numpy as np
+    import torch
+
+    from stochastic_sparse_decode_amd import santa
+    from stochastic_sparse_decode_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    L, hid, inter, Hq, Hkv, d, n_k = 32, 4096, 14336, 32, 8, 128, 32768
+    wl = W.llama(B=1, n_k=n_k, seed=1001)
+    g = torch.Generator(device=dev).manual_seed(7)
+
+    def weight(rows, cols):
+        return (torch.randn(rows, cols, generator=g, device=dev, dtype=torch.float16) / math.sqrt(rows)).contiguous()
+
+    layers = []
+    K0 = torch.from_numpy(wl.K).to(dev)
+    V0 = torch.from_numpy(wl.V).to(dev)
+    for _ in range(L):
+        layers.append(dict(wqkv=weight(hid, (Hq + 2 * Hkv) * d), wo=weight(Hq * d, hid), wg=weight(hid, inter),
+                           wu=weight(hid, inter), wd=weight(inter, hid), K=K0.clone(), V=V0.clone()))
+    nk = torch.from_numpy(wl.n_k.astype(np.int32)).to(dev)
+    q_probe = torch.from_numpy(wl.q).to(dev)  # the query when projections are left out
+    ws = santa.new_workspace(santa.problem(q_probe, K0, wl.scale), dev)
+    att = torch.empty((1, Hq, d), dtype=torch.float32, device=dev)
+    x0 = torch.randn(1, hid, generator=g, device=dev, dtype=torch.float16)
+
+    def attention(lay, q, dense):
+        if dense:
+            santa.santa_dense_decode(q, lay["K"], lay["V"], nk, wl.scale, out=att, workspace=ws)
+        else:
+            santa.santa_decode(q, lay["K"], lay["V"], nk, 128, 2, 1, wl.scale, out=att, workspace=ws)
+        return att
+
+    def step(dense=False, attn=True, other=True):
+        x = x0
+        q = q_probe
+        for lay in layers:
+            if other:
+                qkv = x @ lay["wqkv"]
+                q = qkv[:, :Hq * d].view(1, Hq, d)
+            if attn:
+                a = attention(lay, q, dense)
+            if other:
+                src = a.view(1, Hq * d).to(torch.float16) if attn else qkv[:, :Hq * d]
+                x = x + src @ lay["wo"]
+                h = torch.nn.functional.silu(x @ lay["wg"]) * (x @ lay["wu"])
+                x = x + h @ lay["wd"]
+        return x
+
+    def timed_step(**kw):
+        for _ in range(3):
+            step(**kw)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(args.steps_model):
+                step(**kw)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        gr.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps_model * 1000.0  # us per token
+
+    full_santa = timed_step(dense=False)
+    full_dense = timed_step(dense=True)
+    att_santa = timed_step(dense=False, other=False)
+    att_dense = timed_step(dense=True, other=False)
+    other = timed_step(attn=False)
+    assert santa.santa_workspace_error(ws) == 0
+    print(json.dumps({"model_step": {
+        "model": "Llama-3.1-8B shape, 32 layers, random fp16 weights", "batch": 1, "context": n_k,
+        "us_per_token_santa": full_santa, "us_per_token_dense": full_dense,
+        "attention_us_santa": att_santa, "attention_us_dense": att_dense, "non_attention_us": other,
+        "attention_share_santa": att_santa / full_santa, "attention_share_dense": att_dense / full_dense,
+        "token_speedup_santa_vs_dense": full_dense / full_santa,
+        "timing": "HIP graph of %d whole decode steps, one timed replay" % args.steps_model}}))
+
+
 def main():
     args = parse()
+    if args.model_step:
+        model_step(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on a single GPU; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
