@@ -141,6 +141,42 @@ def ternary_query(q_group, u):
     return q_tilde, kept, A
 
 
+def budget_query(q_group, u, m):
+    """Budget variant of the stochastic queries, for the G heads of one KV
+    head: feature i of head h is kept with probability
+    pi_hi = min(1, m |q_hi| / ||q_h||_1), so about m features per head are
+    kept, and a kept feature takes the value q_hi / pi_hi: q_hi itself where
+    pi_hi = 1 (a clipped feature) and sign(q_hi) ||q_h||_1 / m otherwise, so
+    E[q~] = q.  u (d,) uniforms (multiples of 2^-24) are shared by the group;
+    q = 0 keeps nothing.
+
+    The decision u_i < pi_hi is made exactly: with every value scaled by 2^24
+    to an integer (fp16 values and the uniforms are multiples of 2^-24),
+    keep <=> U_i * L1 < m * Q_hi * 2^24 and clipped <=> m * Q_hi >= L1, in
+    Python integers.  Returns (q_tilde (G, d), kept (G, d) bool,
+    clipped (G, d) bool, c (G,) = ||q_h||_1 / m).
+    """
+    q_group = np.asarray(q_group, dtype=np.float64)
+    G, d = q_group.shape
+    Ui = [int(round(x * 2.0 ** 24)) for x in u]
+    q_tilde = np.zeros((G, d))
+    kept = np.zeros((G, d), dtype=bool)
+    clipped = np.zeros((G, d), dtype=bool)
+    c = np.zeros(G)
+    for h in range(G):
+        Q = [int(round(abs(x) * 2.0 ** 24)) for x in q_group[h]]
+        L1 = sum(Q)
+        c[h] = L1 * 2.0 ** -24 / m
+        for i in range(d):
+            if Q[i] == 0:
+                continue
+            clipped[h, i] = m * Q[i] >= L1
+            kept[h, i] = Ui[i] * L1 < m * Q[i] * 2 ** 24
+            if kept[h, i]:
+                q_tilde[h, i] = q_group[h, i] if clipped[h, i] else np.sign(q_group[h, i]) * c[h]
+    return q_tilde, kept, clipped, c
+
+
 # ----------------------------------------------------------------------------
 # batched drivers
 # ----------------------------------------------------------------------------
@@ -224,11 +260,13 @@ def dense_decode(q, K, V, n_k, scale):
     return out
 
 
-def bernoulli_queries(q, Hkv, seed):
-    """Ternary queries for every (b, h): (q_tilde, kept, A).
+def bernoulli_queries(q, Hkv, seed, budget=0):
+    """Stochastic queries for every (b, h): (q_tilde, kept, A).
 
     The d uniforms of KV head (b, h_kv) come from stream row b * H_kv + h_kv of
     the 'BERN' tag and are shared by the G query heads of that KV head.
+    budget = 0: ternary queries (``ternary_query``; A = max |q|); budget = m
+    > 0: the budget variant (``budget_query``; A = ||q||_1 / m).
     """
     qf = _f64(q)
     B, Hq, d = qf.shape
@@ -240,11 +278,14 @@ def bernoulli_queries(q, Hkv, seed):
         for hk in range(Hkv):
             u = philox.uniforms(seed, b * Hkv + hk, philox.TAG_BERNOULLI, d)
             sl = slice(hk * G, (hk + 1) * G)
-            q_tilde[b, sl], kept[b, sl], A[b, sl] = ternary_query(qf[b, sl], u)
+            if budget > 0:
+                q_tilde[b, sl], kept[b, sl], _, A[b, sl] = budget_query(qf[b, sl], u, budget)
+            else:
+                q_tilde[b, sl], kept[b, sl], A[b, sl] = ternary_query(qf[b, sl], u)
     return q_tilde, kept, A
 
 
-def bernoulli_decode(q, K, V, n_k, S, mode, seed, scale, return_detail=False):
+def bernoulli_decode(q, K, V, n_k, S, mode, seed, scale, return_detail=False, budget=0):
     """Bernoulli qK^T mode: ternary-query scores, then the SANTA value stage.
 
     The scores use q~ in place of q; the softmax, points, search and estimate
@@ -252,7 +293,7 @@ def bernoulli_decode(q, K, V, n_k, S, mode, seed, scale, return_detail=False):
     (out, indices, kept (B, H_q, d) bool) and, on request, a detail dict.
     """
     Hkv = _check_shapes(q, K, V, n_k)[2]
-    q_tilde, kept, _ = bernoulli_queries(q, Hkv, seed)
+    q_tilde, kept, _ = bernoulli_queries(q, Hkv, seed, budget)
     res = santa_decode(q_tilde, K, V, n_k, S, mode, seed, scale,
                        return_detail=return_detail)
     if return_detail:

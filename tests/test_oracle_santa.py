@@ -273,3 +273,70 @@ def test_bernoulli_kept_count_expectation():
               for s in range(4000)]
     sd = np.sqrt((pi * (1 - pi)).sum() / len(counts))
     assert abs(np.mean(counts) - pi.sum()) < 4 * sd
+
+
+# --------------------------------------------------------------------------
+# Bernoulli budget variant: pi = min(1, m |q| / ||q||_1), kept value q / pi
+# --------------------------------------------------------------------------
+
+def test_budget_query_is_unbiased():
+    """E[q~] = q: mean over 10^4 draws within 4.5 sigma for every feature."""
+    rng = np.random.default_rng(21)
+    qg = rng.standard_normal((2, 32)).astype(np.float16).astype(np.float64)
+    m = 8
+    N = 10000
+    acc = np.zeros_like(qg)
+    for seed in range(N):
+        u = philox.uniforms(seed, 0, philox.TAG_BERNOULLI, 32)
+        acc += O.budget_query(qg, u, m)[0]
+    L1 = np.abs(qg).sum(axis=1, keepdims=True)
+    pi = np.minimum(1.0, m * np.abs(qg) / L1)
+    var = qg ** 2 * (1.0 / pi - 1.0)  # Var of (q / pi) Bernoulli(pi)
+    z = (acc / N - qg) / np.sqrt(np.maximum(var, 1e-300) / N)
+    z[var == 0] = 0
+    assert np.abs(z).max() < 4.5
+
+
+def test_budget_query_structure_and_exact_decision():
+    rng = np.random.default_rng(22)
+    qg = (rng.standard_normal((3, 64)) * np.array([[1.0], [0.01], [30.0]])).astype(np.float16).astype(np.float64)
+    u = philox.uniforms(5, 0, philox.TAG_BERNOULLI, 64)
+    for m in (1, 4, 16, 64):
+        qt, kept, clipped, c = O.budget_query(qg, u, m)
+        L1 = np.abs(qg).sum(axis=1)
+        assert np.allclose(c, L1 / m, rtol=1e-15)
+        pi = np.minimum(1.0, m * np.abs(qg) / L1[:, None])
+        # clipped exactly where pi = 1; clipped features are always kept, at q
+        assert np.array_equal(clipped, m * np.abs(qg) >= L1[:, None])
+        assert kept[clipped].all() and np.array_equal(qt[clipped], qg[clipped])
+        # unclipped kept features take sign(q) ||q||_1 / m
+        uk = kept & ~clipped
+        assert np.allclose(np.abs(qt[uk]), np.broadcast_to(c[:, None], qt.shape)[uk], rtol=1e-15)
+        assert np.array_equal(np.sign(qt[kept]), np.sign(qg[kept]))
+        # the decision agrees with the fp64 comparison u < pi wherever that
+        # comparison is not within rounding of a tie
+        margin = np.abs(u[None, :] - pi) > 1e-12
+        assert np.array_equal(kept[margin], (u[None, :] < pi)[margin])
+
+
+def test_budget_query_clips_everything_when_the_budget_covers_all():
+    qg = np.full((2, 16), 0.5)
+    qg[1, ::2] = -0.25
+    qg[1, 1::2] = 0.25
+    u = philox.uniforms(3, 0, philox.TAG_BERNOULLI, 16)
+    qt, kept, clipped, _ = O.budget_query(qg, u, 16)   # m |q_i| >= ||q||_1 for equal magnitudes
+    assert clipped.all() and kept.all() and np.array_equal(qt, qg)
+    qt, kept, _, _ = O.budget_query(np.zeros((1, 16)), u, 4)
+    assert not kept.any() and not qt.any()
+
+
+def test_budget_kept_count_expectation():
+    rng = np.random.default_rng(23)
+    qg = rng.standard_normal((1, 128)).astype(np.float16).astype(np.float64)
+    m = 24
+    pi = np.minimum(1.0, m * np.abs(qg[0]) / np.abs(qg[0]).sum())
+    counts = [O.budget_query(qg, philox.uniforms(s, 0, philox.TAG_BERNOULLI, 128), m)[1].sum()
+              for s in range(2000)]
+    sd = np.sqrt((pi * (1 - pi)).sum() / len(counts))
+    assert abs(np.mean(counts) - pi.sum()) < 4 * sd
+    assert pi.sum() <= m + 1e-9
