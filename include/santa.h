@@ -194,6 +194,18 @@ int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* 
                        int32_t* indices_out, float* scores_out, uint8_t* kept_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Budget variant of santa_bernoulli_qk: head h keeps feature i with
+ * probability pi_i = min(1, budget * |q_hi| / ||q_h||_1) (decided exactly on
+ * the group-shared uniform u_i, same stream as santa_bernoulli_qk), so about
+ * `budget` features per head are kept, and a kept feature takes the value
+ * q_hi / pi_i: q_hi itself where pi_i = 1, sign(q_hi) * ||q_h||_1 / budget
+ * otherwise (E[q~] = q).  budget: 1 .. d.  Everything else is as for
+ * santa_bernoulli_qk. */
+int santa_bernoulli_qk_budget(const santa_problem* problem, const void* q, const void* K_fm, const void* V,
+                              const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, int32_t budget,
+                              float* out, int32_t* indices_out, float* scores_out, uint8_t* kept_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Relayout a row-major K [B][H_kv][max_n_k][d] into the 64-key feature-major
  * tiles read by santa_bernoulli_qk: K_fm[b][h][t][i][x] = K[b][h][64 t + x][i].
  * max_n_k must be a multiple of 64; K and K_fm must not overlap. */

@@ -57,6 +57,7 @@ struct DecodeParams {
   const int32_t* block_table;  // paged cache: [B][max_n_k / block_size] block of each key range, else null
   int lg_block;         // paged cache: log2(block_size)
   int num_blocks;       // paged cache: blocks in K and V, each [Hkv][block_size][D]
+  int budget;           // Bernoulli budget variant: expected kept features per head (m), else 0
   uint64_t seed;
   int D, G;
   int occ;              // sampling kernel variant: 1 = one item per workgroup, 2 = items taken in turn
@@ -64,10 +65,10 @@ struct DecodeParams {
 };
 static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");
 
-enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2, kOpDecodeF8 = 3, kOpDecodePaged = 4 };
+enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2, kOpDecodeF8 = 3, kOpDecodePaged = 4, kOpBernoulliBudget = 5 };
 
 // Key cache kinds of the sampling kernel.
-enum KeyKind { kKeyF16 = 0, kKeyBernoulli = 1, kKeyF8 = 2, kKeyF16Paged = 3 };
+enum KeyKind { kKeyF16 = 0, kKeyBernoulli = 1, kKeyF8 = 2, kKeyF16Paged = 3, kKeyBernoulliBudget = 4 };
 constexpr int kMaxBlocksPerSplit = kSplit / 16;  // smallest block: 16 keys
 
 // Resident-workgroup capacity of the current device for a kernel variant.

@@ -79,7 +79,7 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Resident-workgroup capacity per (device, kernel variant), computed once.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 5 /*kernel*/ * 2 /*workgroups per CU*/;
+constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 6 /*kernel*/ * 2 /*workgroups per CU*/;
 std::mutex g_cap_mutex;
 int g_cap[kMaxDevices][kVariants];
 
@@ -94,6 +94,7 @@ int key_kind(int op) {
     case santa::kOpBernoulli: return santa::kKeyBernoulli;
     case santa::kOpDecodeF8: return santa::kKeyF8;
     case santa::kOpDecodePaged: return santa::kKeyF16Paged;
+    case santa::kOpBernoulliBudget: return santa::kKeyBernoulliBudget;
     default: return santa::kKeyF16;
   }
 }
@@ -171,7 +172,7 @@ int choose_grid(DecodeParams& d, int kind) {
 int sampled_step(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
                  uint8_t* kept_out, const float* k_scale, const Paging& pg, void* ws, size_t ws_bytes, void* stream,
-                 int kind) {
+                 int kind, int budget = 0) {
   int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes);
   if (st != SANTA_OK) return st;
   if (kind == santa::kOpDecodeF8) {
@@ -182,7 +183,9 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   if (S < 1 || S > SANTA_MAX_S) return SANTA_ERR_SHAPE;
   if (mode != SANTA_IID && mode != SANTA_STRATIFIED && mode != SANTA_SYSTEMATIC) return SANTA_ERR_MODE;
   if ((indices_out && !aligned(indices_out, 4)) || (scores_out && !aligned(scores_out, 4))) return SANTA_ERR_ALIGN;
-  if (kind == santa::kOpBernoulli && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
+  const bool bern = kind == santa::kOpBernoulli || kind == santa::kOpBernoulliBudget;
+  if (bern && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
+  if (kind == santa::kOpBernoulliBudget && (budget < 1 || budget > p->head_dim)) return SANTA_ERR_SHAPE;
   DecodeParams d = base_params(p, q, K, V, n_k, out, ws, ws_bytes);
   d.idx_out = indices_out;
   d.scores_out = scores_out;
@@ -191,6 +194,7 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   d.block_table = pg.block_table;
   d.lg_block = pg.lg_block;
   d.num_blocks = pg.num_blocks;
+  d.budget = budget;
   d.S = S;
   d.mode = mode;
   d.seed = seed;
@@ -249,6 +253,14 @@ int santa_bernoulli_qk(const santa_problem* problem, const void* q, const void* 
                        size_t workspace_bytes, void* stream) {
   return sampled_step(problem, q, K_fm, V, n_k, S, mode, seed, out, indices_out, scores_out, kept_out, nullptr,
                       Paging{}, workspace, workspace_bytes, stream, santa::kOpBernoulli);
+}
+
+int santa_bernoulli_qk_budget(const santa_problem* problem, const void* q, const void* K_fm, const void* V,
+                              const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, int32_t budget,
+                              float* out, int32_t* indices_out, float* scores_out, uint8_t* kept_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return sampled_step(problem, q, K_fm, V, n_k, S, mode, seed, out, indices_out, scores_out, kept_out, nullptr,
+                      Paging{}, workspace, workspace_bytes, stream, santa::kOpBernoulliBudget, budget);
 }
 
 int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,

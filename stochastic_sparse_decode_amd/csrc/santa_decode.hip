@@ -67,6 +67,7 @@ struct Shared {
   int next_item;
   // Bernoulli mode
   float A[8];
+  uint64_t l1w[kWaves][8];  // budget variant: per-wave sums of |q| * 2^24
   int wcount[kWaves];
   int nu;
 };
@@ -80,14 +81,41 @@ struct Shared {
 // ---------------------------------------------------------------------------
 // info[j] = (feature index << 16) | keep/sign bits of the j-th kept feature of
 // the union; wt[j] = its fp16 query weight (+1, -1 or 0) for each head, and
-// zero for every j past the union (so padded steps add nothing).
-template <int D, int G>
+// zero for every j past the union (so padded steps add nothing).  Head g's
+// query is then A_g * wt (+ wt2 in the budget variant).
+//
+// Budget variant (BUDGET): feature i of head g is kept with probability
+// pi = min(1, m |q_gi| / ||q_g||_1) and takes the value q_gi / pi: a clipped
+// feature (pi = 1) keeps q_gi exactly (its fp16 value, in wt2), any other
+// kept one sign(q_gi) ||q_g||_1 / m (a sign in wt, A_g = ||q_g||_1 / m).  With
+// Q = |q| * 2^24 and U = the uniform's 24 bits (integers), keep <=>
+// U * L1 < m * Q * 2^24 (L1 = sum of Q) and clipped <=> m * Q >= L1, both
+// decided exactly in 128- and 64-bit integers.
+template <int D, int G, bool BUDGET>
 __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, int hk, bool write_kept,
-                                                Shared& sh, uint32_t* info, uint4* wt) {
+                                                Shared& sh, uint32_t* info, uint4* wt, uint4* wt2) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
-  // A_g = max |q_g| : wave g-loop over features
-  if (w == 0) {
+  if constexpr (BUDGET) {
+    // L1_g = sum_i |q_gi| * 2^24 (an exact integer below 2^47)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint64_t v = tid < D ? (uint64_t)((double)fabsf((float)qb[g * D + tid]) * 16777216.0) : 0ull;
+      for (int m = 1; m < 64; m <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+        v += ((uint64_t)hi << 32) | lo;
+      }
+      if (lane == 0) sh.l1w[w][g] = v;
+    }
+    __syncthreads();
+    if (tid < G) {
+      uint64_t l1 = 0;
+      for (int x = 0; x < (D + 63) / 64; ++x) l1 += sh.l1w[x][tid];
+      sh.l1w[0][tid] = l1;
+      sh.A[tid] = (float)((double)l1 * (1.0 / 16777216.0) / (double)p.budget);
+    }
+  } else if (w == 0) {
+    // A_g = max |q_g| : wave g-loop over features
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float a = 0.f;
@@ -100,17 +128,31 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
   bool any = false;
   uint32_t bits = 0;
   uint32_t hw[4] = {0u, 0u, 0u, 0u};  // fp16 weights of the G heads, two per word
+  uint32_t hq[4] = {0u, 0u, 0u, 0u};  // budget variant: exact query values of clipped features
   if (tid < D) {
     const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hkv + hk), kTagBernoulli, (uint32_t)(tid >> 2));
-    const double ub = (double)uniform_bits(word_of(blk, tid & 3));
+    const uint32_t ux = uniform_bits(word_of(blk, tid & 3));
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float qi = (float)qb[g * D + tid];
-      // u * A < |q|  <=>  (x >> 8) * A < |q| * 2^24, exact in fp64
-      const bool keep = ub * (double)sh.A[g] < (double)fabsf(qi) * 16777216.0;
+      const _Float16 qh = qb[g * D + tid];
+      const float qi = (float)qh;
+      bool keep, clipped = false;
+      if constexpr (BUDGET) {
+        const uint64_t Q = (uint64_t)((double)fabsf(qi) * 16777216.0);
+        const uint64_t L1 = sh.l1w[0][g];
+        const uint64_t mq = (uint64_t)p.budget * Q;  // below 2^47
+        const uint64_t lhs_hi = __umul64hi((uint64_t)ux, L1), lhs_lo = (uint64_t)ux * L1;
+        const uint64_t rhs_hi = mq >> 40, rhs_lo = mq << 24;
+        keep = lhs_hi < rhs_hi || (lhs_hi == rhs_hi && lhs_lo < rhs_lo);
+        clipped = keep && mq >= L1;
+      } else {
+        // u * A < |q|  <=>  (x >> 8) * A < |q| * 2^24, exact in fp64
+        keep = (double)ux * (double)sh.A[g] < (double)fabsf(qi) * 16777216.0;
+      }
       if (keep) bits |= (1u << (2 * g)) | ((qi < 0.f ? 1u : 0u) << (2 * g + 1));
-      const uint32_t h16 = keep ? (qi < 0.f ? 0xBC00u : 0x3C00u) : 0u;  // -1, +1 or 0 in fp16
+      const uint32_t h16 = keep && !clipped ? (qi < 0.f ? 0xBC00u : 0x3C00u) : 0u;  // -1, +1 or 0 in fp16
       hw[g >> 1] |= h16 << (16 * (g & 1));
+      if (clipped) hq[g >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * (g & 1));
       any |= keep;
       if (write_kept) p.kept_out[(size_t)(b * p.Hq + hk * G + g) * D + tid] = keep ? 1 : 0;
     }
@@ -125,16 +167,20 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
     const int pos = before + (w == 1 ? sh.wcount[0] : 0);
     info[pos] = ((uint32_t)tid << 16) | bits;
     wt[pos] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    if constexpr (BUDGET) wt2[pos] = make_uint4(hq[0], hq[1], hq[2], hq[3]);
   }
-  for (int j = nu + tid; j < 128; j += kThreads) wt[j] = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = nu + tid; j < 128; j += kThreads) {
+    wt[j] = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (BUDGET) wt2[j] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (tid == 0) sh.nu = nu;
   __syncthreads();
 }
 
-template <int D, int G>
+template <int D, int G, bool BUDGET>
 __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, int hk, int k0, int len,
                                                 float* cdf, float* mx, const Shared& sh, const uint32_t* info,
-                                                const uint4* wt) {
+                                                const uint4* wt, const uint4* wt2) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int half = lane >> 5, t4 = (lane >> 3) & 3, ko = lane & 7;
   const int ti = w * 4 + t4;  // tile of this lane inside the split (16 tiles)
@@ -143,11 +189,16 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
   const int tile = min(k0 / kTile + ti, (k0 + len - 1) / kTile);
   const _Float16* tb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * tiles_per_head + tile) * (size_t)(D * kTile);
   const int nu = sh.nu;
-  float acc[G][8];
+  float acc[G][8];                      // sums against the sign weights (factor A_g)
+  float acc2[BUDGET ? G : 1][8];        // budget variant: against the clipped values (factor 1)
 #pragma unroll
   for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+#pragma unroll
+  for (int g = 0; g < (BUDGET ? G : 1); ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc2[g][e] = 0.f;
 
   // A lane takes the kept features j = 2 x + half of the list, two steps at a
   // time: the two features' values of a key form one fp16 pair, and so do the
@@ -166,11 +217,19 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
     for (int x = 0; x < UNR; x += 2) {
       const int j0 = 2 * (f0 + x) + half;  // j0 + 2 < 128: the table holds 128 entries
       const uint4 wa = wt[j0], wc = wt[j0 + 2];
-      uint32_t wp[G];
+      uint32_t wp[G], wq[BUDGET ? G : 1];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const uint32_t a = word_of(wa, g >> 1), c = word_of(wc, g >> 1);
         wp[g] = __builtin_amdgcn_perm(c, a, (g & 1) ? 0x07060302u : 0x05040100u);
+      }
+      if constexpr (BUDGET) {
+        const uint4 qa = wt2[j0], qc = wt2[j0 + 2];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t a = word_of(qa, g >> 1), c = word_of(qc, g >> 1);
+          wq[g] = __builtin_amdgcn_perm(c, a, (g & 1) ? 0x07060302u : 0x05040100u);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -181,6 +240,10 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
         for (int g = 0; g < G; ++g) {
           acc[g][2 * i] = __builtin_amdgcn_fdot2(as_h2(wp[g]), as_h2(klo), acc[g][2 * i], false);
           acc[g][2 * i + 1] = __builtin_amdgcn_fdot2(as_h2(wp[g]), as_h2(khi), acc[g][2 * i + 1], false);
+          if constexpr (BUDGET) {
+            acc2[g][2 * i] = __builtin_amdgcn_fdot2(as_h2(wq[g]), as_h2(klo), acc2[g][2 * i], false);
+            acc2[g][2 * i + 1] = __builtin_amdgcn_fdot2(as_h2(wq[g]), as_h2(khi), acc2[g][2 * i + 1], false);
+          }
         }
       }
     }
@@ -193,7 +256,8 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
     for (int e = 0; e < 8; ++e) {
       const float tot = acc[g][e] + __shfl_xor(acc[g][e], 32, 64);
       const int row = ti * kTile + ko * 8 + e;
-      const float s = tot * sc;
+      float s = tot * sc;
+      if constexpr (BUDGET) s = fmaf(acc2[g][e] + __shfl_xor(acc2[g][e], 32, 64), p.scale, s);
       if (half == 0 && row < len) {
         cdf[g * kPad + lidx(row)] = s;
         mx[g] = fmaxf(mx[g], s);
@@ -283,7 +347,8 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 //  sampling tail of one item never stalls the K stream of the next.
 template <int D, int G, int KIND, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
-  constexpr bool BERN = KIND == kKeyBernoulli;
+  constexpr bool BUDGET = KIND == kKeyBernoulliBudget;
+  constexpr bool BERN = KIND == kKeyBernoulli || BUDGET;
   constexpr bool PAGED = KIND == kKeyF16Paged;
   extern __shared__ __align__(16) unsigned char smem[];
   using L = Lds<D, G, OCC>;
@@ -293,6 +358,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   __shared__ Shared sh;
   __shared__ uint32_t binfo[BERN ? 128 : 1];  // Bernoulli kept-feature union
   __shared__ uint4 bwt[BERN ? 128 : 1];       // and its per-head fp16 weights
+  __shared__ uint4 bwt2[BUDGET ? 128 : 1];    // budget variant: exact values of clipped features
   // paged cache: the block of each block-sized key range of the item in
   // score buffer wb (validated; an out-of-range entry reads block 0)
   __shared__ int pblk[PAGED ? 2 : 1][PAGED ? kMaxBlocksPerSplit : 1];
@@ -767,8 +833,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     // ---- score stage: all keys of the split, G query heads ----------------
     float mx[G];
     if constexpr (BERN) {
-      bernoulli_setup<D, G>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo, bwt);
-      score_bernoulli<D, G>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt);
+      bernoulli_setup<D, G, BUDGET>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo, bwt, bwt2);
+      score_bernoulli<D, G, BUDGET>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt, bwt2);
     } else if constexpr (KIND == kKeyF8) {
       score_rowmajor_f8<D, G, OCC == 2 ? (G > kWaves ? 4 : 8) : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     } else {
@@ -951,6 +1017,7 @@ int capacity(int D, int G) {
 template <int OCC>
 int capacity_kind(int D, int G, int key_kind) {
   if (key_kind == kKeyBernoulli) return capacity<kKeyBernoulli, OCC>(D, G);
+  if (key_kind == kKeyBernoulliBudget) return capacity<kKeyBernoulliBudget, OCC>(D, G);
   if (key_kind == kKeyF8) return capacity<kKeyF8, OCC>(D, G);
   if (key_kind == kKeyF16Paged) return capacity<kKeyF16Paged, OCC>(D, G);
   return capacity<kKeyF16, OCC>(D, G);
@@ -959,6 +1026,7 @@ int capacity_kind(int D, int G, int key_kind) {
 template <int OCC>
 hipError_t dispatch_kind(const DecodeParams& p, int key_kind, hipStream_t stream) {
   if (key_kind == kKeyBernoulli) return dispatch<kKeyBernoulli, OCC>(p, stream);
+  if (key_kind == kKeyBernoulliBudget) return dispatch<kKeyBernoulliBudget, OCC>(p, stream);
   if (key_kind == kKeyF8) return dispatch<kKeyF8, OCC>(p, stream);
   if (key_kind == kKeyF16Paged) return dispatch<kKeyF16Paged, OCC>(p, stream);
   return dispatch<kKeyF16, OCC>(p, stream);

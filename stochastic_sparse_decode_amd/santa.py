@@ -63,6 +63,8 @@ def library():
     lib.santa_dense_decode.restype = ctypes.c_int
     lib.santa_bernoulli_qk.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, vp, sz, vp]
     lib.santa_bernoulli_qk.restype = ctypes.c_int
+    lib.santa_bernoulli_qk_budget.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.santa_bernoulli_qk_budget.restype = ctypes.c_int
     lib.santa_pack_k_feature_major.argtypes = [P, vp, vp, vp]
     lib.santa_pack_k_feature_major.restype = ctypes.c_int
     lib.santa_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
@@ -268,8 +270,12 @@ def santa_pack_k_feature_major(K, K_fm=None, stream=None):
 
 
 def santa_bernoulli_qk(q, K_fm, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
-                       kept=None, workspace=None, stream=None):
-    """Bernoulli qK^T step + SANTA value stage; returns ``out`` (B, H_q, d) fp32."""
+                       kept=None, workspace=None, stream=None, budget=0):
+    """Bernoulli qK^T step + SANTA value stage; returns ``out`` (B, H_q, d) fp32.
+
+    budget = 0: ternary queries (keep probability |q_i| / max|q|); budget = m
+    in [1, d]: the budget variant (keep probability min(1, m |q_i| / ||q||_1)).
+    """
     dev = q.device
     for t, nm in ((q, "q"), (K_fm, "K_fm"), (V, "V")):
         _expect(t, nm, torch.float16, dev)
@@ -286,11 +292,18 @@ def santa_bernoulli_qk(q, K_fm, V, n_k, S, mode, seed, scale, out=None, indices=
     if workspace is None:
         workspace = new_workspace(prob, dev)
     mode = MODES.get(mode, mode)
-    st = library().santa_bernoulli_qk(ctypes.byref(prob), _ptr(q), _ptr(K_fm), _ptr(V), _ptr(n_k), int(S),
-                                      int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
-                                      _ptr(scores), _ptr(kept), _ptr(workspace), workspace.numel(),
-                                      _stream(stream))
-    _check(st, "santa_bernoulli_qk")
+    if budget:
+        st = library().santa_bernoulli_qk_budget(ctypes.byref(prob), _ptr(q), _ptr(K_fm), _ptr(V), _ptr(n_k),
+                                                 int(S), int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, int(budget),
+                                                 _ptr(out), _ptr(indices), _ptr(scores), _ptr(kept),
+                                                 _ptr(workspace), workspace.numel(), _stream(stream))
+        _check(st, "santa_bernoulli_qk_budget")
+    else:
+        st = library().santa_bernoulli_qk(ctypes.byref(prob), _ptr(q), _ptr(K_fm), _ptr(V), _ptr(n_k), int(S),
+                                          int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
+                                          _ptr(scores), _ptr(kept), _ptr(workspace), workspace.numel(),
+                                          _stream(stream))
+        _check(st, "santa_bernoulli_qk")
     return out
 
 

@@ -128,3 +128,17 @@ def test_paged_host_checks(lib):
     assert call(_prob(max_n_k=4000), block=64, ws_bytes=santa.workspace_bytes(_prob(max_n_k=4000))) == 2
     assert call(p, blocks=0) == 2         # empty pool
     assert call(p, ws_bytes=16) == 5
+
+
+def test_bernoulli_budget_host_checks(lib):
+    vp = ctypes.c_void_p
+    p = _prob()
+    nb = santa.workspace_bytes(p)
+
+    def call(budget, prob=p):
+        return lib.santa_bernoulli_qk_budget(ctypes.byref(prob), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 8, 2, 0,
+                                             budget, vp(FAKE), None, None, None, vp(FAKE), nb, None)
+
+    assert call(0) == 2        # budget below 1
+    assert call(129) == 2      # budget above d
+    assert call(16, _prob(max_n_k=1000)) == 2   # feature-major tiles need max_n_k % 64 == 0

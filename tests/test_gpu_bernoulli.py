@@ -116,3 +116,51 @@ def test_bernoulli_persistent_parity(mode):
     s_o = O.all_scores(q_t, wl.K, wl.n_k, wl.scale)
     m = ~np.isnan(s_o)
     assert np.abs(sc_g[m] - s_o[m]).max() <= 1e-4 * max(1.0, np.abs(s_o[m]).max())
+
+
+# --------------------------------------------------------------------------
+# budget variant: keep probability min(1, m |q| / ||q||_1), value q / pi
+# --------------------------------------------------------------------------
+
+def run_budget(wl, S, mode, seed, m):
+    q, K, V, nk = P.to_dev(wl)
+    K_fm = santa.santa_pack_k_feature_major(K)
+    B, Hq = wl.B, wl.Hq
+    idx = torch.full((B, Hq, S), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((B, Hq, wl.max_n_k), float("nan"), dtype=torch.float32, device="cuda")
+    kept = torch.full((B, Hq, wl.d), 7, dtype=torch.uint8, device="cuda")
+    ws = santa.new_workspace(santa.problem(q, K, wl.scale), q.device)
+    out = santa.santa_bernoulli_qk(q, K_fm, V, nk, S, mode, seed, wl.scale, indices=idx, scores=sc, kept=kept,
+                                   workspace=ws, budget=m)
+    torch.cuda.synchronize()
+    assert santa.santa_workspace_error(ws) == 0
+    return out.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy(), kept.cpu().numpy().astype(bool)
+
+
+BUDGET_CASES = [
+    ("gqa4_m16", lambda: W.random_case(2, 8, 2, 128, [4096, 2500], max_n_k=4096, seed=61), 16),
+    ("gqa4_m64", lambda: W.random_case(1, 8, 2, 128, [3000], max_n_k=3008, seed=62), 64),
+    ("d64_g1_m4", lambda: W.random_case(1, 2, 2, 64, [1000], max_n_k=1024, seed=63), 4),
+    ("g8_m32", lambda: W.random_case(1, 16, 2, 128, [3000], max_n_k=3008, seed=64), 32),
+]
+
+
+@pytest.mark.parametrize("name,make,m", BUDGET_CASES, ids=[c[0] for c in BUDGET_CASES])
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_bernoulli_budget_parity(name, make, m, mode):
+    wl = make()
+    S, seed = 128, 41 + mode
+    print("[bernoulli-budget] %s m=%d mode=%d" % (name, m, mode), flush=True)
+    out_g, idx_g, sc_g, kept_g = run_budget(wl, S, mode, seed, m)
+    out_o, idx_o, kept_o, det = O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, seed, wl.scale,
+                                                   return_detail=True, budget=m)
+    assert np.array_equal(kept_g, kept_o)  # exact integer decision on both sides
+    rep = P.compare_indices(idx_g, idx_o, det, P.BAND)
+    print("   %s" % rep, flush=True)
+    assert rep.bad == 0
+    est = P.oracle_estimate_from_indices(wl.V, idx_g, wl.n_k, wl.Hq, S)
+    assert np.abs(out_g - est).max() <= P.OUT_TOL
+    q_t, _, _ = O.bernoulli_queries(wl.q, wl.Hkv, seed, budget=m)
+    s_o = O.all_scores(q_t, wl.K, wl.n_k, wl.scale)
+    msk = ~np.isnan(s_o)
+    assert np.abs(sc_g[msk] - s_o[msk]).max() <= 1e-4 * max(1.0, np.abs(s_o[msk]).max())
