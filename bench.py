@@ -69,6 +69,8 @@ def parse():
                     choices=["llama32k", "batched", "sweep131k", "bernoulli", "llama32k-fp8k", "batched-paged"])
     ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid"])
     ap.add_argument("--S", type=int, default=128)
+    ap.add_argument("--budget", type=int, default=0,
+                    help="Bernoulli workload: 0 = ternary queries, m > 0 = the budget variant with m features")
     ap.add_argument("--rotate-bytes", type=float, default=2.0, help="GiB of distinct KV copies to rotate over")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of a HIP graph")
@@ -160,7 +162,7 @@ def timed(fn, sets, steps, warmup, graph=True):
     return start.elapsed_time(stop) / steps  # ms per step (= per launch: one launch per step)
 
 
-def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False, fp8_cache=None):
+def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False, fp8_cache=None, budget=0):
     """Time the fp64 oracle on whole decode steps of the same workload (bounded);
     nbytes = the step's algorithmic bytes (the Bernoulli steps use seed 1, as
     the timed GPU steps do, so their kept features and bytes are the same)."""
@@ -174,7 +176,7 @@ def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False, fp8_cache=None):
     n = 0
     while True:
         if bernoulli:
-            O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, 1, wl.scale)
+            O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, 1, wl.scale, budget=budget)
         elif fp8_cache is not None:
             O.santa_decode_fp8k(wl.q, fp8_cache[0], fp8_cache[1], wl.V, wl.n_k, S, mode, n, wl.scale)
         else:
@@ -337,7 +339,7 @@ def main():
     elif args.workload == "bernoulli":
         sets = [(santa.santa_pack_k_feature_major(k), v) for k, v in sets]
         step = lambda kv: santa.santa_bernoulli_qk(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa
-                                                   workspace=ws)
+                                                   workspace=ws, budget=args.budget)
     else:
         step = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
                                              workspace=ws)
@@ -354,7 +356,7 @@ def main():
         # the kept features of the timed steps (every step uses seed 1)
         kept = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         santa.santa_bernoulli_qk(q, sets[0][0], sets[0][1], nk, S, mode, 1, wl.scale, out=out, kept=kept,
-                                 workspace=ws)
+                                 workspace=ws, budget=args.budget)
         torch.cuda.synchronize()
         nbytes = bernoulli_bytes(kept, wl, S)
     elif fp8k:
@@ -389,7 +391,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f8 (E4M3) keys, f16 q and values, f32 accumulate" if fp8k else "f16 in, f32 accumulate",
         "data": "synthetic (seeded; rotated over %d KV copies, %.2f GiB)" % (R, R * set_bytes / (1 << 30)),
-        "config": {"workload": desc, "mode": args.mode, "S": S, "global_batch": wl.B, "seq_len": int(wl.n_k.max()),
+        "config": {"workload": desc + (", budget %d features" % args.budget if args.budget else ""),
+                   "mode": args.mode, "S": S, "global_batch": wl.B, "seq_len": int(wl.n_k.max()),
                    "parallelism": "none (1 GPU)"},
         "algorithmic_bytes_per_step": nbytes,
         "timing": "HIP graph of %d steps, one timed replay" % args.steps if not args.eager else "eager launches",
@@ -411,7 +414,7 @@ def main():
         res["speedup_vs_dense"] = dense_ms / ms
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(wl, S, mode, args.cpu_seconds, nbytes, args.workload == "bernoulli",
-                                           (K8, ks) if fp8k else None)
+                                           (K8, ks) if fp8k else None, args.budget)
     print(json.dumps(res))
 
 
