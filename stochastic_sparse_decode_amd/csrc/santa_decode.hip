@@ -68,6 +68,7 @@ struct Shared {
   // Bernoulli mode
   float A[8];
   uint64_t l1w[kWaves][8];  // budget variant: per-wave sums of |q| * 2^24
+  float amax[kWaves][8];    // ternary queries: per-wave max |q|
   int wcount[kWaves];
   int nu;
 };
@@ -96,63 +97,79 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
                                                 Shared& sh, uint32_t* info, uint4* wt, uint4* wt2) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
-  if constexpr (BUDGET) {
-    // L1_g = sum_i |q_gi| * 2^24 (an exact integer below 2^47)
+  constexpr int QW = (D + 63) / 64;  // waves that hold features
+  // thread tid < D holds feature tid of every head and its uniform; the query
+  // is read once, and its load overlaps the generator's arithmetic
+  _Float16 qh[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      uint64_t v = tid < D ? (uint64_t)((double)fabsf((float)qb[g * D + tid]) * 16777216.0) : 0ull;
+  for (int g = 0; g < G; ++g) qh[g] = tid < D ? qb[g * D + tid] : (_Float16)0;
+  uint32_t ux = 0;
+  if (tid < D) {
+    const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hkv + hk), kTagBernoulli, (uint32_t)(tid >> 2));
+    ux = uniform_bits(word_of(blk, tid & 3));
+  }
+  // per wave: max |q_g| (ternary), or sum of |q_g| * 2^24 (budget; exact
+  // integers, the sum below 2^47); every thread then combines the waves
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if constexpr (BUDGET) {
+      uint64_t v = (uint64_t)((double)fabsf((float)qh[g]) * 16777216.0);
       for (int m = 1; m < 64; m <<= 1) {
         const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
         v += ((uint64_t)hi << 32) | lo;
       }
-      if (lane == 0) sh.l1w[w][g] = v;
-    }
-    __syncthreads();
-    if (tid < G) {
-      uint64_t l1 = 0;
-      for (int x = 0; x < (D + 63) / 64; ++x) l1 += sh.l1w[x][tid];
-      sh.l1w[0][tid] = l1;
-      sh.A[tid] = (float)((double)l1 * (1.0 / 16777216.0) / (double)p.budget);
-    }
-  } else if (w == 0) {
-    // A_g = max |q_g| : wave g-loop over features
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float a = 0.f;
-      for (int i = lane; i < D; i += 64) a = fmaxf(a, fabsf((float)qb[g * D + i]));
+      if (lane == 0 && w < QW) sh.l1w[w][g] = v;
+    } else {
+      float a = fabsf((float)qh[g]);
       for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
-      if (lane == 0) sh.A[g] = a;
+      if (lane == 0 && w < QW) sh.amax[w][g] = a;
     }
   }
   __syncthreads();
+  float A[G];
+  uint64_t L1[BUDGET ? G : 1];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if constexpr (BUDGET) {
+      L1[g] = 0ull;
+#pragma unroll
+      for (int x = 0; x < QW; ++x) L1[g] += sh.l1w[x][g];
+      A[g] = (float)((double)L1[g] * (1.0 / 16777216.0) / (double)p.budget);
+    } else {
+      A[g] = sh.amax[0][g];
+#pragma unroll
+      for (int x = 1; x < QW; ++x) A[g] = fmaxf(A[g], sh.amax[x][g]);
+    }
+  }
+  if (tid < G) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (g == tid) sh.A[g] = A[g];
+  }
   bool any = false;
   uint32_t bits = 0;
   uint32_t hw[4] = {0u, 0u, 0u, 0u};  // fp16 weights of the G heads, two per word
   uint32_t hq[4] = {0u, 0u, 0u, 0u};  // budget variant: exact query values of clipped features
   if (tid < D) {
-    const uint4 blk = stream_block(p.seed, (uint32_t)(b * p.Hkv + hk), kTagBernoulli, (uint32_t)(tid >> 2));
-    const uint32_t ux = uniform_bits(word_of(blk, tid & 3));
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const _Float16 qh = qb[g * D + tid];
-      const float qi = (float)qh;
+      const float qi = (float)qh[g];
       bool keep, clipped = false;
       if constexpr (BUDGET) {
         const uint64_t Q = (uint64_t)((double)fabsf(qi) * 16777216.0);
-        const uint64_t L1 = sh.l1w[0][g];
         const uint64_t mq = (uint64_t)p.budget * Q;  // below 2^47
-        const uint64_t lhs_hi = __umul64hi((uint64_t)ux, L1), lhs_lo = (uint64_t)ux * L1;
+        const uint64_t lhs_hi = __umul64hi((uint64_t)ux, L1[g]), lhs_lo = (uint64_t)ux * L1[g];
         const uint64_t rhs_hi = mq >> 40, rhs_lo = mq << 24;
         keep = lhs_hi < rhs_hi || (lhs_hi == rhs_hi && lhs_lo < rhs_lo);
-        clipped = keep && mq >= L1;
+        clipped = keep && mq >= L1[g];
       } else {
         // u * A < |q|  <=>  (x >> 8) * A < |q| * 2^24, exact in fp64
-        keep = (double)ux * (double)sh.A[g] < (double)fabsf(qi) * 16777216.0;
+        keep = (double)ux * (double)A[g] < (double)fabsf(qi) * 16777216.0;
       }
       if (keep) bits |= (1u << (2 * g)) | ((qi < 0.f ? 1u : 0u) << (2 * g + 1));
       const uint32_t h16 = keep && !clipped ? (qi < 0.f ? 0xBC00u : 0x3C00u) : 0u;  // -1, +1 or 0 in fp16
       hw[g >> 1] |= h16 << (16 * (g & 1));
-      if (clipped) hq[g >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * (g & 1));
+      if (clipped) hq[g >> 1] |= (uint32_t)__builtin_bit_cast(uint16_t, qh[g]) << (16 * (g & 1));
       any |= keep;
       if (write_kept) p.kept_out[(size_t)(b * p.Hq + hk * G + g) * D + tid] = keep ? 1 : 0;
     }
