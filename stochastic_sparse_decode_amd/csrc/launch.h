@@ -22,7 +22,7 @@ constexpr uint32_t kErrBlockTable = 2u;  // a block-table entry out of range (re
 // Device pointers carved out of the caller's workspace.
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
-  uint32_t* work_ctr;   // dynamic work-item counter, returns to 0 at kernel end
+  uint32_t* work_ctr;   // dense kernel: dynamic work-item counter, returns to 0 at kernel end
   uint64_t* launches;   // launch counter of the sampling kernel: kLaunchUnit added per launch
   uint32_t* bar_done;   // [groups] arrivals of split partial outputs (dense), back to 0 at kernel end
   uint64_t* stats;      // [groups][ns][G][2] (tag:32 | split max bits, tag:32 | split mass bits)

@@ -30,12 +30,15 @@
 //        device atomics (split 0 clears the row before it publishes).
 //
 // Scheduling: `grid` workgroups are all resident (grid <= occupancy capacity).
-// Workgroup w starts with item w; further items are taken in increasing order
-// from an atomic counter.  A wave only waits for splits of its own group,
-// all of which have been taken by running workgroups or will be taken by
-// workgroups that finish earlier groups, so the waits always end as long as a
-// group has no more splits than there are workgroups.  Every wait is bounded
-// (kSpinLimit polls); a timeout sets an error bit instead of hanging.
+// One item per workgroup when the items fit (OCC = 1); otherwise (OCC = 2,
+// two workgroups per CU) workgroup x takes the valid splits x, x + grid,
+// x + 2 grid, ... and streams item k before it finishes item k - 1, so its
+// wait for the other splits of item k - 1 overlaps its own K stream.  A wave
+// only waits for splits of its own group, and every workgroup publishes its
+// item of a round before it waits for any item of that round or a later
+// one, so the waits always end as long as a group has no more splits than
+// there are workgroups.  Every wait is bounded (kSpinLimit polls); a timeout
+// sets an error bit instead of hanging.
 #include "device_common.h"
 #include "launch.h"
 #include "score_stage.h"
@@ -64,7 +67,6 @@ struct Lds {
 struct Shared {
   float wmax[2][kWaves][8];  // per score buffer: split maximum of each head, per wave
   uint32_t epoch;  // launch tag of this launch
-  int next_item;
   // Bernoulli mode
   float A[8];
   uint64_t l1w[kWaves][8];  // budget variant: per-wave sums of |q| * 2^24
@@ -462,23 +464,32 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[wb][x][g]);
 
-        double acc = 0.0;
+        uint64_t acc = 0;  // at most kPer * 2^31
         {
           float sv[kPer];
 #pragma unroll
           for (int i = 0; i < kPer; ++i) sv[i] = cg[lidx(lane * kPer + i)];
+          if (len == kSplit) {
 #pragma unroll
-          for (int i = 0; i < kPer; ++i) {
-            // rows past the split's end hold unrelated LDS contents: their
-            // argument is replaced by -1000, whose exponential is 0 in fp32
-            const float wv = exp_nonpos(lane * kPer + i < len ? sv[i] - m : -1000.f);
-            const uint32_t q = (uint32_t)(wv * kFix);  // trunc(w * 2^31), exact: w <= 1
-            acc += (double)q;
-            wt.q[i] = q;
+            for (int i = 0; i < kPer; ++i) {
+              const uint32_t q = (uint32_t)(exp_nonpos(sv[i] - m) * kFix);  // trunc(w * 2^31), exact: w <= 1
+              acc += q;
+              wt.q[i] = q;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+              // rows past the split's end hold unrelated LDS contents: their
+              // argument is replaced by -1000, whose exponential is 0 in fp32
+              const float wv = exp_nonpos(lane * kPer + i < len ? sv[i] - m : -1000.f);
+              const uint32_t q = (uint32_t)(wv * kFix);
+              acc += q;
+              wt.q[i] = q;
+            }
           }
         }
-        const double incl = wave_incl_scan_exact(acc);
-        wt.excl = incl - acc;  // exact: all values are integers below 2^53
+        const double incl = wave_incl_scan_exact((double)acc);
+        wt.excl = incl - (double)acc;  // exact: all values are integers below 2^53
         wt.total = readlane_f64(incl, 63);
         wt.m = m;
   };
@@ -571,6 +582,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 
         // 3. wait for every split of the group, merge
         double Z = 0.0, Olo = 0.0, Ohi = 0.0, rs = 0.0;
+        double cume[kPer + 1];
         {
           // The slots of the first kRegChunks * 64 splits are read together
           // and kept in registers (one round trip however many splits there
@@ -596,6 +608,16 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
               return __ballot(!all) == 0ull;
             };
             poll_issue(it, g, pl);
+            // while the slot reads are in flight: the exact local CDF at the
+            // lane's edges (edge e is the right edge of key lane*kPer+e-1);
+            // an edge at or past the split's last key gets a value above any
+            // split mass, which the clamp to the split's end replaces
+            cume[0] = wt.excl;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) cume[i + 1] = cume[i] + (double)wt.q[i];
+#pragma unroll
+            for (int e = 0; e <= kPer; ++e)
+              if (lane * kPer + e - 1 >= len - 1) cume[e] = 0x1.0p64;
             if (!test()) {
               uint32_t spins = 0;
               while (true) {
@@ -692,38 +714,33 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         } else {
           // systematic / stratified: the number of points below an edge X is a
           // closed-form function of y = X S / Z; a key's count is the
-          // difference at its two edges.  The edges are the same doubles in
-          // the neighbouring lane or split, so every point is counted once.
+          // difference at its two edges.  y = ylo + a cum at an interior edge
+          // (cum the exact local CDF value there), clamped to the split's end
+          // yhi; an edge shared with the neighbouring lane or split is the same
+          // double on both sides (the same operations on the same operands),
+          // so every point is counted once.  The last key of the sequence ends
+          // at t = 1.
           const double inv = (double)S / Z;
-          // edge e is the right edge of the lane's key e - 1 (e = 0: the
-          // lane's left edge); cum is the exact local CDF value there.  The
-          // last key of the sequence ends at t = 1.
-          auto edge = [&](int e, double cum) -> double {
-            return lane * kPer + e - 1 >= len - 1 ? Ohi : fmin(Olo + rs * cum, Ohi);
-          };
+          const double u0 = p.mode == 2 ? usys : 0.0;
+          const double ylo = fma(Olo, inv, -u0), yhi = fma(Ohi, inv, -u0), a = rs * inv;
           auto at_end = [&](int e, int n) -> int { return is_last && lane * kPer + e - 1 >= len - 1 ? S : n; };
           // counts from the points below consecutive edges, one edge at a time
           auto roll = [&](const auto& below) {
-            double cum = wt.excl;
-            int prev_n = below(0, cum);
+            int prev_n = below(0, fmin(fma(cume[0], a, ylo), yhi));
             nstart = prev_n;
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
-              cum += (double)wt.q[i];
-              const int n = below(i + 1, cum);
+              const int n = below(i + 1, fmin(fma(cume[i + 1], a, ylo), yhi));
               cnt[i] = n - prev_n;
               prev_n = n;
             }
           };
           if (p.mode == 2) {
-            // t_k = (k + u) / S:  #{k : t_k Z < X} = ceil(y - u), clamped to [0, S]
-            roll([&](int e, double cum) {
-              return at_end(e, (int)fmin(fmax(ceil(edge(e, cum) * inv - usys), 0.0), (double)S));
-            });
+            // t_k = (k + u) / S:  #{k : t_k Z < X} = ceil(y), clamped to [0, S]
+            roll([&](int e, double y) { return at_end(e, min(max((int)ceil(y), 0), S)); });
           } else {
             // t_k = (k + u_k) / S:  #{k : t_k Z < X} = f + [u_f < y - f], f = floor(y)
-            roll([&](int e, double cum) {
-              const double y = edge(e, cum) * inv;
+            roll([&](int e, double y) {
               const double f = fmin(floor(y), (double)S);
               const uint32_t uf = ug[min((int)f, S - 1)];
               return at_end(e, (int)f + ((f < (double)S && (double)uf * 0x1.0p-24 < y - f) ? 1 : 0));
