@@ -616,8 +616,10 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) cume[i + 1] = cume[i] + (double)wt.q[i];
 #pragma unroll
-            for (int e = 0; e <= kPer; ++e)
+            for (int e = 0; e <= kPer; ++e) {
               if (lane * kPer + e - 1 >= len - 1) cume[e] = 0x1.0p64;
+              asm volatile("" : "+v"(cume[e]));  // computed here, not after the wait
+            }
             if (!test()) {
               uint32_t spins = 0;
               while (true) {
