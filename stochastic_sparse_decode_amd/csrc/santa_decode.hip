@@ -494,6 +494,29 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         wt.m = m;
   };
 
+  // The pipelined variant finishes an item after streaming the next one: the
+  // weights stay in the item's score buffer (each score of head g replaced by
+  // its weight) instead of being computed a second time.  Only wave g
+  // accesses head g's row from here on, and one wave's LDS accesses complete
+  // in order.
+  auto stash_weights = [&](int g, float* scb, const Weights& wt) {
+    uint32_t* cg = (uint32_t*)(scb + g * kPad);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) cg[lidx(lane * kPer + i)] = wt.q[i];
+  };
+  auto reload_weights = [&](int g, const float* scb, Weights& wt) {
+    const uint32_t* cg = (const uint32_t*)(scb + g * kPad);
+    uint64_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      wt.q[i] = cg[lidx(lane * kPer + i)];
+      acc += wt.q[i];
+    }
+    const double incl = wave_incl_scan_exact((double)acc);
+    wt.excl = incl - (double)acc;
+    wt.total = readlane_f64(incl, 63);
+  };
+
   // Publish head g's (split max, split mass).
   auto publish = [&](const ItemCtx& it, int g, const Weights& wt) {
         const uint32_t tag = sh.epoch;
@@ -919,6 +942,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         Gather gt;
         tail_a(it, g, scb, wb, wt, gt);
         tail_b(it, g, wb, gt);
+      } else {
+        stash_weights(g, scb, wt);
       }
     }
   };
@@ -985,7 +1010,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         for (int g = w; g < G; g += kWaves) {
           Weights wt;
           Gather gt;
-          weights(prev, g, score_buf(cb ^ 1), cb ^ 1, wt);
+          reload_weights(g, score_buf(cb ^ 1), wt);
           tail_a(prev, g, score_buf(cb ^ 1), cb ^ 1, wt, gt);
           tail_b(prev, g, cb ^ 1, gt);
         }
