@@ -47,13 +47,18 @@ namespace santa {
 
 namespace {
 
-constexpr int kUniRow = kMaxS + 64;  // per-head uniform / list row (+ one spare slot per lane)
+constexpr int kUniRow = kMaxS + 64;  // per-head row of uniforms
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 // Dynamic LDS of one workgroup:
-//   sc  [nbuf][G][kPad]  fp32 scores; the i.i.d. scheme overwrites a head's
-//                        scores with its local CDF once the weights are known
-//   uni [G][kUniRow]     24-bit uniforms of the points (stratified, i.i.d.);
-//                        afterwards the head's list of selected keys
+//   sc  [nbuf][G][kPad]  fp32 scores; then a head's weights (the i.i.d.
+//                        scheme: its local CDF), then its list of selected
+//                        keys (kMaxS entries + one spare slot per lane)
+//   uni [G][kUniRow]     24-bit uniforms of the points (stratified, i.i.d.)
 //   cnt [G][kSplit / 2]  i.i.d. points per key, two 16-bit counters a word
 template <int D, int G, int OCC>
 struct Lds {
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   // held in doubles, so every partial sum is exact in any order).
   struct Weights {
     uint32_t q[kPer];
-    double excl, total;
+    double excl, lsum, total;  // the lane's exclusive prefix and own sum, the split's total
     float m;
   };
   auto weights = [&](const ItemCtx& it, int g, const float* scb, int wb, Weights& wt) {
@@ -489,7 +494,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           }
         }
         const double incl = wave_incl_scan_exact((double)acc);
-        wt.excl = incl - (double)acc;  // exact: all values are integers below 2^53
+        wt.lsum = (double)acc;
+        wt.excl = incl - wt.lsum;  // exact: all values are integers below 2^53
         wt.total = readlane_f64(incl, 63);
         wt.m = m;
   };
@@ -513,7 +519,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       acc += wt.q[i];
     }
     const double incl = wave_incl_scan_exact((double)acc);
-    wt.excl = incl - (double)acc;
+    wt.lsum = (double)acc;
+    wt.excl = incl - wt.lsum;
     wt.total = readlane_f64(incl, 63);
   };
 
@@ -570,7 +577,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       pl.rc[c] = load_dev(slots + (x * G + g) * 2 + 1);
     }
   };
-  auto tail_a = [&](const ItemCtx& it, int g, float* scb, int wb, const Weights& wt, Gather& gt) {
+  auto tail_a = [&](const ItemCtx& it, int g, float* scb, int wb, const Weights& wt, Gather& gt, bool stashed) {
         const int s = it.s, len = it.len, k0 = it.k0, nsg = it.nsg, b = it.b, hk = it.hk, h0 = it.h0;
         const bool is_last = it.is_last;
         const uint32_t tag = sh.epoch;
@@ -599,13 +606,14 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             if (lane * kPer + i < len) cg[lidx(lane * kPer + i)] = (float)cum;  // nondecreasing
           }
           for (int i = lane; i < kSplit / 2; i += 64) cw[i] = 0u;
+        } else if (!stashed) {
+          stash_weights(g, scb, wt);  // read back by the lanes that place points
         }
         const double usys = p.mode == 2 ? uniform_f64(stream_block(p.seed, row, kTagSystematic, 0u).x) : 0.0;
         wave_lds_sync();
 
         // 3. wait for every split of the group, merge
         double Z = 0.0, Olo = 0.0, Ohi = 0.0, rs = 0.0;
-        double cume[kPer + 1];
         {
           // The slots of the first kRegChunks * 64 splits are read together
           // and kept in registers (one round trip however many splits there
@@ -631,18 +639,6 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
               return __ballot(!all) == 0ull;
             };
             poll_issue(it, g, pl);
-            // while the slot reads are in flight: the exact local CDF at the
-            // lane's edges (edge e is the right edge of key lane*kPer+e-1);
-            // an edge at or past the split's last key gets a value above any
-            // split mass, which the clamp to the split's end replaces
-            cume[0] = wt.excl;
-#pragma unroll
-            for (int i = 0; i < kPer; ++i) cume[i + 1] = cume[i] + (double)wt.q[i];
-#pragma unroll
-            for (int e = 0; e <= kPer; ++e) {
-              if (lane * kPer + e - 1 >= len - 1) cume[e] = 0x1.0p64;
-              asm volatile("" : "+v"(cume[e]));  // computed here, not after the wait
-            }
             if (!test()) {
               uint32_t spins = 0;
               while (true) {
@@ -706,14 +702,18 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           Z = (double)carry;
         }
 
-        // 4. points per key of this lane: cnt[i] for key lane*kPer+i; the
-        // lane's points are numbers nstart .. nstart + sum(cnt) - 1 in the
-        // ascending order of the S points
-        int cnt[kPer];
-        int nstart = 0;
+        // 4. points per key and the list of selected keys (key | count << 16),
+        // in key order, in the head's score row (free by now: the i.i.d.
+        // search is done with it, the other schemes read the weights there
+        // only at keys above any list position written so far); the sampled
+        // indices (optional output), ascending
+        uint32_t* list = (uint32_t*)cg;
+        int* ix = p.idx_out ? p.idx_out + (size_t)row * S : nullptr;
+        int nsel = 0;
         if (p.mode == 0) {
           // i.i.d.: the points in [Olo, Ohi) (the last split: [Olo, Z)) are
           // searched one by one; earlier points are counted for the numbering
+          int cnt[kPer];
           int before = 0;
           for (int k = lane; k < S; k += 64) {
             const double tz = (double)ug[k] * 0x1.0p-24 * Z;
@@ -735,83 +735,127 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             lsum += cnt[2 * i] + cnt[2 * i + 1];
           }
           const int bsum = __builtin_amdgcn_readlane(wave_incl_scan_dpp(before), 63);
-          nstart = bsum + wave_incl_scan_dpp(lsum) - lsum;
+          const int nstart = bsum + wave_incl_scan_dpp(lsum) - lsum;
+          if (ix) {
+            int k = nstart;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i)
+              for (int c = 0; c < cnt[i] && k < S; ++c) ix[k++] = k0 + lane * kPer + i;
+          }
+          uint32_t sel = 0;
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) sel |= (cnt[i] > 0 ? 1u : 0u) << i;
+          const int nl = __popc(sel);
+          const int incl_n = wave_incl_scan_dpp(nl);
+          nsel = __builtin_amdgcn_readlane(incl_n, 63);
+          if (nsel > 0) {
+            wave_lds_sync();  // every lane is done with the local CDF
+            // every key is written; an unselected one goes to the lane's own
+            // slot past the list (no branches, no two lanes on one address)
+            int pos = incl_n - nl;
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+              const bool on = cnt[i] > 0;
+              list[on ? pos : kMaxS + lane] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
+              pos += on ? 1 : 0;
+            }
+          }
         } else {
           // systematic / stratified: the number of points below an edge X is a
           // closed-form function of y = X S / Z; a key's count is the
-          // difference at its two edges.  y = ylo + a cum at an interior edge
-          // (cum the exact local CDF value there), clamped to the split's end
-          // yhi; an edge shared with the neighbouring lane or split is the same
-          // double on both sides (the same operations on the same operands),
-          // so every point is counted once.  The last key of the sequence ends
-          // at t = 1.
+          // difference at its two edges.  y = ylo + a cum, cum the exact local
+          // CDF value at the edge, clamped to the split's end yhi; an edge
+          // shared with the neighbouring key, lane or split is the same double
+          // on both sides (the same operations on the same exact operands), so
+          // every point is counted once.  The sequence's last key ends at t = 1.
           const double inv = (double)S / Z;
           const double u0 = p.mode == 2 ? usys : 0.0;
           const double ylo = fma(Olo, inv, -u0), yhi = fma(Ohi, inv, -u0), a = rs * inv;
-          auto at_end = [&](int e, int n) -> int { return is_last && lane * kPer + e - 1 >= len - 1 ? S : n; };
-          // counts from the points below consecutive edges, one edge at a time
-          auto roll = [&](const auto& below) {
-            int prev_n = below(0, fmin(fma(cume[0], a, ylo), yhi));
-            nstart = prev_n;
+          auto place = [&](auto sys) {
+            // number of points below the right edge of key k (k = -1: the
+            // split's left edge), cum the exact local CDF value there
+            auto n_at = [&](int k, double cum) -> int {
+              const bool end = k >= len - 1;
+              const double y = end ? yhi : fmin(fma(cum, a, ylo), yhi);
+              int n;
+              if constexpr (decltype(sys)::value) {
+                n = min(max((int)ceil(y), 0), S);  // t_k = (k + u) / S: ceil(y)
+              } else {
+                // t_k = (k + u_k) / S: f + [u_f < y - f], f = floor(y)
+                const double f = fmin(floor(y), (double)S);
+                const uint32_t uf = ug[min((int)f, S - 1)];
+                n = (int)f + ((f < (double)S && (double)uf * 0x1.0p-24 < y - f) ? 1 : 0);
+              }
+              return end && is_last ? S : n;
+            };
+            // the lane's two edges: points nL .. nR - 1 fall in its keys
+            const int nL = n_at(lane * kPer - 1, wt.excl);
+            const int nR = n_at(lane * kPer + kPer - 1, wt.excl + wt.lsum);
+            // Only lanes with points need their keys' edges.  Four such lanes
+            // at a time, one per row of 16 lanes: lane i of row r takes key i
+            // of the r-th lane, whose exact CDF value comes from a scan of the
+            // weights over the row.
+            uint64_t act = __ballot(nR > nL);
+            const int r = lane >> 4, i = lane & 15;
+            while (act != 0ull) {
+              int src[4];
 #pragma unroll
-            for (int i = 0; i < kPer; ++i) {
-              const int n = below(i + 1, fmin(fma(cume[i + 1], a, ylo), yhi));
-              cnt[i] = n - prev_n;
-              prev_n = n;
+              for (int x = 0; x < 4; ++x) {
+                src[x] = act != 0ull ? __ffsll((unsigned long long)act) - 1 : -1;
+                act &= act - 1ull;  // (no effect once empty)
+              }
+              const int sl = r == 0 ? src[0] : r == 1 ? src[1] : r == 2 ? src[2] : src[3];
+              const bool valid = sl >= 0;
+              const int key = (valid ? sl : 0) * kPer + i;
+              const uint32_t qk = list[lidx(key)];  // the key's weight
+              double c = valid ? (double)qk : 0.0;
+              c += __builtin_bit_cast(double, dpp_u64<0x111, 0xF>(__builtin_bit_cast(uint64_t, c)));
+              c += __builtin_bit_cast(double, dpp_u64<0x112, 0xF>(__builtin_bit_cast(uint64_t, c)));
+              c += __builtin_bit_cast(double, dpp_u64<0x114, 0xF>(__builtin_bit_cast(uint64_t, c)));
+              c += __builtin_bit_cast(double, dpp_u64<0x118, 0xF>(__builtin_bit_cast(uint64_t, c)));
+              double ex = 0.0;
+              int nl0 = 0;
+#pragma unroll
+              for (int x = 0; x < 4; ++x) {
+                const int sx = src[x] >= 0 ? src[x] : 0;
+                const double e = readlane_f64(wt.excl, sx);
+                const int n0 = __builtin_amdgcn_readlane(nL, sx);
+                ex = r == x ? e : ex;
+                nl0 = r == x ? n0 : nl0;
+              }
+              const int nr = n_at(key, ex + c);  // right edge of the key
+              const int up = __builtin_amdgcn_update_dpp(0, nr, 0x111, 0xF, 0xF, true);  // right edge of key - 1
+              const int nl = i == 0 ? nl0 : up;
+              const int cnt = valid ? nr - nl : 0;
+              const uint64_t selm = __ballot(cnt > 0);
+              const int pos = nsel + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(selm >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)selm, 0u));
+              if (cnt > 0) {
+                list[pos] = (uint32_t)key | ((uint32_t)cnt << 16);
+                if (ix)
+                  for (int x = 0; x < cnt && nl + x < S; ++x) ix[nl + x] = k0 + key;
+              }
+              nsel += __popcll(selm);
             }
           };
-          if (p.mode == 2) {
-            // t_k = (k + u) / S:  #{k : t_k Z < X} = ceil(y), clamped to [0, S]
-            roll([&](int e, double y) { return at_end(e, min(max((int)ceil(y), 0), S)); });
-          } else {
-            // t_k = (k + u_k) / S:  #{k : t_k Z < X} = f + [u_f < y - f], f = floor(y)
-            roll([&](int e, double y) {
-              const double f = fmin(floor(y), (double)S);
-              const uint32_t uf = ug[min((int)f, S - 1)];
-              return at_end(e, (int)f + ((f < (double)S && (double)uf * 0x1.0p-24 < y - f) ? 1 : 0));
-            });
-          }
+          if (p.mode == 2)
+            place(Flag<true>{});
+          else
+            place(Flag<false>{});
         }
 
-        // sampled indices (optional output), ascending
-        if (p.idx_out) {
-          int* ix = p.idx_out + (size_t)row * S;
-          int k = nstart;
-#pragma unroll
-          for (int i = 0; i < kPer; ++i)
-            for (int c = 0; c < cnt[i] && k < S; ++c) ix[k++] = k0 + lane * kPer + i;
-        }
-
-        // 5. gather: the selected keys (key | count << 16) listed in key order
-        // in the head's uniform area (each value row is read once and weighted
-        // by its count, an exact product in fp32); the first kVU rows per
-        // lane are requested here
-        uint32_t sel = 0;
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) sel |= (cnt[i] > 0 ? 1u : 0u) << i;
-        const int nl = __popc(sel);
-        const int incl_n = wave_incl_scan_dpp(nl);
-        const int nsel = __builtin_amdgcn_readlane(incl_n, 63);
+        // 5. gather: each selected value row is read once and weighted by its
+        // count (an exact product in fp32); the first kVU rows per lane are
+        // requested here
         gt.nsel = nsel;
         if (nsel > 0) {
-          uint32_t* list = ug;
-          wave_lds_sync();  // every lane is done with the uniforms
-          // every key is written; an unselected one goes to the lane's own
-          // slot past the list (no branches, no two lanes on one address)
-          int pos = incl_n - nl;
-#pragma unroll
-          for (int i = 0; i < kPer; ++i) {
-            const bool on = cnt[i] > 0;
-            list[on ? pos : kMaxS + lane] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
-            pos += on ? 1 : 0;
-          }
           wave_lds_sync();
-          const int r = lane / LPR, c = lane % LPR;
+          const int rr = lane / LPR, c = lane % LPR;
 #pragma unroll
           for (int u = 0; u < kVU; ++u) {
-            const int i = u * RPW + r;
-            gt.ee[u] = i < nsel ? list[i] : 0u;
-            gt.vv[u] = i < nsel ? *(const uint4*)(row_of(p.V, it, wb, (int)(gt.ee[u] & 0xffffu)) + c * 8)
+            const int x = u * RPW + rr;
+            gt.ee[u] = x < nsel ? list[x] : 0u;
+            gt.vv[u] = x < nsel ? *(const uint4*)(row_of(p.V, it, wb, (int)(gt.ee[u] & 0xffffu)) + c * 8)
                                 : make_uint4(0, 0, 0, 0);
           }
         }
@@ -822,7 +866,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         const int b = it.b, hk = it.hk, k0 = it.k0;
         const uint32_t row = (uint32_t)(b * p.Hq + it.h0 + g);
         float* orow = p.out + (size_t)row * D;
-        const uint32_t* list = uni + g * kUniRow;
+        const uint32_t* list = (const uint32_t*)(score_buf(wb) + g * kPad);
         uint32_t* cw = cntw + g * (kSplit / 2);
         {
           const int r = lane / LPR, c = lane % LPR;
@@ -940,7 +984,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       publish(it, g, wt);
       if (finish_now) {
         Gather gt;
-        tail_a(it, g, scb, wb, wt, gt);
+        tail_a(it, g, scb, wb, wt, gt, false);
         tail_b(it, g, wb, gt);
       } else {
         stash_weights(g, scb, wt);
@@ -1011,7 +1055,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           Weights wt;
           Gather gt;
           reload_weights(g, score_buf(cb ^ 1), wt);
-          tail_a(prev, g, score_buf(cb ^ 1), cb ^ 1, wt, gt);
+          tail_a(prev, g, score_buf(cb ^ 1), cb ^ 1, wt, gt, true);
           tail_b(prev, g, cb ^ 1, gt);
         }
       if (!have) break;
