@@ -28,6 +28,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+SPREAD_REPLAYS = 20  # further timed replays of the step graph, for percentiles of the step time
+SETTLE_MS = 50.0     # untimed replays of the step graph before the timed one
 CSRC = os.path.join(ROOT, "stochastic_sparse_decode_amd", "csrc")
 KERNEL_SOURCES = ("santa_decode.hip", "score_stage.h", "device_common.h", "launch.h")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "santa_decode_llama8b_32k_traffic.txt")
@@ -127,14 +129,16 @@ def algorithmic_bytes(wl, S, dense=False):
     return k_bytes + wl.B * wl.Hkv * S * wl.d * 2
 
 
-def timed(fn, sets, steps, warmup, graph=True):
+def timed(fn, sets, steps, warmup, graph=True, spread=None):
     """ms per step over exactly `steps` steps, rotating over the KV copies.
 
     With graph=True the `steps` launches are captured once into a HIP graph
     and the timed region is one replay, so host-side launch overhead (Python,
     ctypes) is not part of the measurement; the events are recorded on the
     stream the kernels run on.  With graph=False every step is launched from
-    Python.
+    Python.  With a list in `spread` (graph=True), SPREAD_REPLAYS further
+    replays are timed one by one after the timed one and their ms per step
+    are left in it (for percentiles; the returned value is the timed replay's).
     """
     import torch
     for i in range(warmup):
@@ -146,12 +150,25 @@ def timed(fn, sets, steps, warmup, graph=True):
         with torch.cuda.graph(g):
             for i in range(steps):
                 fn(sets[i % len(sets)])
-        g.replay()  # untimed replay
-        torch.cuda.synchronize()
+        # untimed replays for at least SETTLE_MS of GPU work: the first
+        # milliseconds of work in a process run up to 5% slower per step
+        t0 = time.perf_counter()
+        for _ in range(200):
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= SETTLE_MS * 1e-3:
+                break
         stream = torch.cuda.current_stream()
         start.record(stream)
         g.replay()
         stop.record(stream)
+        if spread is not None:
+            for _ in range(SPREAD_REPLAYS):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                spread.append((e0, e1))
     else:
         stream = torch.cuda.current_stream()
         start.record(stream)
@@ -159,6 +176,8 @@ def timed(fn, sets, steps, warmup, graph=True):
             fn(sets[i % len(sets)])
         stop.record(stream)
     torch.cuda.synchronize()
+    if spread is not None:
+        spread[:] = [e0.elapsed_time(e1) / steps for e0, e1 in spread]
     return start.elapsed_time(stop) / steps  # ms per step (= per launch: one launch per step)
 
 
@@ -343,7 +362,8 @@ def main():
     else:
         step = lambda kv: santa.santa_decode(q, kv[0], kv[1], nk, S, mode, 1, wl.scale, out=out,  # noqa: E731
                                              workspace=ws)
-    ms = timed(step, sets, args.steps, args.warmup, graph=not args.eager)
+    spread = [] if not args.eager else None
+    ms = timed(step, sets, args.steps, args.warmup, graph=not args.eager, spread=spread)
     assert santa.santa_workspace_error(ws) == 0
     # the graph's last step must equal an eager launch on the same KV copy
     last = out.clone()
@@ -397,6 +417,10 @@ def main():
         "algorithmic_bytes_per_step": nbytes,
         "timing": "HIP graph of %d steps, one timed replay" % args.steps if not args.eager else "eager launches",
         "eager_us_per_step": eager_ms * 1000.0,
+        "replay_us_per_step": ({"replays": len(spread), "mean": float(np.mean(spread)) * 1000.0,
+                                "p10": float(np.percentile(spread, 10)) * 1000.0,
+                                "p50": float(np.percentile(spread, 50)) * 1000.0,
+                                "p90": float(np.percentile(spread, 90)) * 1000.0} if spread else None),
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic() if args.workload == "llama32k" and args.mode == "systematic"
