@@ -301,12 +301,12 @@ def model_step(args):
 
 def main():
     args = parse()
-    if args.model_step:
-        model_step(args)
-        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on a single GPU; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.model_step:
+        model_step(args)
+        return
     import numpy as np
     import torch
 
