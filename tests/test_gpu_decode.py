@@ -156,6 +156,16 @@ def test_persistent_ragged_invalid_parity(case, mode):
     check_parity(wl, 32, mode, 17, "persistent")
 
 
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_group_beyond_register_chunks_parity(mode):
+    # one KV head with 294 splits: more than the 256 whose slots are read into
+    # registers at once, so the waits and the merge also take the chunk-wise
+    # path (the pipelined variant: 294 items exceed one per CU)
+    wl = W.random_case(1, 4, 1, 64, [300123], max_n_k=300123, seed=77, planted=True)
+    assert (wl.max_n_k + 1023) // 1024 > 256
+    check_parity(wl, 128, mode, 23, "long group")
+
+
 # --------------------------------------------------------------------------
 # Llama-3.1-8B decode layer at 32k (32 q heads, 8 KV heads, d=128)
 # --------------------------------------------------------------------------
