@@ -207,6 +207,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Maximum over the lanes of this lane's row of 16 that are congruent to it
+// modulo G (G a power of two, at most 8), in every lane: rotations of the row
+// by G, 2G, .., 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float row_max_mod(float v) {
+  static_assert(G >= 1 && G <= 8 && (G & (G - 1)) == 0, "G is a power of two up to 8");
+  if constexpr (G <= 1) v = fmaxf(v, dpp_row_ror<0x121>(v));  // row_ror:1
+  if constexpr (G <= 2) v = fmaxf(v, dpp_row_ror<0x122>(v));  // row_ror:2
+  if constexpr (G <= 4) v = fmaxf(v, dpp_row_ror<0x124>(v));  // row_ror:4
+  return fmaxf(v, dpp_row_ror<0x128>(v));                     // row_ror:8
+}
+
 // Inclusive prefix sum of 32-bit integers over the wave (same DPP pattern).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ int dpp_i32(int v) {

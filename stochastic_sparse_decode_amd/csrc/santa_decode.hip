@@ -70,7 +70,7 @@ struct Lds {
 };
 
 struct Shared {
-  float wmax[2][kWaves][8];  // per score buffer: split maximum of each head, per wave
+  float wmax[2][kWaves * 4][8];  // per score buffer: split maximum of each head, per wave and row of 16 lanes
   uint32_t epoch;  // launch tag of this launch
   // Bernoulli mode
   float A[8];
@@ -465,9 +465,11 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   auto weights = [&](const ItemCtx& it, int g, const float* scb, int wb, Weights& wt) {
         const int len = it.len;
         const float* cg = scb + g * kPad;
+        // one value per wave (Bernoulli stage) or per wave and row of 16 lanes
+        constexpr int kParts = BERN ? kWaves : kWaves * 4;
         float m = sh.wmax[wb][0][g];
 #pragma unroll
-        for (int x = 1; x < kWaves; ++x) m = fmaxf(m, sh.wmax[wb][x][g]);
+        for (int x = 1; x < kParts; ++x) m = fmaxf(m, sh.wmax[wb][x][g]);
 
         uint64_t acc = 0;  // at most kPer * 2^31
         {
@@ -962,10 +964,21 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       else
         score_rowmajor<D, G, LB>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     }
+    if constexpr (BERN) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float m = wave_max(mx[g]);
-      if (lane == 0) sh.wmax[wb][w][g] = m;
+      for (int g = 0; g < G; ++g) {
+        const float m = wave_max(mx[g]);
+        if (lane == 0) sh.wmax[wb][w][g] = m;
+      }
+    } else {
+      // the row-major stages leave head (lane mod G)'s running maximum in each
+      // lane (and -inf for the other heads): one value per head and row of 16
+      // lanes, combined by the readers
+      float m = mx[0];
+#pragma unroll
+      for (int g = 1; g < G; ++g) m = fmaxf(m, mx[g]);
+      m = row_max_mod<G>(m);
+      if ((lane & 15) < G) sh.wmax[wb][w * 4 + (lane >> 4)][lane & 15] = m;
     }
     if (tid == 0 && !counted) {
       uint64_t c = lc;
