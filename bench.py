@@ -68,7 +68,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama32k",
-                    choices=["llama32k", "batched", "sweep131k", "bernoulli", "llama32k-fp8k", "batched-paged"])
+                    choices=["llama32k", "batched", "sweep131k", "sweep", "bernoulli", "llama32k-fp8k",
+                             "batched-paged"])
+    ap.add_argument("--n-k", type=int, default=131072, help="sweep workload: keys per sequence")
+    ap.add_argument("--r", type=float, default=1.0, help="sweep workload: logit standard deviation")
     ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid"])
     ap.add_argument("--S", type=int, default=128)
     ap.add_argument("--budget", type=int, default=0,
@@ -87,7 +90,7 @@ def parse():
     return ap.parse_args()
 
 
-def make_workload(name):
+def make_workload(name, n_k=131072, r=1.0):
     from stochastic_sparse_decode_amd import workloads as W
     if name == "llama32k":
         return W.llama(B=1, n_k=32768, seed=1001), "Llama-3.1-8B decode layer, B=1, 32q/8kv, d=128, n_k=32768"
@@ -103,6 +106,9 @@ def make_workload(name):
                 "Llama-3.1-8B decode layer, B=16, n_k~U[8192,32768], 32q/8kv, d=128")
     if name == "sweep131k":
         return W.sweep(B=4, n_k=131072, r=1.0, seed=1003), "context sweep B=4, n_k=131072, r=1, 32q/8kv, d=128"
+    if name == "sweep":
+        return (W.sweep(B=4, n_k=n_k, r=r, seed=1003),
+                "context sweep B=4, n_k=%d, r=%g, 32q/8kv, d=128" % (n_k, r))
     return W.bernoulli(B=8, n_k=32768, seed=1004), "Bernoulli case B=8, n_k=32768, 32q/8kv, d=128"
 
 
@@ -127,6 +133,23 @@ def algorithmic_bytes(wl, S, dense=False):
     if dense:
         return 2 * k_bytes
     return k_bytes + wl.B * wl.Hkv * S * wl.d * 2
+
+
+def value_rows(indices, Hkv, d):
+    """V-row counts of one step from its sampled indices (B, H_q, S): the S rows
+    per KV head the byte count assumes, the G*S rows if every query head read
+    its own, and the distinct (sequence, KV head, key) rows actually sampled.
+    Indices of -1 (an invalid length) are not rows."""
+    import torch
+    B, Hq, S = indices.shape
+    per_kv = indices.reshape(B, Hkv, (Hq // Hkv) * S).to(torch.int64)
+    srt = torch.sort(per_kv, dim=-1).values
+    valid = srt >= 0
+    first = torch.ones_like(valid)
+    first[..., 1:] = srt[..., 1:] != srt[..., :-1]
+    distinct = int((first & valid).sum().item())
+    return {"S_per_kv_head": B * Hkv * S, "G_S_rows": B * Hq * S, "distinct_measured": distinct,
+            "distinct_bytes": distinct * d * 2}
 
 
 def timed(fn, sets, steps, warmup, graph=True, spread=None):
@@ -324,7 +347,7 @@ def main():
         return
 
     mode = santa.MODES[args.mode]
-    wl, desc = make_workload(args.workload)
+    wl, desc = make_workload(args.workload, args.n_k, args.r)
     q = torch.from_numpy(wl.q).to(dev)
     nk = torch.from_numpy(wl.n_k.astype(np.int32)).to(dev)
     K0 = torch.from_numpy(wl.K).to(dev)
@@ -384,6 +407,14 @@ def main():
     else:
         nbytes = algorithmic_bytes(wl, S)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    vrows = None
+    if args.workload in ("llama32k", "batched", "sweep131k", "sweep"):
+        # the sampled rows of one step (untimed, same seed as the timed steps)
+        idx = torch.empty((wl.B, q.shape[1], S), dtype=torch.int32, device=dev)
+        santa.santa_decode(q, sets[0][0], sets[0][1], nk, S, mode, 1, wl.scale, out=out, indices=idx,
+                           workspace=ws)
+        torch.cuda.synchronize()
+        vrows = value_rows(idx.cpu(), wl.Hkv, wl.d)
 
     exact_ms = None
     if (args.workload in ("bernoulli", "batched-paged") or fp8k) and not args.no_dense:
@@ -426,6 +457,8 @@ def main():
                      "traffic": measured_traffic() if args.workload == "llama32k" and args.mode == "systematic"
                      and S == 128 else None},
     }
+    if vrows is not None:
+        res["value_rows"] = vrows
     if exact_ms is not None:
         key = {"llama32k-fp8k": "fp16_santa", "batched-paged": "contiguous_santa"}.get(args.workload, "exact_santa")
         res[key] = {"us_per_step": exact_ms * 1000.0,

@@ -58,3 +58,17 @@ def test_more_than_one_gpu_is_refused():
         assert r.returncode != 0
         assert "single GPU" in r.stderr
         assert r.stdout.strip() == ""
+
+
+def test_value_rows_counts_distinct_per_kv_head():
+    import torch
+    # B=1, H_q=4, H_kv=2 (G=2), S=3; heads 0,1 share KV head 0, heads 2,3 KV head 1
+    idx = torch.tensor([[[5, 5, 9], [9, 1, 1], [0, 0, 0], [-1, -1, -1]]], dtype=torch.int32)
+    r = bench.value_rows(idx, 2, 64)
+    # KV head 0: {1, 5, 9}; KV head 1: {0} (the -1 entries are no rows)
+    assert r["distinct_measured"] == 4
+    assert r["distinct_bytes"] == 4 * 64 * 2
+    assert r["S_per_kv_head"] == 2 * 3 and r["G_S_rows"] == 4 * 3
+    # the same key index in different sequences is a different row
+    two = torch.stack([idx[0], idx[0]])
+    assert bench.value_rows(two, 2, 64)["distinct_measured"] == 8
