@@ -214,22 +214,33 @@ def cpu_baseline(wl, S, mode, seconds, nbytes, bernoulli=False, fp8_cache=None, 
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        if bernoulli:
-            O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, 1, wl.scale, budget=budget)
-        elif fp8_cache is not None:
-            O.santa_decode_fp8k(wl.q, fp8_cache[0], fp8_cache[1], wl.V, wl.n_k, S, mode, n, wl.scale)
-        else:
-            O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, n, wl.scale)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    per_step = (time.perf_counter() - t0) / n
-    tbs = nbytes / per_step / 1e12
-    return {"value": tbs, "unit": "TB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full decode step(s) of the same workload, %.2f s per step" % (n, per_step)}
+
+    def run(budget_s):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            if bernoulli:
+                O.bernoulli_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, 1, wl.scale, budget=budget)
+            elif fp8_cache is not None:
+                O.santa_decode_fp8k(wl.q, fp8_cache[0], fp8_cache[1], wl.V, wl.n_k, S, mode, n, wl.scale)
+            else:
+                O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, mode, n, wl.scale)
+            n += 1
+            if time.perf_counter() - t0 >= budget_s:
+                return n, (time.perf_counter() - t0) / n
+
+    n, per_step = run(seconds)
+    res = {"value": nbytes / per_step / 1e12, "unit": "TB/s", "cores": threads, "kind": "oracle",
+           "sample": "%d full decode step(s) of the same workload, %.2f s per step" % (n, per_step)}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, per1 = run(seconds / 2)
+        res["single_thread"] = {"value": nbytes / per1 / 1e12, "unit": "TB/s", "cores": 1,
+                                "sample": "%d full decode step(s), %.2f s per step" % (n1, per1)}
+    except ImportError:  # pragma: no cover
+        pass
+    return res
 
 
 def model_step(args):
