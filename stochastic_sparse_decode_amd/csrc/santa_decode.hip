@@ -714,17 +714,37 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
         int nsel = 0;
         if (p.mode == 0) {
           // i.i.d.: the points in [Olo, Ohi) (the last split: [Olo, Z)) are
-          // searched one by one; earlier points are counted for the numbering
+          // searched; earlier points are counted for the numbering.  The
+          // in-range points are first packed to the front of the head's
+          // uniform row (in place: every pass reads its 64 entries before any
+          // lane writes, and writes only below the next pass's entries), so
+          // the wave runs one search per 64 in-range points rather than one
+          // per 64 points of the head.
           int cnt[kPer];
           int before = 0;
-          for (int k = lane; k < S; k += 64) {
-            const double tz = (double)ug[k] * 0x1.0p-24 * Z;
-            if (tz < Olo) {
-              ++before;
-              continue;
+          int nin = 0;
+          float* tin = (float*)ug;
+          for (int k0p = 0; k0p < S; k0p += 64) {
+            const int k = k0p + lane;
+            bool in = false;
+            float x = 0.f;
+            if (k < S) {
+              const double tz = (double)ug[k] * 0x1.0p-24 * Z;
+              if (tz < Olo) {
+                ++before;
+              } else if (is_last || tz < Ohi) {
+                in = true;
+                x = (float)((tz - Olo) / rs);
+              }
             }
-            if (!is_last && tz >= Ohi) continue;
-            const int j = key_of(cg, len, (float)((tz - Olo) / rs));
+            const uint64_t inm = __ballot(in);
+            wave_lds_sync();  // the pass's reads are done before its writes
+            if (in) tin[nin + __popcll(inm & ((1ull << lane) - 1ull))] = x;
+            nin += __popcll(inm);
+          }
+          wave_lds_sync();
+          for (int i = lane; i < nin; i += 64) {
+            const int j = key_of(cg, len, tin[i]);
             atomicAdd(&cw[j >> 1], 1u << ((j & 1) * 16));
           }
           wave_lds_sync();
