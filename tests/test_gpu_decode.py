@@ -310,3 +310,17 @@ def test_gpu_mean_over_seeds_matches_dense():
         z = (est.mean(axis=0) - dense) / np.sqrt(var / N)
         print("   mode %d: max |z| = %.2f" % (mode, np.abs(z).max()), flush=True)
         assert (np.abs(z) > 3).sum() <= 2 and np.abs(z).max() < 5
+
+
+def test_iid_many_points_in_one_split_parity():
+    # i.i.d. draws where the split holding a heavy key receives several waves'
+    # worth (> 128) of the head's points while the other splits keep theirs:
+    # the in-range points are packed and searched in rounds of 64
+    wl = W.random_case(1, 4, 1, 128, [4096], seed=77, planted=True)
+    wl.K[0, 0, 0] = (wl.K[0, 0, 0].astype(np.float32) * 0.7).astype(np.float16)  # sink: about a third of the mass
+    S = 512
+    for seed in range(3):
+        _, idx_o, _ = O.santa_decode(wl.q, wl.K, wl.V, wl.n_k, S, 0, seed, wl.scale, return_detail=True)
+        in_first = (idx_o[0] < 1024).sum(axis=-1)
+        assert in_first.max() > 128 and (idx_o[0] >= 1024).any(), in_first
+        check_parity(wl, S, 0, seed, "iid-heavy-split")
