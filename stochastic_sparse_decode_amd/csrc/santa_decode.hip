@@ -346,15 +346,21 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t u, int l) {
 }
 
 // Number of keys j < len with c_j <= tau (c nondecreasing): the first key
-// whose CDF value exceeds tau, clamped to len - 1.  Branch-free binary search
-// over the split's 1024 slots (ten dependent LDS reads).
+// whose CDF value exceeds tau, clamped to len - 1.  Branch-free radix-4
+// search over the split's 1024 slots: each level reads three probes together
+// and keeps the quarter they select (the probe test is true, then false, along
+// the split), so five dependent rounds of LDS reads instead of ten.  Probes
+// stay below 1023 - step.
 __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
+  static_assert(kSplit == 1024, "five radix-4 levels cover the split");
   int lo = 0;
 #pragma unroll
-  for (int step = kSplit / 2; step >= 1; step >>= 1) {
-    const int probe = lo + step - 1;
-    const float v = c[lidx(probe)];
-    lo = (probe < len && v <= tau) ? lo + step : lo;
+  for (int step = kSplit / 4; step >= 1; step >>= 2) {
+    const int p1 = lo + step - 1, p2 = lo + 2 * step - 1, p3 = lo + 3 * step - 1;
+    const float v1 = c[lidx(p1)], v2 = c[lidx(p2)], v3 = c[lidx(p3)];
+    const int adv = (p1 < len && v1 <= tau ? 1 : 0) + (p2 < len && v2 <= tau ? 1 : 0) +
+                    (p3 < len && v3 <= tau ? 1 : 0);
+    lo += adv * step;
   }
   return lo < len ? lo : len - 1;
 }
