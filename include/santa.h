@@ -115,7 +115,17 @@ typedef struct santa_problem {
   int32_t head_dim;     /* d: 64 or 128 */
   int32_t max_n_k;      /* rows reserved per (sequence, KV head) in K and V, >= 1 */
   float scale;          /* finite; score = scale * <q, k> (typically 1/sqrt(d)) */
+  uint32_t flags;       /* 0 or SANTA_DETERMINISTIC; other bits are rejected (SANTA_ERR_UNSUPPORTED) */
 } santa_problem;
+
+/* santa_problem.flags bit of the sampling entry points: `out` is computed as
+ * the exact sum of the gathered value rows (times their counts), rounded once
+ * to fp32 after the division by S, so equal inputs and seed give bit-identical
+ * outputs on every run.  Without it the splits of the key sequence add their
+ * fp32 shares atomically in the order they finish (faster: no wait for the
+ * last share), and outputs may differ between runs in the last bits.
+ * santa_dense_decode ignores the flag: it always merges in a fixed order. */
+#define SANTA_DETERMINISTIC 1u
 
 /* Largest sample count accepted by santa_decode / santa_bernoulli_qk. */
 #define SANTA_MAX_S 1024
@@ -211,6 +221,17 @@ int santa_bernoulli_qk_budget(const santa_problem* problem, const void* q, const
  * max_n_k must be a multiple of 64; K and K_fm must not overlap. */
 int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void* K_fm, void* stream);
 
+/* Measurement utility (not part of the decode step): read `bytes` bytes of the
+ * device buffer `buf` once with the 16-byte non-temporal loads the decode
+ * kernels stream K with, using workgroups_per_cu (1..8) workgroups of 256
+ * threads per compute unit, each reading one contiguous range.  Nothing is
+ * written except, practically never, one word of `sink` (device memory, 4
+ * bytes): the loaded words are folded into a value that is stored only if it
+ * equals a fixed constant, so the loads cannot be optimised away.  It gives
+ * the bandwidth a bare read of the decode step's bytes reaches in one launch.
+ * bytes must be a multiple of 16 and buf 16-byte aligned. */
+int santa_stream_read(const void* buf, size_t bytes, int32_t workgroups_per_cu, uint32_t* sink, void* stream);
+
 /* Copy the device error bits of a workspace to *flags (synchronises `stream`).
  * Bit 0: a bounded cross-workgroup wait timed out (results invalid).
  * Bit 1: a block-table entry of santa_decode_paged was out of range. */
@@ -220,7 +241,7 @@ int santa_workspace_error(const void* workspace, uint32_t* flags, void* stream);
 const char* santa_status_string(int status);
 
 /* ABI version of this header (incremented on incompatible changes). */
-#define SANTA_ABI_VERSION 1
+#define SANTA_ABI_VERSION 2
 int32_t santa_abi_version(void);
 
 #ifdef __cplusplus

@@ -23,10 +23,12 @@ santa    scores, softmax distribution, stratum points, inverse-CDF search,
          gather-average estimate, dense attention and the Bernoulli qK^T mode.
 moments  exact first and second moments of the three estimators.
 fp8      exact decoding of the OCP E4M3 bytes of the fp8 key cache.
+parity   index-parity bookkeeping: which index differences a CDF boundary
+         within the tolerance band excuses.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
 against something other than itself (known-answer vectors, a library
 routine, closed forms, brute-force enumeration or fine-grid integration).
 """
 
-from . import fp8, philox, santa, moments  # noqa: F401
+from . import fp8, moments, parity, philox, santa  # noqa: F401

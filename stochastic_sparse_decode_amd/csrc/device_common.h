@@ -300,6 +300,10 @@ __device__ __forceinline__ void store_dev(uint64_t* p, uint64_t v) {
 __device__ __forceinline__ void atomic_add_noret(uint64_t* p, uint64_t v) {
   (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Device-scope 64-bit integer add without return (global_atomic_add_x2).
+__device__ __forceinline__ void atomic_add_dev(uint64_t* p, uint64_t v) {
+  (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Device-scope float add without return (global_atomic_add_f32).
 __device__ __forceinline__ void atomic_add_dev(float* p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -10,6 +10,7 @@ namespace santa {
 constexpr int kThreads = 256;   // threads per workgroup (4 waves)
 constexpr int kWaves = kThreads / 64;
 constexpr int kSplit = 1024;    // keys per work item (one split of one KV head)
+constexpr int kMinSplit = 512;  // shorter splits of the plain fp16 cache (small problems)
 constexpr int kMaxS = 1024;     // largest sample count
 constexpr int kTile = 64;       // keys per feature-major tile (Bernoulli mode)
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait: ~1 s, then error flag
@@ -19,13 +20,22 @@ constexpr uint64_t kLaunchUnit = 1ull << 20;  // launch counter increment per la
 constexpr uint32_t kErrSpinTimeout = 1u;
 constexpr uint32_t kErrBlockTable = 2u;  // a block-table entry out of range (read as block 0)
 
-// Device pointers carved out of the caller's workspace.
+// Device pointers carved out of the caller's workspace.  The words that must
+// be zero when a launch starts (the dense kernel's work counter and arrival
+// counters; every dense launch leaves them at zero) sit in the header and in a
+// counter region of fixed size right after it, which no other region of any
+// problem ever overlaps; statistics slots carry the launch's tag and partial
+// records are written before they are read, so a buffer can serve problems of
+// different sizes.
+constexpr int kMaxDenseGroups = 16384;  // B * H_kv of a dense step (its counters fill 64 KiB)
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dense kernel: dynamic work-item counter, returns to 0 at kernel end
   uint64_t* launches;   // launch counter of the sampling kernel: kLaunchUnit added per launch
-  uint32_t* bar_done;   // [groups] arrivals of split partial outputs (dense), back to 0 at kernel end
-  uint64_t* stats;      // [groups][ns][G][2] (tag:32 | split max bits, tag:32 | split mass bits)
+  uint32_t* arrive;     // [groups] dense kernel: splits of the group that stored their record, back to 0
+  uint64_t* stats;      // [groups][G][ns][2] (tag:32 | split max bits, tag:32 | split mass bits); sized for
+                        // splits of kMinSplit keys
+  uint64_t* acc;        // [groups][G][D] exact output sums of the deterministic mode (cleared by split 0 per launch)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
 };
 
@@ -60,7 +70,10 @@ struct DecodeParams {
   int budget;           // Bernoulli budget variant: expected kept features per head (m), else 0
   uint64_t seed;
   int D, G;
-  int occ;              // sampling kernel variant: 1 = one item per workgroup, 2 = items taken in turn
+  int occ;              // sampling kernel variant: 1 = one item per workgroup (one per CU), 2 = items taken in
+                        // turn (two workgroups per CU), 3 = one item per workgroup (two per CU)
+  int split;            // keys per work item of the sampling kernel: kSplit, or 512 (variant 3, plain fp16 cache)
+  int det;              // 1: out is the exact sum of the gathered rows rounded once (bit-reproducible)
   Workspace ws;
 };
 static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");
@@ -72,11 +85,13 @@ enum KeyKind { kKeyF16 = 0, kKeyBernoulli = 1, kKeyF8 = 2, kKeyF16Paged = 3, kKe
 constexpr int kMaxBlocksPerSplit = kSplit / 16;  // smallest block: 16 keys
 
 // Resident-workgroup capacity of the current device for a kernel variant.
-int decode_capacity(int D, int G, int key_kind, int occ);
+int decode_capacity(int D, int G, int key_kind, int variant, int split);
 int dense_capacity(int D, int G);
 
 hipError_t launch_decode(const DecodeParams& p, int key_kind, hipStream_t stream);
 hipError_t launch_dense(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups_per_cu, uint32_t* sink,
+                              hipStream_t stream);
 hipError_t launch_pack_feature_major(const void* K, void* K_fm, int B, int Hkv, int max_n_k, int D,
                                      hipStream_t stream);
 

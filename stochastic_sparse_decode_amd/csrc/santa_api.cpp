@@ -32,18 +32,25 @@ int group_size(const santa_problem* p) { return p->num_q_heads / p->num_kv_heads
 
 bool supported(const santa_problem* p) {
   const int G = group_size(p);
+  if ((p->flags & ~SANTA_DETERMINISTIC) != 0u) return false;
   return (p->head_dim == 64 || p->head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
-// Workspace layout.  The header (error bits, work counter) sits at offset 0
-// and the partial outputs follow it; the flags that must read zero at the
-// start of a launch (arrival counters, statistics slots) sit at the END of
-// the caller's buffer.  Every launch leaves its flags at zero, and because
-// flags are placed against the end and data against the start, the data of
-// a smaller problem never lands on the flag words of a larger one that uses
-// the same buffer (and the other way round).
+// Workspace layout: a 256-byte header (error bits, the dense kernel's work
+// counter, the launch counter), a 64 KiB region of the dense kernel's arrival
+// counters, then the dense kernel's partial records, the statistics slots and
+// the exact output sums of the deterministic mode.  The header's work counter
+// and the arrival counters must be zero when a launch starts (every dense
+// launch leaves them at zero; the caller zero-fills a new buffer), and no
+// region of any problem overlaps them, since the data regions start after the
+// fixed-size counter region.  Slots carry a launch tag, and partial records
+// and exact sums are written (or cleared) before they are read in every
+// launch, so problems of different sizes may share a buffer even though their
+// data regions overlap.
+constexpr size_t kCounterBytes = (size_t)santa::kMaxDenseGroups * sizeof(uint32_t);
+
 struct Layout {
-  size_t partial_bytes, flag_bytes, total;
+  size_t partial, stats, acc, total;
 };
 
 Layout layout_of(const santa_problem* p) {
@@ -51,27 +58,28 @@ Layout layout_of(const santa_problem* p) {
   const size_t groups = (size_t)p->batch * p->num_kv_heads;
   const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
-  L.partial_bytes = round_up(groups * ns * G * (D + 2) * sizeof(float));
-  L.flag_bytes = round_up(groups * sizeof(uint32_t)) + round_up(groups * ns * G * 2 * sizeof(uint64_t));
-  L.total = kAlign + L.partial_bytes + L.flag_bytes;
+  L.partial = round_up(groups * ns * G * (D + 2) * sizeof(float));
+  const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
+  L.stats = round_up(groups * ns_min * G * 2 * sizeof(uint64_t));
+  L.acc = round_up(groups * G * D * sizeof(uint64_t));
+  L.total = kAlign + kCounterBytes + L.partial + L.stats + L.acc;
   return L;
 }
 
-Workspace carve(void* base, size_t bytes, const santa_problem* p) {
+Workspace carve(void* base, const santa_problem* p) {
   unsigned char* b = (unsigned char*)base;
-  const size_t groups = (size_t)p->batch * p->num_kv_heads;
-  const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
-  const size_t G = (size_t)group_size(p);
-  unsigned char* end = b + bytes / kAlign * kAlign;
-  unsigned char* done = end - round_up(groups * sizeof(uint32_t));
-  unsigned char* stats = done - round_up(groups * ns * G * 2 * sizeof(uint64_t));
+  const Layout L = layout_of(p);
   Workspace w;
   w.err = (uint32_t*)b;
   w.work_ctr = (uint32_t*)b + 1;
   w.launches = (uint64_t*)(b + 8);
-  w.partial = (float*)(b + kAlign);
-  w.bar_done = (uint32_t*)done;
-  w.stats = (uint64_t*)stats;
+  w.arrive = (uint32_t*)(b + kAlign);
+  unsigned char* x = b + kAlign + kCounterBytes;
+  w.partial = (float*)x;
+  x += L.partial;
+  w.stats = (uint64_t*)x;
+  x += L.stats;
+  w.acc = (uint64_t*)x;
   return w;
 }
 
@@ -79,14 +87,14 @@ bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Resident-workgroup capacity per (device, kernel variant), computed once.
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 6 /*kernel*/ * 2 /*workgroups per CU*/;
+constexpr int kVariants = 2 /*D*/ * 4 /*G*/ * 6 /*kernel*/ * 4 /*variant: dense, 1, 2, 3*/ * 2 /*split*/;
 std::mutex g_cap_mutex;
 int g_cap[kMaxDevices][kVariants];
 
-int variant_index(int D, int G, int kind, int occ) {
+int variant_index(int D, int G, int kind, int occ, int split) {
   const int di = D == 128 ? 1 : 0;
   const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-  return ((kind * 2 + di) * 4 + gi) * 2 + (occ == 2 ? 1 : 0);
+  return (((kind * 2 + di) * 4 + gi) * 4 + (occ & 3)) * 2 + (split == santa::kSplit ? 0 : 1);
 }
 
 int key_kind(int op) {
@@ -104,14 +112,14 @@ struct Paging {
   int lg_block = 0, num_blocks = 0;
 };
 
-int capacity(int D, int G, int kind, int occ) {
+int capacity(int D, int G, int kind, int occ, int split = santa::kSplit) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   std::lock_guard<std::mutex> lock(g_cap_mutex);
-  int& slot = g_cap[dev][variant_index(D, G, kind, occ)];
+  int& slot = g_cap[dev][variant_index(D, G, kind, kind == santa::kOpDense ? 0 : occ, split)];
   if (slot == 0) {
     slot = kind == santa::kOpDense ? santa::dense_capacity(D, G)
-                                   : santa::decode_capacity(D, G, key_kind(kind), occ);
+                                   : santa::decode_capacity(D, G, key_kind(kind), occ, split);
   }
   return slot;
 }
@@ -145,27 +153,53 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
   d.scale = p->scale;
   d.ns = (p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   d.total_items = p->batch * p->num_kv_heads * d.ns;
-  d.ws = carve(ws, ws_bytes, p);
+  d.ws = carve(ws, p);
+  d.det = (p->flags & SANTA_DETERMINISTIC) ? 1 : 0;
   return d;
 }
 
-// grid = all items if they fit the resident capacity, else the capacity (and
-// then a group's splits must fit in it, for the cross-workgroup waits).  The
-// sampling kernel comes in two variants: one workgroup per CU and one item per
-// workgroup when every item fits (no item loop), else two workgroups per CU
-// that take items in turn (one streams while the other waits in its sampling
-// tail).
+// Launch shape.  Dense: grid = all items if they fit the resident capacity,
+// else the capacity.  Sampling kernel:
+//  - the plain fp16 cache, when splits of kSplit keys would give fewer than
+//    two per CU and splits of kMinSplit keys give at most two per CU: splits
+//    of kMinSplit keys, one per workgroup, two workgroups per CU (variant 3);
+//  - else, when every kSplit item fits one workgroup per CU: one item per
+//    workgroup (variant 1);
+//  - else two workgroups per CU take the items in turn (variant 2); a group's
+//    splits must then fit in the grid, for the cross-workgroup waits.
 int choose_grid(DecodeParams& d, int kind) {
   d.occ = 1;
+  d.split = santa::kSplit;
+  const long long groups = (long long)d.B * d.Hkv;
+  auto set_split = [&](int split) {
+    d.split = split;
+    d.ns = (d.max_n_k + split - 1) / split;
+    d.total_items = (int)(groups * d.ns);
+  };
+  set_split(santa::kSplit);
   int cap = capacity(d.D, d.G, kind, 1);
   if (cap <= 0) return SANTA_ERR_HIP;
-  if (kind != santa::kOpDense && d.total_items > cap) {
+  if (kind == santa::kOpDense) {
+    d.grid = d.total_items < cap ? d.total_items : cap;
+    return SANTA_OK;
+  }
+  if (kind == santa::kOpDecode && d.total_items < 2 * cap) {
+    const int cap3 = capacity(d.D, d.G, kind, 3, santa::kMinSplit);
+    const long long items = groups * ((d.max_n_k + santa::kMinSplit - 1) / santa::kMinSplit);
+    if (cap3 > 0 && items <= cap3) {
+      set_split(santa::kMinSplit);
+      d.occ = 3;
+      d.grid = d.total_items;
+      return SANTA_OK;
+    }
+  }
+  if (d.total_items > cap) {
     d.occ = 2;
     cap = capacity(d.D, d.G, kind, 2);
     if (cap <= 0) return SANTA_ERR_HIP;
   }
   d.grid = d.total_items < cap ? d.total_items : cap;
-  if (kind != santa::kOpDense && d.grid < d.total_items && d.ns > d.grid) return SANTA_ERR_UNSUPPORTED;
+  if (d.grid < d.total_items && d.ns > d.grid) return SANTA_ERR_UNSUPPORTED;
   return SANTA_OK;
 }
 
@@ -267,6 +301,7 @@ int santa_dense_decode(const santa_problem* problem, const void* q, const void* 
                        const int32_t* n_k, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes);
   if (st != SANTA_OK) return st;
+  if ((long long)problem->batch * problem->num_kv_heads > santa::kMaxDenseGroups) return SANTA_ERR_UNSUPPORTED;
   DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, workspace_bytes);
   st = choose_grid(d, santa::kOpDense);
   if (st != SANTA_OK) return st;
@@ -282,6 +317,14 @@ int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void
   if (!aligned(K, 16) || !aligned(K_fm, 16)) return SANTA_ERR_ALIGN;
   const hipError_t e = santa::launch_pack_feature_major(K, K_fm, problem->batch, problem->num_kv_heads,
                                                         problem->max_n_k, problem->head_dim, (hipStream_t)stream);
+  return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+}
+
+int santa_stream_read(const void* buf, size_t bytes, int32_t workgroups_per_cu, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return SANTA_ERR_NULL;
+  if (bytes % 16 != 0 || workgroups_per_cu < 1 || workgroups_per_cu > 8) return SANTA_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return SANTA_ERR_ALIGN;
+  const hipError_t e = santa::launch_stream_read(buf, bytes, workgroups_per_cu, sink, (hipStream_t)stream);
   return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
 }
 

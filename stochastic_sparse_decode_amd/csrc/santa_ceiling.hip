@@ -1,0 +1,64 @@
+// Plain streaming read of a device buffer: the bandwidth one launch draws
+// from HBM when it does nothing but read, with the 16-byte non-temporal loads
+// and the two-buffer schedule of the decode kernels' score stage.  This is a
+// measurement kernel: the decode step's effective bandwidth is compared with
+// what a bare read of the same bytes reaches in one launch.
+#include "device_common.h"
+#include "launch.h"
+
+namespace santa {
+
+namespace {
+
+constexpr int kReadLB = 8;  // 16-byte loads per lane per buffer (two buffers in flight)
+
+// Workgroup x reads the contiguous range [x per, (x+1) per) of 16-byte words;
+// the four waves interleave at 16-byte granularity (1 KiB per wave load).  The
+// words are folded into one XOR, which is stored only if it equals a fixed
+// value (practically never), so the loads cannot be dropped and nothing else
+// is written.
+__global__ __launch_bounds__(kThreads) void read_kernel(const uint4* buf, size_t n16, uint32_t* sink) {
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  constexpr size_t step = (size_t)kThreads * kReadLB;
+  uint32_t acc = 0;
+  uint4 a[kReadLB], b[kReadLB];
+  auto issue = [&](uint4 (&v)[kReadLB], size_t base) {
+#pragma unroll
+    for (int u = 0; u < kReadLB; ++u) {
+      const size_t i = base + (size_t)u * kThreads + threadIdx.x;
+      v[u] = i < hi ? load_nt(buf + i) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto fold = [&](const uint4 (&v)[kReadLB]) {
+#pragma unroll
+    for (int u = 0; u < kReadLB; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  };
+  issue(a, lo);
+  for (size_t base = lo; base < hi; base += 2 * step) {
+    issue(b, base + step);
+    fold(a);
+    issue(a, base + 2 * step);
+    fold(b);
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups_per_cu, uint32_t* sink,
+                              hipStream_t stream) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)(cus * workgroups_per_cu)), dim3(kThreads), 0, stream,
+                     (const uint4*)buf, n16, sink);
+  return hipGetLastError();
+}
+
+}  // namespace santa

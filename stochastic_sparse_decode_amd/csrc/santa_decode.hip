@@ -10,7 +10,7 @@
 // key features are read.
 //
 // Work decomposition (one GPU, gfx950):
-//   work item = (sequence b, KV head, split of kSplit keys).  Items of one KV
+//   work item = (sequence b, KV head, split of SPLIT keys).  Items of one KV
 //   head ("group") are consecutive.  A workgroup (256 threads, 4 waves) takes
 //   an item and streams that split's K rows once with 16-byte loads, scoring
 //   the G query heads of the group from one read (GQA packing); the scores
@@ -55,18 +55,26 @@ struct Flag {
 };
 
 // Dynamic LDS of one workgroup:
-//   sc  [nbuf][G][kPad]  fp32 scores; then a head's weights (the i.i.d.
+//   sc  [nbuf][G][pad]   fp32 scores; then a head's weights (the i.i.d.
 //                        scheme: its local CDF), then its list of selected
-//                        keys (kMaxS entries + one spare slot per lane)
-//   uni [G][kUniRow]     24-bit uniforms of the points (stratified, i.i.d.)
-//   cnt [G][kSplit / 2]  i.i.d. points per key, two 16-bit counters a word
-template <int D, int G, int OCC>
+//                        keys (at most SPLIT entries + one spare slot per lane)
+//   uni [G][kUniRow]     24-bit uniforms of the points (stratified, i.i.d.);
+//                        finally the sums of the gather's row slots
+//   cnt [G][SPLIT / 2]   i.i.d. points per key, two 16-bit counters a word
+template <int D, int G, int NBUF, int SPLIT>
 struct Lds {
-  static constexpr int nbuf = OCC == 1 ? 1 : 2;  // score buffers: the pipelined variant keeps two items
-  static constexpr size_t sc_bytes = sizeof(float) * G * kPad;
+  static constexpr int nbuf = NBUF;  // score buffers: the pipelined variant keeps two items
+  static constexpr size_t sc_bytes = sizeof(float) * G * pad_of<SPLIT>();
   static constexpr size_t uni_bytes = sizeof(uint32_t) * G * kUniRow;
-  static constexpr size_t cnt_bytes = sizeof(uint32_t) * G * (kSplit / 2);
+  static constexpr size_t cnt_bytes = sizeof(uint32_t) * G * (SPLIT / 2);
   static constexpr size_t bytes = nbuf * sc_bytes + uni_bytes + cnt_bytes;
+};
+
+// Launch variants of the sampling kernel.
+enum Variant {
+  kOneItem = 1,     // one work item per workgroup, one workgroup per CU
+  kPersistent = 2,  // two workgroups per CU take the valid splits in turn
+  kOneItemTwo = 3,  // one work item per workgroup, two workgroups per CU
 };
 
 struct Shared {
@@ -209,6 +217,7 @@ __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, in
   const int half = lane >> 5, t4 = (lane >> 3) & 3, ko = lane & 7;
   const int ti = w * 4 + t4;  // tile of this lane inside the split (16 tiles)
   const int tiles_per_head = p.max_n_k / kTile;
+  constexpr int kPad = pad_of<kSplit>();  // the Bernoulli stage runs splits of kSplit keys
   // tiles past the sequence end re-read its last tile (results discarded)
   const int tile = min(k0 / kTile + ti, (k0 + len - 1) / kTile);
   const _Float16* tb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * tiles_per_head + tile) * (size_t)(D * kTile);
@@ -347,15 +356,21 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t u, int l) {
 
 // Number of keys j < len with c_j <= tau (c nondecreasing): the first key
 // whose CDF value exceeds tau, clamped to len - 1.  Branch-free radix-4
-// search over the split's 1024 slots: each level reads three probes together
+// search over the split's SPLIT slots: each level reads three probes together
 // and keeps the quarter they select (the probe test is true, then false, along
-// the split), so five dependent rounds of LDS reads instead of ten.  Probes
-// stay below 1023 - step.
+// the split), so five dependent rounds of LDS reads instead of ten for 1024
+// slots; for 512 slots one binary level comes first.  Probes stay below
+// SPLIT - 1.
+template <int SPLIT>
 __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
-  static_assert(kSplit == 1024, "five radix-4 levels cover the split");
+  static_assert(SPLIT == 1024 || SPLIT == 512, "radix-4 levels (and one binary level) cover the split");
   int lo = 0;
+  if constexpr (SPLIT == 512) {
+    const int p1 = 255;
+    lo += (p1 < len && c[lidx(p1)] <= tau) ? 256 : 0;
+  }
 #pragma unroll
-  for (int step = kSplit / 4; step >= 1; step >>= 2) {
+  for (int step = (SPLIT == 512 ? 64 : SPLIT / 4); step >= 1; step >>= 2) {
     const int p1 = lo + step - 1, p2 = lo + 2 * step - 1, p3 = lo + 3 * step - 1;
     const float v1 = c[lidx(p1)], v2 = c[lidx(p2)], v3 = c[lidx(p3)];
     const int adv = (p1 < len && v1 <= tau ? 1 : 0) + (p2 < len && v2 <= tau ? 1 : 0) +
@@ -368,22 +383,30 @@ __device__ __forceinline__ int key_of(const float* c, int len, float tau) {
 // ---------------------------------------------------------------------------
 // The fused kernel.
 // ---------------------------------------------------------------------------
-// OCC = workgroups per CU the register budget is sized for.
-//  OCC = 1: every work item has its own workgroup (grid = total_items,
-//  launched only then): stream the split, publish, wait, finish; no item loop.
-//  OCC = 2: two workgroups per CU take the valid splits round-robin and
+// VAR (Variant):
+//  kOneItem, kOneItemTwo: every work item has its own workgroup (grid =
+//  total_items, launched only then; one or two workgroups per CU): stream the
+//  split, publish, wait, finish; no item loop.
+//  kPersistent: two workgroups per CU take the valid splits round-robin and
 //  pipeline them: stream item k and publish its statistics, then finish item
 //  k - 1 (whose group has normally published everything by then), so the
 //  sampling tail of one item never stalls the K stream of the next.
-template <int D, int G, int KIND, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
+// SPLIT: keys per work item, 1024, or 512 for the plain fp16 cache when the
+// problem has too few 1024-key splits to give every CU two.
+template <int D, int G, int KIND, int VAR, int SPLIT>
+__global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kernel(DecodeParams p) {
   constexpr bool BUDGET = KIND == kKeyBernoulliBudget;
   constexpr bool BERN = KIND == kKeyBernoulli || BUDGET;
   constexpr bool PAGED = KIND == kKeyF16Paged;
+  constexpr int OCC = VAR == kOneItem ? 1 : 2;  // workgroups per CU
+  constexpr bool LOOP = VAR == kPersistent;
+  constexpr int kPer = SPLIT / 64;           // keys per lane in the per-head steps
+  constexpr int kPad = pad_of<SPLIT>();
+  static_assert(SPLIT == kSplit || KIND == kKeyF16, "shorter splits are built for the plain fp16 cache only");
   extern __shared__ __align__(16) unsigned char smem[];
-  using L = Lds<D, G, OCC>;
+  using L = Lds<D, G, LOOP ? 2 : 1, SPLIT>;
   uint32_t* uni = (uint32_t*)(smem + L::nbuf * L::sc_bytes);                  // [G][kUniRow]
-  uint32_t* cntw = (uint32_t*)(smem + L::nbuf * L::sc_bytes + L::uni_bytes);  // [G][kSplit / 2]
+  uint32_t* cntw = (uint32_t*)(smem + L::nbuf * L::sc_bytes + L::uni_bytes);  // [G][SPLIT / 2]
   auto score_buf = [&](int i) -> float* { return (float*)(smem + (size_t)i * L::sc_bytes); };  // [G][kPad]
   __shared__ Shared sh;
   __shared__ uint32_t binfo[BERN ? 128 : 1];  // Bernoulli kept-feature union
@@ -391,7 +414,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   __shared__ uint4 bwt2[BUDGET ? 128 : 1];    // budget variant: exact values of clipped features
   // paged cache: the block of each block-sized key range of the item in
   // score buffer wb (validated; an out-of-range entry reads block 0)
-  __shared__ int pblk[PAGED ? 2 : 1][PAGED ? kMaxBlocksPerSplit : 1];
+  __shared__ int pblk[PAGED ? 2 : 1][PAGED ? SPLIT / 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
@@ -439,10 +462,10 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     // length does not wait for it; it is first needed after the score stage
     if (tid == 0 && !counted) lc = load_dev(p.ws.launches);
     it.valid = n >= 1 && n <= p.max_n_k;
-    it.nsg = it.valid ? (n + kSplit - 1) / kSplit : 0;
+    it.nsg = it.valid ? (n + SPLIT - 1) / SPLIT : 0;
     it.active = it.valid && it.s < it.nsg;
-    it.k0 = it.s * kSplit;
-    it.len = it.active ? min(kSplit, n - it.k0) : 0;
+    it.k0 = it.s * SPLIT;
+    it.len = it.active ? min(SPLIT, n - it.k0) : 0;
     it.is_last = it.s == it.nsg - 1;
     return it;
   };
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           float sv[kPer];
 #pragma unroll
           for (int i = 0; i < kPer; ++i) sv[i] = cg[lidx(lane * kPer + i)];
-          if (len == kSplit) {
+          if (len == SPLIT) {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
               const uint32_t q = (uint32_t)(exp_nonpos(sv[i] - m) * kFix);  // trunc(w * 2^31), exact: w <= 1
@@ -532,20 +555,24 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     wt.total = readlane_f64(incl, 63);
   };
 
+  // Statistics slots of head g of an item's group: [group][head][split][2].
+  auto slot_row = [&](const uint64_t* base, const ItemCtx& it, int g) -> const uint64_t* {
+    return base + ((size_t)it.group * G + g) * p.ns * 2;
+  };
   // Publish head g's (split max, split mass).
   auto publish = [&](const ItemCtx& it, int g, const Weights& wt) {
         const uint32_t tag = sh.epoch;
-        uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
         // Each half of the 16-byte slot carries the launch tag, so a reader
         // accepts it only when both halves were written by this launch.  Split
-        // 0 cleared the output rows before its score stage; the wait makes
-        // sure those stores have completed (they have, long ago) before any
-        // split can see its slot and add.
+        // 0 cleared the output rows (the exact rows in the deterministic mode)
+        // before its score stage; the wait makes sure those stores have
+        // completed (they have, long ago) before any split can see its slot
+        // and add.
         if (it.s == 0) wait_memory();
-        if (lane == 0) {
+        if (lane < 2) {
           const uint64_t t = (uint64_t)tag << 32;
-          store_dev(slots + (it.s * G + g) * 2, t | __float_as_uint(wt.m));
-          store_dev(slots + (it.s * G + g) * 2 + 1, t | __float_as_uint((float)wt.total));
+          uint64_t* sl = const_cast<uint64_t*>(slot_row(p.ws.stats, it, g)) + it.s * 2 + lane;
+          store_dev(sl, t | __float_as_uint(lane == 0 ? wt.m : (float)wt.total));
         }
         // this workgroup's share of the launch counter (its read has completed:
         // the value is in LDS); issued after the publish so that no wait before
@@ -561,7 +588,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   // adds the value rows into the output.
   constexpr int kVU = 4;  // value loads per lane per round of the gather
   constexpr int LPR = D / 8, RPW = 64 / LPR;
-  static_assert(RPW * D <= kSplit / 2 && D % 64 == 0, "row-slot sums fit the head's counter area");
+  static_assert(2 * RPW * D <= kUniRow && D % 64 == 0, "exact row-slot sums fit the head's uniform row");
   struct Gather {
     int nsel;
     uint32_t ee[kVU];
@@ -576,26 +603,28 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   struct Poll {
     uint64_t ra[kRegChunks], rc[kRegChunks];
   };
+  // Chunks past the group's last split are not read.
   auto poll_issue = [&](const ItemCtx& it, int g, Poll& pl) {
-    const uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
+    const uint64_t* slots = slot_row(p.ws.stats, it, g);
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c) {
+      if (c > 0 && c * 64 >= it.nsg) break;
       const int x = min(c * 64 + lane, it.nsg - 1);
-      pl.ra[c] = load_dev(slots + (x * G + g) * 2);
-      pl.rc[c] = load_dev(slots + (x * G + g) * 2 + 1);
+      pl.ra[c] = load_dev(slots + x * 2);
+      pl.rc[c] = load_dev(slots + x * 2 + 1);
     }
   };
   auto tail_a = [&](const ItemCtx& it, int g, float* scb, int wb, const Weights& wt, Gather& gt, bool stashed) {
         const int s = it.s, len = it.len, k0 = it.k0, nsg = it.nsg, b = it.b, hk = it.hk, h0 = it.h0;
         const bool is_last = it.is_last;
         const uint32_t tag = sh.epoch;
-        const uint64_t* slots = p.ws.stats + (size_t)it.group * p.ns * G * 2;  // [split][head][2]
+        const uint64_t* slots = slot_row(p.ws.stats, it, g);
         const uint32_t row = (uint32_t)(b * p.Hq + h0 + g);
         float* cg = scb + g * kPad;
         // while the other splits finish: the points' uniforms, and for i.i.d.
         // draws the fp32 local CDF to search and cleared counters
         uint32_t* ug = uni + g * kUniRow;
-        uint32_t* cw = cntw + g * (kSplit / 2);
+        uint32_t* cw = cntw + g * (SPLIT / 2);
         if (p.mode != 2) {
           const uint32_t stag = p.mode == 1 ? kTagStratified : kTagIid;
           const int nb = (S + 3) >> 2;
@@ -613,7 +642,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             cum += (double)wt.q[i];
             if (lane * kPer + i < len) cg[lidx(lane * kPer + i)] = (float)cum;  // nondecreasing
           }
-          for (int i = lane; i < kSplit / 2; i += 64) cw[i] = 0u;
+          for (int i = lane; i < SPLIT / 2; i += 64) cw[i] = 0u;
         } else if (!stashed) {
           stash_weights(g, scb, wt);  // read back by the lanes that place points
         }
@@ -628,18 +657,21 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           // are up to that bound); splits beyond it are polled and re-read a
           // chunk of 64 at a time.
           auto read_slot = [&](int x, bool& ok) -> float2 {
-            const uint64_t a = load_dev(slots + (x * G + g) * 2);
-            const uint64_t c = load_dev(slots + (x * G + g) * 2 + 1);
+            const uint64_t a = load_dev(slots + x * 2);
+            const uint64_t c = load_dev(slots + x * 2 + 1);
             ok = (uint32_t)(a >> 32) == tag && (uint32_t)(c >> 32) == tag;
             return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
           };
           float2 v[kRegChunks];
           {
             Poll pl;
+#pragma unroll
+            for (int c = 0; c < kRegChunks; ++c) v[c] = make_float2(-INFINITY, 0.f);
             auto test = [&]() -> bool {
               bool all = true;
 #pragma unroll
               for (int c = 0; c < kRegChunks; ++c) {
+                if (c > 0 && c * 64 >= nsg) break;
                 v[c] = make_float2(__uint_as_float((uint32_t)pl.ra[c]), __uint_as_float((uint32_t)pl.rc[c]));
                 const bool ok = (uint32_t)(pl.ra[c] >> 32) == tag && (uint32_t)(pl.rc[c] >> 32) == tag;
                 all = all && (ok || c * 64 + lane >= nsg);
@@ -750,7 +782,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           }
           wave_lds_sync();
           for (int i = lane; i < nin; i += 64) {
-            const int j = key_of(cg, len, tin[i]);
+            const int j = key_of<SPLIT>(cg, len, tin[i]);
             atomicAdd(&cw[j >> 1], 1u << ((j & 1) * 16));
           }
           wave_lds_sync();
@@ -784,7 +816,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < kPer; ++i) {
               const bool on = cnt[i] > 0;
-              list[on ? pos : kMaxS + lane] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
+              list[on ? pos : SPLIT + lane] = (uint32_t)(lane * kPer + i) | ((uint32_t)cnt[i] << 16);
               pos += on ? 1 : 0;
             }
           }
@@ -833,7 +865,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
                 act &= act - 1ull;  // (no effect once empty)
               }
               const int sl = r == 0 ? src[0] : r == 1 ? src[1] : r == 2 ? src[2] : src[3];
-              const bool valid = sl >= 0;
+              const bool valid = sl >= 0 && i < kPer;  // rows of 16 lanes, kPer <= 16 keys per source lane
               const int key = (valid ? sl : 0) * kPer + i;
               const uint32_t qk = list[lidx(key)];  // the key's weight
               double c = valid ? (double)qk : 0.0;
@@ -888,14 +920,107 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           }
         }
   };
+  // Deterministic mode: the split's share of head g's estimate, sum over its
+  // selected keys of count * V row, is formed exactly (fp16 values are
+  // multiples of 2^-24 below 2^16, so every product and partial sum of at most
+  // kMaxS points is a multiple of 2^-24 below 2^50: exact in fp64) and added in
+  // units of 2^-24 to the head's int64 row, together with a marker 2^52 per
+  // element, so integer sums make the total independent of the order the
+  // splits arrive in.  Every split adds (its share may be zero), and the
+  // group's last split waits until every element carries nsg markers, then
+  // writes out = total 2^-24 / S, rounded once to fp32.
+  constexpr uint64_t kMarker = 1ull << 52;
+  auto tail_exact = [&](const ItemCtx& it, int g, int wb, const Gather& gt) {
+        const int nsel = gt.nsel;
+        const uint32_t row = (uint32_t)(it.b * p.Hq + it.h0 + g);
+        float* scb = score_buf(wb);
+        const uint32_t* list = (const uint32_t*)(scb + g * kPad);
+        const int r = lane / LPR, c = lane % LPR;
+        double a8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a8[e] = 0.0;
+        auto add_rows = [&](const uint4 (&vv)[kVU], const uint32_t (&ee)[kVU]) {
+#pragma unroll
+          for (int u = 0; u < kVU; ++u) {
+            const double cf = (double)(ee[u] >> 16);
+            float f8[8];
+            unpack8(vv[u], f8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a8[e] = fma(cf, (double)f8[e], a8[e]);  // exact
+          }
+        };
+        if (nsel > 0) {
+          add_rows(gt.vv, gt.ee);
+          for (int i0 = RPW * kVU; i0 < nsel; i0 += RPW * kVU) {
+            uint4 vv[kVU];
+            uint32_t ee[kVU];
+#pragma unroll
+            for (int u = 0; u < kVU; ++u) {
+              const int i = i0 + u * RPW + r;
+              ee[u] = i < nsel ? list[i] : 0u;
+              vv[u] = i < nsel ? *(const uint4*)(row_of(p.V, it, wb, (int)(ee[u] & 0xffffu)) + c * 8)
+                               : make_uint4(0, 0, 0, 0);
+            }
+            add_rows(vv, ee);
+          }
+        }
+        // the RPW row slots are summed through LDS (the head's uniform row, free
+        // by now) so that lane l ends with features l, l + 64, ...
+        double* part = (double*)(uni + g * kUniRow);  // [RPW][D]
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[r * D + c * 8 + e] = a8[e];
+        wave_lds_sync();
+        uint64_t* arow = p.ws.acc + (size_t)row * D;
+#pragma unroll
+        for (int f = 0; f < D / 64; ++f) {
+          double v = 0.0;
+#pragma unroll
+          for (int x = 0; x < RPW; ++x) v += part[x * D + f * 64 + lane];  // exact
+          // v 2^24 is an integer below 2^50 in magnitude: adding 1.5 2^52
+          // leaves it in the low mantissa bits (two's complement offset)
+          const double y = fma(v, 16777216.0, 6755399441055744.0);
+          const int64_t units = (int64_t)(__builtin_bit_cast(uint64_t, y) - 0x4338000000000000ull);
+          atomic_add_dev(arow + f * 64 + lane, (uint64_t)units + kMarker);
+        }
+        if (!it.is_last) return;
+        // the group's last split: wait for every split's share, then round once
+        wait_memory();
+        const uint64_t want = (uint64_t)it.nsg;
+        uint64_t tot[D / 64];
+        uint32_t spins = 0;
+        while (true) {
+          bool ok = true;
+#pragma unroll
+          for (int f = 0; f < D / 64; ++f) {
+            tot[f] = load_dev(arow + f * 64 + lane);
+            ok = ok && ((tot[f] + (kMarker >> 1)) >> 52) == want;
+          }
+          if (__ballot(!ok) == 0ull) break;
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(kPollSleep);
+        }
+        float* orow = p.out + (size_t)row * D;
+#pragma unroll
+        for (int f = 0; f < D / 64; ++f) {
+          const int64_t units = (int64_t)(tot[f] - want * kMarker);
+          orow[f * 64 + lane] = (float)((double)units * 0x1.0p-24 / (double)S);
+        }
+  };
   auto tail_b = [&](const ItemCtx& it, int g, int wb, const Gather& gt) {
         const int nsel = gt.nsel;
+        if (p.det) {
+          tail_exact(it, g, wb, gt);
+          return;
+        }
         if (nsel == 0) return;
         const int b = it.b, hk = it.hk, k0 = it.k0;
         const uint32_t row = (uint32_t)(b * p.Hq + it.h0 + g);
         float* orow = p.out + (size_t)row * D;
         const uint32_t* list = (const uint32_t*)(score_buf(wb) + g * kPad);
-        uint32_t* cw = cntw + g * (kSplit / 2);
         {
           const int r = lane / LPR, c = lane % LPR;
           float a8[8];
@@ -924,10 +1049,10 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
             }
             add_rows(vv, ee);
           }
-          // sum the RPW row slots through LDS (the i.i.d. counter area of the
-          // head, free by now) so that lane l ends with features l, l + 64, ...:
-          // each atomic instruction then covers 64 consecutive floats
-          float* part = (float*)cw;  // [RPW][D]
+          // sum the RPW row slots through LDS (the head's uniform row, free by
+          // now) so that lane l ends with features l, l + 64, ...: each atomic
+          // instruction then covers 64 consecutive floats
+          float* part = (float*)(uni + g * kUniRow);  // [RPW][D]
           wave_lds_sync();
           *(float4*)(part + r * D + c * 8) = make_float4(a8[0], a8[1], a8[2], a8[3]);
           *(float4*)(part + r * D + c * 8 + 4) = make_float4(a8[4], a8[5], a8[6], a8[7]);
@@ -958,8 +1083,14 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     // covers them); every split adds into a row only after it has seen
     // split 0's statistics for that head
     if (it.s == 0)
-      for (int g = w; g < G; g += kWaves)
-        for (int i = lane; i < D; i += 64) store_dev(p.out + (size_t)(it.b * p.Hq + it.h0 + g) * D + i, 0.f);
+      for (int g = w; g < G; g += kWaves) {
+        const size_t row = (size_t)(it.b * p.Hq + it.h0 + g) * D;
+        if (p.det) {
+          for (int i = lane; i < D; i += 64) store_dev(p.ws.acc + row + i, 0ull);
+        } else {
+          for (int i = lane; i < D; i += 64) store_dev(p.out + row + i, 0.f);
+        }
+      }
 
     // ---- score stage: all keys of the split, G query heads ----------------
     float mx[G];
@@ -988,7 +1119,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       if constexpr (PAGED)
         score_rowmajor_rows<D, G, LB>(p, it.b, it.hk, it.len, scb, mx, [&](int j) { return row_of(p.K, it, wb, j); });
       else
-        score_rowmajor<D, G, LB>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+        score_rowmajor<D, G, LB, SPLIT>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     }
     if constexpr (BERN) {
 #pragma unroll
@@ -1013,7 +1144,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     }
     lds_barrier();
     if (p.scores_out) {
-      write_scores<G>(p, it.b, it.hk, it.k0, it.len, scb);
+      write_scores<G, SPLIT>(p, it.b, it.hk, it.k0, it.len, scb);
       __syncthreads();
     }
     // ---- from here on, wave g owns query head g ----------------------------
@@ -1031,11 +1162,11 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
     }
   };
 
-  if constexpr (OCC == 1) {
+  if constexpr (!LOOP) {
     start_item(describe(blockIdx.x), score_buf(0), 0, true);
   } else {
     // Only valid splits are items, numbered sequence by sequence: sequence b
-    // has H_kv * nsg_b of them (nsg_b = ceil(n_k[b] / kSplit) for a valid
+    // has H_kv * nsg_b of them (nsg_b = ceil(n_k[b] / SPLIT) for a valid
     // length, none otherwise).  Workgroup x takes items x, x + grid,
     // x + 2 grid, ... (no shared counter, no skipped splits).  The splits of
     // a group are consecutive items, so with nsg <= grid they fall in at most
@@ -1058,7 +1189,7 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
       for (int c0 = 0; c0 < p.B; c0 += 64) {
         const int bq = c0 + lane;
         const int n = c0 == 0 ? nk0 : (bq < p.B ? p.n_k[bq] : 0);
-        const int nsgq = (n >= 1 && n <= p.max_n_k) ? (n + kSplit - 1) / kSplit : 0;
+        const int nsgq = (n >= 1 && n <= p.max_n_k) ? (n + SPLIT - 1) / SPLIT : 0;
         const int cnt = nsgq * p.Hkv;
         const int incl = wave_incl_scan_dpp(cnt) + carry;
         const uint64_t hit = __ballot(incl > t);
@@ -1074,8 +1205,8 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
           it.valid = true;
           it.active = true;
           it.nsg = nsgb;
-          it.k0 = it.s * kSplit;
-          it.len = min(kSplit, nb - it.k0);
+          it.k0 = it.s * SPLIT;
+          it.len = min(SPLIT, nb - it.k0);
           it.is_last = it.s == nsgb - 1;
           return true;
         }
@@ -1108,82 +1239,103 @@ __global__ __launch_bounds__(kThreads, OCC) void decode_kernel(DecodeParams p) {
   if (tid == 0 && !counted) atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
 }
 
-template <int D, int G, int OCC>
-size_t lds_bytes() { return Lds<D, G, OCC>::bytes; }
+// The one-item variant with two workgroups per CU asks for 56 KiB of LDS so
+// that no more than two of its workgroups share a CU (three would need more
+// than the CU's 160 KiB): the grid then spreads over every CU instead of
+// stacking up to four workgroups (its register use would allow that) on some.
+constexpr size_t kTwoPerCuLds = 56 * 1024;
 
-template <int D, int G, int KIND, int OCC>
+template <int D, int G, int VAR, int SPLIT>
+size_t lds_bytes() {
+  const size_t b = Lds<D, G, VAR == kPersistent ? 2 : 1, SPLIT>::bytes;
+  return VAR == kOneItemTwo && b < kTwoPerCuLds ? kTwoPerCuLds : b;
+}
+
+template <int D, int G, int KIND, int VAR, int SPLIT>
 int capacity_t() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  auto fn = decode_kernel<D, G, KIND, OCC>;
-  const size_t lds = lds_bytes<D, G, OCC>();
+  auto fn = decode_kernel<D, G, KIND, VAR, SPLIT>;
+  const size_t lds = lds_bytes<D, G, VAR, SPLIT>();
   (void)hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess) return 0;
   return per_cu * cus;
 }
 
-template <int D, int G, int KIND, int OCC>
+template <int D, int G, int KIND, int VAR, int SPLIT>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const size_t lds = lds_bytes<D, G, OCC>();
-  hipLaunchKernelGGL((decode_kernel<D, G, KIND, OCC>), dim3(p.grid), dim3(kThreads), lds, stream, p);
+  const size_t lds = lds_bytes<D, G, VAR, SPLIT>();
+  hipLaunchKernelGGL((decode_kernel<D, G, KIND, VAR, SPLIT>), dim3(p.grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
-// (D, G, key kind) combinations that are built; the fp8 score stage needs
-// G <= D / 16
-template <int D, int G, int KIND>
-constexpr bool built() { return KIND != kKeyF8 || fp8_supported<D, G>(); }
+// (D, G, key kind, variant, split) combinations that are built: the fp8 score
+// stage needs G <= D / 16; 512-key splits exist for the plain fp16 cache with
+// one item per workgroup, two workgroups per CU.
+template <int D, int G, int KIND, int VAR, int SPLIT>
+constexpr bool built() {
+  if (KIND == kKeyF8 && !fp8_supported<D, G>()) return false;
+  if (SPLIT == 512) return KIND == kKeyF16 && VAR == kOneItemTwo;
+  return VAR != kOneItemTwo;
+}
 
-
-template <int KIND, int OCC>
+template <int KIND, int VAR, int SPLIT>
 hipError_t dispatch(const DecodeParams& p, hipStream_t stream) {
 #define SANTA_CASE(DD, GG)                                                                     \
-  if constexpr (built<DD, GG, KIND>())                                                         \
-    if (p.D == DD && p.G == GG) return launch_t<DD, GG, KIND, OCC>(p, stream);
+  if constexpr (built<DD, GG, KIND, VAR, SPLIT>())                                             \
+    if (p.D == DD && p.G == GG) return launch_t<DD, GG, KIND, VAR, SPLIT>(p, stream);
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
   return hipErrorInvalidValue;
 }
 
-template <int KIND, int OCC>
+template <int KIND, int VAR, int SPLIT>
 int capacity(int D, int G) {
 #define SANTA_CASE(DD, GG)                                                                     \
-  if constexpr (built<DD, GG, KIND>())                                                         \
-    if (D == DD && G == GG) return capacity_t<DD, GG, KIND, OCC>();
+  if constexpr (built<DD, GG, KIND, VAR, SPLIT>())                                             \
+    if (D == DD && G == GG) return capacity_t<DD, GG, KIND, VAR, SPLIT>();
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
   return 0;
 }
 
-template <int OCC>
+template <int VAR, int SPLIT>
 int capacity_kind(int D, int G, int key_kind) {
-  if (key_kind == kKeyBernoulli) return capacity<kKeyBernoulli, OCC>(D, G);
-  if (key_kind == kKeyBernoulliBudget) return capacity<kKeyBernoulliBudget, OCC>(D, G);
-  if (key_kind == kKeyF8) return capacity<kKeyF8, OCC>(D, G);
-  if (key_kind == kKeyF16Paged) return capacity<kKeyF16Paged, OCC>(D, G);
-  return capacity<kKeyF16, OCC>(D, G);
+  if (key_kind == kKeyBernoulli) return capacity<kKeyBernoulli, VAR, SPLIT>(D, G);
+  if (key_kind == kKeyBernoulliBudget) return capacity<kKeyBernoulliBudget, VAR, SPLIT>(D, G);
+  if (key_kind == kKeyF8) return capacity<kKeyF8, VAR, SPLIT>(D, G);
+  if (key_kind == kKeyF16Paged) return capacity<kKeyF16Paged, VAR, SPLIT>(D, G);
+  return capacity<kKeyF16, VAR, SPLIT>(D, G);
 }
 
-template <int OCC>
+template <int VAR, int SPLIT>
 hipError_t dispatch_kind(const DecodeParams& p, int key_kind, hipStream_t stream) {
-  if (key_kind == kKeyBernoulli) return dispatch<kKeyBernoulli, OCC>(p, stream);
-  if (key_kind == kKeyBernoulliBudget) return dispatch<kKeyBernoulliBudget, OCC>(p, stream);
-  if (key_kind == kKeyF8) return dispatch<kKeyF8, OCC>(p, stream);
-  if (key_kind == kKeyF16Paged) return dispatch<kKeyF16Paged, OCC>(p, stream);
-  return dispatch<kKeyF16, OCC>(p, stream);
+  if (key_kind == kKeyBernoulli) return dispatch<kKeyBernoulli, VAR, SPLIT>(p, stream);
+  if (key_kind == kKeyBernoulliBudget) return dispatch<kKeyBernoulliBudget, VAR, SPLIT>(p, stream);
+  if (key_kind == kKeyF8) return dispatch<kKeyF8, VAR, SPLIT>(p, stream);
+  if (key_kind == kKeyF16Paged) return dispatch<kKeyF16Paged, VAR, SPLIT>(p, stream);
+  return dispatch<kKeyF16, VAR, SPLIT>(p, stream);
 }
 
 }  // namespace
 
-int decode_capacity(int D, int G, int key_kind, int occ) {
-  return occ == 2 ? capacity_kind<2>(D, G, key_kind) : capacity_kind<1>(D, G, key_kind);
+int decode_capacity(int D, int G, int key_kind, int variant, int split) {
+  if (split == 512) return variant == kOneItemTwo ? capacity_kind<kOneItemTwo, 512>(D, G, key_kind) : 0;
+  if (variant == kPersistent) return capacity_kind<kPersistent, kSplit>(D, G, key_kind);
+  return variant == kOneItem ? capacity_kind<kOneItem, kSplit>(D, G, key_kind) : 0;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int key_kind, hipStream_t stream) {
-  return p.occ == 2 ? dispatch_kind<2>(p, key_kind, stream) : dispatch_kind<1>(p, key_kind, stream);
+  if (p.split == 512) {
+    if (p.occ == kOneItemTwo) return dispatch_kind<kOneItemTwo, 512>(p, key_kind, stream);
+    return hipErrorInvalidValue;
+  }
+  if (p.occ == kPersistent) return dispatch_kind<kPersistent, kSplit>(p, key_kind, stream);
+  if (p.occ == kOneItem) return dispatch_kind<kOneItem, kSplit>(p, key_kind, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace santa

@@ -8,8 +8,8 @@
 // sum p * v and sum p.  The last workgroup of a KV head to finish merges the
 // per-split (max, sum, vector) triples in split order:
 //   out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
-// Scheduling (persistent workgroups, atomic work counter) is the one used by
-// the SANTA kernel; there is no cross-workgroup wait in this kernel.
+// Scheduling: persistent workgroups take items from an atomic work counter;
+// there is no cross-workgroup wait in this kernel.
 #include "device_common.h"
 #include "launch.h"
 #include "score_stage.h"
@@ -17,6 +17,8 @@
 namespace santa {
 
 namespace {
+
+constexpr int kPad = pad_of<kSplit>();
 
 template <int D, int G>
 struct DenseLds {
@@ -169,7 +171,8 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
       }
       wait_memory();
       __syncthreads();
-      if (tid == 0) sh.last = atomic_add_dev(p.ws.bar_done + group, 1u) == (uint32_t)(nsg - 1);
+      // arrival counter of the group (zero at rest: the last arrival resets it)
+      if (tid == 0) sh.last = atomic_add_dev(p.ws.arrive + group, 1u) == (uint32_t)(nsg - 1);
       __syncthreads();
       if (sh.last) {
         // out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s, split order
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
           const int i = tid + o * kThreads;
           if (i < G * D) p.out[(size_t)(b * p.Hq + h0) * D + i] = num[o] / sh.den[i / D];
         }
-        if (tid == 0) store_dev(p.ws.bar_done + group, 0u);
+        if (tid == 0) store_dev(p.ws.arrive + group, 0u);
       }
     }
 

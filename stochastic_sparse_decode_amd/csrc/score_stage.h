@@ -7,12 +7,17 @@
 
 namespace santa {
 
-constexpr int kPer = kSplit / 64;                // CDF elements per lane in the scan
-constexpr int kPad = kSplit + kSplit / 16 + 16;  // padded LDS row of one head (= 16 mod 32 banks)
+// LDS row of one head's scores for a split of SPLIT keys: index lidx(j) =
+// j + j/16 spreads a lane's consecutive keys over the banks; the row also has
+// room past its keys for one spare list slot per lane (SPLIT + lane), and its
+// length is 16 mod 32 banks so that the heads' rows start on different banks.
+template <int SPLIT>
+constexpr int pad_of() { return SPLIT + 64 + 16; }
 __device__ __forceinline__ int lidx(int j) { return j + (j >> 4); }  // bank-spread index
+static_assert(pad_of<1024>() % 32 == 16 && pad_of<512>() % 32 == 16, "row length 16 mod 32 banks");
 
 // LB = wave-wide 16-byte loads per register buffer (two buffers in flight)
-template <int D, int G, int LB = 16>
+template <int D, int G, int LB = 16, int SPLIT = kSplit>
 struct Geo {
   static constexpr int LPR = D / 8;        // lanes per key row (16 B each)
   static constexpr int RPW = 64 / LPR;     // key rows per wave-wide load
@@ -21,7 +26,7 @@ struct Geo {
   static constexpr int NB = (LB / U) > 0 ? (LB / U) : 1;   // blocks per buffer
   static constexpr int ROWS_IT = NB * kWaves * BR;          // rows per workgroup iteration
   static_assert(U * G == LPR, "group size must divide the row width");
-  static_assert(kSplit % ROWS_IT == 0, "an iteration never crosses the split end");
+  static_assert(SPLIT % ROWS_IT == 0, "an iteration never crosses the split end");
 };
 
 // ---------------------------------------------------------------------------
@@ -29,10 +34,11 @@ struct Geo {
 // lanes per row, U rows per lane per block so that the U*G partial dot
 // products of a lane reduce-scatter to exactly one (row, head) score per lane.
 // ---------------------------------------------------------------------------
-template <int D, int G, int LB = 16>
+template <int D, int G, int LB = 16, int SPLIT = kSplit>
 __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int hk, int k0, int len,
                                                float* cdf, float* mx) {
-  using Gm = Geo<D, G, LB>;
+  using Gm = Geo<D, G, LB, SPLIT>;
+  constexpr int kPad = pad_of<SPLIT>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / Gm::LPR, c = lane % Gm::LPR;
   const _Float16* Kb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
@@ -44,12 +50,12 @@ __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int
   const int my_u = c / G, my_g = c % G;
   float m_run = -INFINITY;
 
-  // A split is always streamed in NIT = kSplit / ROWS_IT fully unrolled
+  // A split is always streamed in NIT = SPLIT / ROWS_IT fully unrolled
   // iterations with two register buffers: the loads of iteration i+1 are in
   // flight while iteration i is reduced.  Loads are unconditional (rows past
   // the split's end re-read its last row, an L1 hit) so that the compiler
   // counts outstanding loads exactly and never waits for the prefetch.
-  constexpr int NIT = kSplit / Gm::ROWS_IT;
+  constexpr int NIT = SPLIT / Gm::ROWS_IT;
   uint4 buf[2][Gm::NB][Gm::U];
   auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
 #pragma unroll
@@ -73,7 +79,7 @@ __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int
 #pragma unroll
         for (int g = 0; g < G; ++g) v[u * G + g] = dot8(buf[it & 1][nb][u], qv[g]);
       row_reduce_scatter<Gm::LPR>(v, lane);
-      // rows < kSplit always; rows >= len land in unused LDS slots
+      // rows < SPLIT always; rows >= len land in unused LDS slots
       const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
       const float s = v[0] * p.scale;
       cdf[my_g * kPad + lidx(row)] = s;
@@ -88,10 +94,11 @@ __device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int
 // row j (0 <= j < len) of the split.  (The contiguous stage above keeps its
 // own copy: routing it through a row-pointer functor made the compiler
 // schedule its loads worse.)
-template <int D, int G, int LB, typename RowPtr>
+template <int D, int G, int LB, typename RowPtr, int SPLIT = kSplit>
 __device__ __forceinline__ void score_rowmajor_rows(const DecodeParams& p, int b, int hk, int len, float* cdf,
                                                     float* mx, const RowPtr& row_ptr) {
-  using Gm = Geo<D, G, LB>;
+  using Gm = Geo<D, G, LB, SPLIT>;
+  constexpr int kPad = pad_of<SPLIT>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / Gm::LPR, c = lane % Gm::LPR;
   const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
@@ -102,12 +109,12 @@ __device__ __forceinline__ void score_rowmajor_rows(const DecodeParams& p, int b
   const int my_u = c / G, my_g = c % G;
   float m_run = -INFINITY;
 
-  // A split is always streamed in NIT = kSplit / ROWS_IT fully unrolled
+  // A split is always streamed in NIT = SPLIT / ROWS_IT fully unrolled
   // iterations with two register buffers: the loads of iteration i+1 are in
   // flight while iteration i is reduced.  Loads are unconditional (rows past
   // the split's end re-read its last row, an L1 hit) so that the compiler
   // counts outstanding loads exactly and never waits for the prefetch.
-  constexpr int NIT = kSplit / Gm::ROWS_IT;
+  constexpr int NIT = SPLIT / Gm::ROWS_IT;
   uint4 buf[2][Gm::NB][Gm::U];
   auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
 #pragma unroll
@@ -131,7 +138,7 @@ __device__ __forceinline__ void score_rowmajor_rows(const DecodeParams& p, int b
 #pragma unroll
         for (int g = 0; g < G; ++g) v[u * G + g] = dot8(buf[it & 1][nb][u], qv[g]);
       row_reduce_scatter<Gm::LPR>(v, lane);
-      // rows < kSplit always; rows >= len land in unused LDS slots
+      // rows < SPLIT always; rows >= len land in unused LDS slots
       const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
       const float s = v[0] * p.scale;
       cdf[my_g * kPad + lidx(row)] = s;
@@ -149,7 +156,7 @@ __device__ __forceinline__ void score_rowmajor_rows(const DecodeParams& p, int b
 // with the query's fp16 pairs (v_dot2_f32_f16, fp32 accumulate); the sum is
 // scaled by scale * k_scale[b, h_kv] once.  Same schedule as the fp16 stage.
 // ---------------------------------------------------------------------------
-template <int D, int G, int LB = 16>
+template <int D, int G, int LB = 16, int SPLIT = kSplit>
 struct GeoF8 {
   static constexpr int LPR = D / 16;       // lanes per key row (16 B each)
   static constexpr int RPW = 64 / LPR;     // key rows per wave-wide load
@@ -158,16 +165,17 @@ struct GeoF8 {
   static constexpr int NB = (LB / U) > 0 ? (LB / U) : 1;   // blocks per buffer
   static constexpr int ROWS_IT = NB * kWaves * BR;          // rows per workgroup iteration
   static_assert(U >= 1 && U * G == LPR, "group size must divide the row width");
-  static_assert(kSplit % ROWS_IT == 0, "an iteration never crosses the split end");
+  static_assert(SPLIT % ROWS_IT == 0, "an iteration never crosses the split end");
 };
 
 template <int D, int G>
 constexpr bool fp8_supported() { return G <= D / 16; }
 
-template <int D, int G, int LB = 16>
+template <int D, int G, int LB = 16, int SPLIT = kSplit>
 __device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, int hk, int k0, int len,
                                                   float* cdf, float* mx) {
-  using Gm = GeoF8<D, G, LB>;
+  using Gm = GeoF8<D, G, LB, SPLIT>;
+  constexpr int kPad = pad_of<SPLIT>();
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / Gm::LPR, c = lane % Gm::LPR;
   const uint8_t* Kb = (const uint8_t*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
@@ -182,7 +190,7 @@ __device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, 
 
   const int my_u = c / G, my_g = c % G;
   float m_run = -INFINITY;
-  constexpr int NIT = kSplit / Gm::ROWS_IT;
+  constexpr int NIT = SPLIT / Gm::ROWS_IT;
   uint4 buf[2][Gm::NB][Gm::U];
   auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
 #pragma unroll
@@ -221,7 +229,7 @@ __device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, 
         }
       }
       row_reduce_scatter<Gm::LPR>(v, lane);
-      // rows < kSplit always; rows >= len land in unused LDS slots
+      // rows < SPLIT always; rows >= len land in unused LDS slots
       const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
       const float s = v[0] * sc;
       cdf[my_g * kPad + lidx(row)] = s;
@@ -233,8 +241,9 @@ __device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, 
 }
 
 // Copy the split's scores from LDS to scores_out (debug output), coalesced.
-template <int G>
+template <int G, int SPLIT = kSplit>
 __device__ __forceinline__ void write_scores(const DecodeParams& p, int b, int hk, int k0, int len, const float* cdf) {
+  constexpr int kPad = pad_of<SPLIT>();
   if (!p.scores_out) return;
   for (int i = threadIdx.x; i < G * len; i += kThreads) {
     const int g = i / len, j = i % len;

@@ -17,6 +17,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanta.s
 IID, STRATIFIED, SYSTEMATIC = 0, 1, 2
 MODES = {"iid": IID, "stratified": STRATIFIED, "systematic": SYSTEMATIC}
 MAX_S = 1024
+DETERMINISTIC = 1  # santa_problem.flags: bit-reproducible out (exact sum, one rounding)
 ERR_SPIN_TIMEOUT = 1
 
 
@@ -34,6 +35,7 @@ class Problem(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("max_n_k", ctypes.c_int32),
         ("scale", ctypes.c_float),
+        ("flags", ctypes.c_uint32),
     ]
 
 
@@ -67,6 +69,8 @@ def library():
     lib.santa_bernoulli_qk_budget.restype = ctypes.c_int
     lib.santa_pack_k_feature_major.argtypes = [P, vp, vp, vp]
     lib.santa_pack_k_feature_major.restype = ctypes.c_int
+    lib.santa_stream_read.argtypes = [vp, sz, i32, vp, vp]
+    lib.santa_stream_read.restype = ctypes.c_int
     lib.santa_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     lib.santa_workspace_error.restype = ctypes.c_int
     lib.santa_status_string.argtypes = [ctypes.c_int]
@@ -95,16 +99,17 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def problem(q, K, scale):
+def problem(q, K, scale, deterministic=False):
     """santa_problem for q (B, H_q, d) and K (B, H_kv, max_n_k, d)."""
     B, Hq, d = q.shape
-    return Problem(B, Hq, K.shape[1], d, K.shape[2], float(scale))
+    return Problem(B, Hq, K.shape[1], d, K.shape[2], float(scale), DETERMINISTIC if deterministic else 0)
 
 
-def problem_fm(q, K_fm, scale):
+def problem_fm(q, K_fm, scale, deterministic=False):
     """santa_problem for q and a feature-major K (B, H_kv, max_n_k/64, d, 64)."""
     B, Hq, d = q.shape
-    return Problem(B, Hq, K_fm.shape[1], d, K_fm.shape[2] * K_fm.shape[4], float(scale))
+    return Problem(B, Hq, K_fm.shape[1], d, K_fm.shape[2] * K_fm.shape[4], float(scale),
+                   DETERMINISTIC if deterministic else 0)
 
 
 def workspace_bytes(prob):
@@ -122,38 +127,102 @@ def new_workspace(prob, device):
 def _expect(t, name, dtype, device, ndim=None):
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if t.device != device:
-        raise ValueError("%s must be on %s" % (name, device))
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if ndim is not None and t.dim() != ndim:
-        raise ValueError("%s must have %d dims" % (name, ndim))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+
+
+def _shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_q(q):
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a (B, H_q, d) tensor, got %s" % (tuple(q.shape) if hasattr(q, "shape") else q,))
+
+
+def _on_gpu(q):
+    if q.device.type != "cuda":
+        raise ValueError("the decode step runs on a GPU: q is on %s" % q.device)
+
+
+def _check_step(q, kv, kv_names, n_k, out, indices, scores, S, max_n_k, extra=()):
+    """Dtype, shape, contiguity and device of every tensor of a decode step,
+    against the problem that q (B, H_q, d) and the key cache define; raises
+    before the library is called (the library cannot check device buffer
+    sizes).  kv: the key and value caches, already shape-checked by the
+    caller; extra: further (tensor, name, dtype, shape) entries."""
+    if q.dim() != 3:
+        raise ValueError("q must be (B, H_q, d), got shape %s" % (tuple(q.shape),))
+    B, Hq, d = q.shape
+    dev = q.device
+    _expect(q, "q", torch.float16, dev)
+    for t, nm in zip(kv, kv_names):
+        _expect(t, nm, t.dtype, dev)
+    _expect(n_k, "n_k", torch.int32, dev, 1)
+    _shape(n_k, "n_k", (B,))
+    if out is not None:
+        _expect(out, "out", torch.float32, dev)
+        _shape(out, "out", (B, Hq, d))
+    if indices is not None:
+        _expect(indices, "indices", torch.int32, dev)
+        _shape(indices, "indices", (B, Hq, int(S)))
+    if scores is not None:
+        _expect(scores, "scores", torch.float32, dev)
+        _shape(scores, "scores", (B, Hq, max_n_k))
+    for t, nm, dt, shp in extra:
+        _expect(t, nm, dt, dev)
+        _shape(t, nm, shp)
+    _on_gpu(q)
+
+
+def _check_workspace(workspace, prob, dev):
+    need = workspace_bytes(prob)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 vector (see new_workspace)")
+    if workspace.device != dev:
+        raise ValueError("workspace must be on %s" % dev)
+    if workspace.numel() < need:
+        raise ValueError("workspace holds %d bytes, the problem needs %d" % (workspace.numel(), need))
+
+
+def _kv_pair(q, K, V, dtype_k=torch.float16, name_k="K"):
+    """K (B, H_kv, max_n_k, d) and V of the same shape, H_q a multiple of H_kv."""
+    B, Hq, d = q.shape
+    if K.dim() != 4 or K.shape[0] != B or K.shape[3] != d or Hq % max(K.shape[1], 1) != 0:
+        raise ValueError("%s must be (B=%d, H_kv, max_n_k, d=%d) with H_q=%d a multiple of H_kv, got %s"
+                         % (name_k, B, d, Hq, tuple(K.shape)))
+    if K.dtype != dtype_k:
+        raise TypeError("%s must be %s, got %s" % (name_k, dtype_k, K.dtype))
+    _expect(V, "V", torch.float16, q.device, 4)
+    _shape(V, "V", K.shape)
 
 
 def santa_decode(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, deterministic=False):
     """SANTA decode step; returns ``out`` (B, H_q, d) fp32.
 
     q (B, H_q, d), K and V (B, H_kv, max_n_k, d): contiguous fp16 on one GPU;
     n_k (B,) int32 on the same GPU.  ``indices`` (B, H_q, S) int32 and
     ``scores`` (B, H_q, max_n_k) fp32, if given, receive the sampled indices
     and the scores.  ``workspace``: from ``new_workspace`` (allocated here if
-    None).
+    None).  ``deterministic``: the SANTA_DETERMINISTIC flag (bit-reproducible
+    ``out``).
     """
+    _check_q(q)
+    _kv_pair(q, K, V)
+    _check_step(q, (K, V), ("K", "V"), n_k, out, indices, scores, S, K.shape[2])
     dev = q.device
-    for t, nm in ((q, "q"), (K, "K"), (V, "V")):
-        _expect(t, nm, torch.float16, dev)
-    _expect(n_k, "n_k", torch.int32, dev, 1)
-    prob = problem(q, K, scale)
+    prob = problem(q, K, scale, deterministic)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    _expect(out, "out", torch.float32, dev)
-    if indices is not None:
-        _expect(indices, "indices", torch.int32, dev)
-    if scores is not None:
-        _expect(scores, "scores", torch.float32, dev)
     if workspace is None:
         workspace = new_workspace(prob, dev)
+    _check_workspace(workspace, prob, dev)
     mode = MODES.get(mode, mode)
     st = library().santa_decode(ctypes.byref(prob), _ptr(q), _ptr(K), _ptr(V), _ptr(n_k), int(S), int(mode),
                                 int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
@@ -163,32 +232,25 @@ def santa_decode(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, sco
 
 
 def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
-                      workspace=None, stream=None):
+                      workspace=None, stream=None, deterministic=False):
     """SANTA decode step on an fp8 key cache; returns ``out`` (B, H_q, d) fp32.
 
     K8 (B, H_kv, max_n_k, d) uint8 holds OCP E4M3 bytes and k_scale (B, H_kv)
     fp32 their scales (K = k_scale * decoded K8); q, V, n_k and the optional
     outputs are as for ``santa_decode``.
     """
+    _check_q(q)
+    _kv_pair(q, K8, V, torch.uint8, "K8")
+    B, Hq, d = q.shape
+    _check_step(q, (K8, V), ("K8", "V"), n_k, out, indices, scores, S, K8.shape[2],
+                extra=((k_scale, "k_scale", torch.float32, K8.shape[:2]),))
     dev = q.device
-    for t, nm in ((q, "q"), (V, "V")):
-        _expect(t, nm, torch.float16, dev)
-    _expect(K8, "K8", torch.uint8, dev, 4)
-    _expect(k_scale, "k_scale", torch.float32, dev, 2)
-    _expect(n_k, "n_k", torch.int32, dev, 1)
-    if tuple(V.shape) != tuple(K8.shape) or tuple(k_scale.shape) != tuple(K8.shape[:2]):
-        raise ValueError("K8 %s, V %s and k_scale %s do not match" % (tuple(K8.shape), tuple(V.shape),
-                                                                      tuple(k_scale.shape)))
-    prob = problem(q, K8, scale)
+    prob = problem(q, K8, scale, deterministic)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    _expect(out, "out", torch.float32, dev)
-    if indices is not None:
-        _expect(indices, "indices", torch.int32, dev)
-    if scores is not None:
-        _expect(scores, "scores", torch.float32, dev)
     if workspace is None:
         workspace = new_workspace(prob, dev)
+    _check_workspace(workspace, prob, dev)
     mode = MODES.get(mode, mode)
     st = library().santa_decode_fp8k(ctypes.byref(prob), _ptr(q), _ptr(K8), _ptr(k_scale), _ptr(V), _ptr(n_k),
                                      int(S), int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
@@ -197,39 +259,42 @@ def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, out=None, in
     return out
 
 
-def problem_paged(q, K_cache, block_table, scale):
+def problem_paged(q, K_cache, block_table, scale, deterministic=False):
     """santa_problem for q and a paged cache (num_blocks, H_kv, P, d) with a
     block table (B, max_blocks): max_n_k = max_blocks * P."""
     B, Hq, d = q.shape
-    return Problem(B, Hq, K_cache.shape[1], d, block_table.shape[1] * K_cache.shape[2], float(scale))
+    return Problem(B, Hq, K_cache.shape[1], d, block_table.shape[1] * K_cache.shape[2], float(scale),
+                   DETERMINISTIC if deterministic else 0)
 
 
 def santa_decode_paged(q, K_cache, V_cache, block_table, n_k, S, mode, seed, scale, out=None, indices=None,
-                       scores=None, workspace=None, stream=None):
+                       scores=None, workspace=None, stream=None, deterministic=False):
     """SANTA decode step on a paged KV cache; returns ``out`` (B, H_q, d) fp32.
 
     K_cache, V_cache (num_blocks, H_kv, block_size, d) fp16; block_table
     (B, max_blocks) int32: key j of sequence b is row j % block_size of block
     block_table[b, j // block_size].  The rest is as for ``santa_decode``.
     """
+    _check_q(q)
+    B, Hq, d = q.shape
+    if K_cache.dim() != 4 or K_cache.shape[3] != d or Hq % max(K_cache.shape[1], 1) != 0:
+        raise ValueError("K_cache must be (num_blocks, H_kv, block_size, d=%d), got %s" % (d, tuple(K_cache.shape)))
+    if K_cache.dtype != torch.float16:
+        raise TypeError("K_cache must be torch.float16, got %s" % K_cache.dtype)
+    _expect(V_cache, "V_cache", torch.float16, q.device, 4)
+    _shape(V_cache, "V_cache", K_cache.shape)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be (B=%d, max_blocks), got %s" % (B, tuple(block_table.shape)))
+    _check_step(q, (K_cache, V_cache), ("K_cache", "V_cache"), n_k, out, indices, scores, S,
+                block_table.shape[1] * K_cache.shape[2],
+                extra=((block_table, "block_table", torch.int32, block_table.shape),))
     dev = q.device
-    for t, nm in ((q, "q"), (K_cache, "K_cache"), (V_cache, "V_cache")):
-        _expect(t, nm, torch.float16, dev)
-    _expect(block_table, "block_table", torch.int32, dev, 2)
-    _expect(n_k, "n_k", torch.int32, dev, 1)
-    if K_cache.dim() != 4 or tuple(V_cache.shape) != tuple(K_cache.shape):
-        raise ValueError("K_cache %s and V_cache %s must be (num_blocks, H_kv, block_size, d)" % (
-            tuple(K_cache.shape), tuple(V_cache.shape)))
-    prob = problem_paged(q, K_cache, block_table, scale)
+    prob = problem_paged(q, K_cache, block_table, scale, deterministic)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    _expect(out, "out", torch.float32, dev)
-    if indices is not None:
-        _expect(indices, "indices", torch.int32, dev)
-    if scores is not None:
-        _expect(scores, "scores", torch.float32, dev)
     if workspace is None:
         workspace = new_workspace(prob, dev)
+    _check_workspace(workspace, prob, dev)
     mode = MODES.get(mode, mode)
     st = library().santa_decode_paged(ctypes.byref(prob), _ptr(q), _ptr(K_cache), _ptr(V_cache), _ptr(block_table),
                                       int(K_cache.shape[2]), int(K_cache.shape[0]), _ptr(n_k), int(S), int(mode),
@@ -241,16 +306,16 @@ def santa_decode_paged(q, K_cache, V_cache, block_table, n_k, S, mode, seed, sca
 
 def santa_dense_decode(q, K, V, n_k, scale, out=None, workspace=None, stream=None):
     """Exact split-K decode attention; returns ``out`` (B, H_q, d) fp32."""
+    _check_q(q)
+    _kv_pair(q, K, V)
+    _check_step(q, (K, V), ("K", "V"), n_k, out, None, None, 1, K.shape[2])
     dev = q.device
-    for t, nm in ((q, "q"), (K, "K"), (V, "V")):
-        _expect(t, nm, torch.float16, dev)
-    _expect(n_k, "n_k", torch.int32, dev, 1)
     prob = problem(q, K, scale)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    _expect(out, "out", torch.float32, dev)
     if workspace is None:
         workspace = new_workspace(prob, dev)
+    _check_workspace(workspace, prob, dev)
     st = library().santa_dense_decode(ctypes.byref(prob), _ptr(q), _ptr(K), _ptr(V), _ptr(n_k), _ptr(out),
                                       _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "santa_dense_decode")
@@ -259,38 +324,48 @@ def santa_dense_decode(q, K, V, n_k, scale, out=None, workspace=None, stream=Non
 
 def santa_pack_k_feature_major(K, K_fm=None, stream=None):
     """Feature-major copy of K: (B, H_kv, max_n_k/64, d, 64) fp16."""
-    B, Hkv, n, d = K.shape
     _expect(K, "K", torch.float16, K.device, 4)
+    B, Hkv, n, d = K.shape
+    if K.device.type != "cuda":
+        raise ValueError("K must be on a GPU, got %s" % K.device)
+    if n % 64 != 0:
+        raise ValueError("max_n_k (%d) must be a multiple of 64 for the feature-major layout" % n)
     if K_fm is None:
         K_fm = torch.empty((B, Hkv, n // 64, d, 64), dtype=torch.float16, device=K.device)
-    prob = Problem(B, Hkv, Hkv, d, n, 1.0)
+    _expect(K_fm, "K_fm", torch.float16, K.device)
+    _shape(K_fm, "K_fm", (B, Hkv, n // 64, d, 64))
+    prob = Problem(B, Hkv, Hkv, d, n, 1.0, 0)
     st = library().santa_pack_k_feature_major(ctypes.byref(prob), _ptr(K), _ptr(K_fm), _stream(stream))
     _check(st, "santa_pack_k_feature_major")
     return K_fm
 
 
 def santa_bernoulli_qk(q, K_fm, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
-                       kept=None, workspace=None, stream=None, budget=0):
+                       kept=None, workspace=None, stream=None, budget=0, deterministic=False):
     """Bernoulli qK^T step + SANTA value stage; returns ``out`` (B, H_q, d) fp32.
 
     budget = 0: ternary queries (keep probability |q_i| / max|q|); budget = m
     in [1, d]: the budget variant (keep probability min(1, m |q_i| / ||q||_1)).
     """
+    _check_q(q)
+    B, Hq, d = q.shape
+    if (K_fm.dim() != 5 or K_fm.shape[0] != B or K_fm.shape[3] != d or K_fm.shape[4] != 64
+            or Hq % max(K_fm.shape[1], 1) != 0):
+        raise ValueError("K_fm must be (B=%d, H_kv, max_n_k/64, d=%d, 64), got %s" % (B, d, tuple(K_fm.shape)))
+    if K_fm.dtype != torch.float16:
+        raise TypeError("K_fm must be torch.float16, got %s" % K_fm.dtype)
+    max_n_k = K_fm.shape[2] * 64
+    _expect(V, "V", torch.float16, q.device, 4)
+    _shape(V, "V", (B, K_fm.shape[1], max_n_k, d))
+    extra = ((kept, "kept", torch.uint8, (B, Hq, d)),) if kept is not None else ()
+    _check_step(q, (K_fm, V), ("K_fm", "V"), n_k, out, indices, scores, S, max_n_k, extra=extra)
     dev = q.device
-    for t, nm in ((q, "q"), (K_fm, "K_fm"), (V, "V")):
-        _expect(t, nm, torch.float16, dev)
-    _expect(n_k, "n_k", torch.int32, dev, 1)
-    prob = problem_fm(q, K_fm, scale)
+    prob = problem_fm(q, K_fm, scale, deterministic)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    if indices is not None:
-        _expect(indices, "indices", torch.int32, dev)
-    if scores is not None:
-        _expect(scores, "scores", torch.float32, dev)
-    if kept is not None:
-        _expect(kept, "kept", torch.uint8, dev)
     if workspace is None:
         workspace = new_workspace(prob, dev)
+    _check_workspace(workspace, prob, dev)
     mode = MODES.get(mode, mode)
     if budget:
         st = library().santa_bernoulli_qk_budget(ctypes.byref(prob), _ptr(q), _ptr(K_fm), _ptr(V), _ptr(n_k),
@@ -305,6 +380,19 @@ def santa_bernoulli_qk(q, K_fm, V, n_k, S, mode, seed, scale, out=None, indices=
                                           _stream(stream))
         _check(st, "santa_bernoulli_qk")
     return out
+
+
+def santa_stream_read(buf, workgroups_per_cu=2, sink=None, stream=None):
+    """Read every byte of the contiguous device tensor ``buf`` once (the
+    bare-read bandwidth ceiling; writes nothing but, practically never, sink)."""
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(library().santa_stream_read(_ptr(buf), nbytes, int(workgroups_per_cu), _ptr(sink), _stream(stream)),
+           "santa_stream_read")
+    return sink
 
 
 def santa_workspace_error(workspace, stream=None):

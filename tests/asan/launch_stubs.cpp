@@ -1,0 +1,15 @@
+// Stand-ins for the kernel launchers of libsanta, for a host-only build of the
+// C-ABI layer (santa_api.cpp) under AddressSanitizer and UndefinedBehavior-
+// Sanitizer.  No device code is built: every capacity query reports no
+// resident workgroups, so a call that passes its host checks returns
+// SANTA_ERR_HIP without launching anything.
+#include "launch.h"
+
+namespace santa {
+int decode_capacity(int, int, int, int, int) { return 0; }
+int dense_capacity(int, int) { return 0; }
+hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_dense(const DecodeParams&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_pack_feature_major(const void*, void*, int, int, int, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_stream_read(const void*, size_t, int, uint32_t*, hipStream_t) { return hipErrorNoDevice; }
+}  // namespace santa

@@ -1,17 +1,16 @@
 """Comparison helpers for GPU-vs-oracle parity tests.
 
-Index parity rule: the sampled index of point k must equal the oracle's, except
-when the point lies within `band` of every CDF value separating the two
-indices (the GPU accumulates the CDF in fp32/fp64 from fp32 scores, the oracle
-in fp64 from exact inputs, so a point that close to a boundary may fall on
-either side).  Such excused flips are counted and reported.
+Index parity rule (``oracle/parity.py``): the sampled index of point k must
+equal the oracle's, except when the point lies within `band` of every CDF value
+separating the two indices (the GPU accumulates the CDF from fp32 scores, the
+oracle in fp64 from exact inputs, so a point that close to a boundary may fall
+on either side).  Such excused flips are counted and reported.
 """
-
-from dataclasses import dataclass
 
 import numpy as np
 import torch
 
+from oracle import parity as OP
 from oracle import santa as O
 
 BAND = 1e-5          # excused distance for GPU vs oracle (fp64 scores)
@@ -20,47 +19,10 @@ OUT_TOL = 2e-3       # max-abs error of the SANTA output
 DENSE_TOL = 1e-3     # max-abs error of the dense output
 
 
-@dataclass
-class IndexReport:
-    points: int = 0
-    exact: int = 0
-    excused: int = 0
-    bad: int = 0
-    heads_with_flips: int = 0
-
-    def __str__(self):
-        return ("points=%d exact=%d excused(<band)=%d bad=%d heads_with_flips=%d"
-                % (self.points, self.exact, self.excused, self.bad, self.heads_with_flips))
-
-
-def compare_indices(idx_gpu, idx_or, detail, band, flips_out=None):
-    """Compare (B, H, S) index arrays using the oracle's points and CDFs."""
-    rep = IndexReport()
-    B, H, S = idx_or.shape
-    for b in range(B):
-        for h in range(H):
-            if (b, h) not in detail["t"]:
-                continue  # invalid sequence
-            g, o = idx_gpu[b, h], idx_or[b, h]
-            rep.points += S
-            diff = np.nonzero(g != o)[0]
-            rep.exact += S - len(diff)
-            if len(diff):
-                rep.heads_with_flips += 1
-                if flips_out is not None:
-                    flips_out.add((b, h))
-            t, F = detail["t"][(b, h)], detail["F"][(b, h)]
-            for k in diff:
-                lo, hi = sorted((int(g[k]), int(o[k])))
-                if lo < 0 or hi >= len(F):
-                    rep.bad += 1
-                    continue
-                between = F[lo:hi]  # CDF values separating the two keys
-                if len(between) and np.all(np.abs(between - t[k]) < band):
-                    rep.excused += 1
-                else:
-                    rep.bad += 1
-    return rep
+IndexReport = OP.IndexReport
+compare_indices = OP.compare_indices
+compare_head = OP.compare_head
+min_boundary_distance = OP.min_boundary_distance
 
 
 def oracle_estimate_from_indices(V, idx, n_k, Hq, S):

@@ -32,14 +32,14 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert santa.santa_abi_version() == 1
+    assert santa.santa_abi_version() == 2
     for code in range(8):
         assert santa.status_string(code).startswith("SANTA_")
     assert "unknown" in santa.status_string(99)
 
 
 def _prob(**kw):
-    p = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_n_k=32768, scale=0.125)
+    p = dict(batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, max_n_k=32768, scale=0.125, flags=0)
     p.update(kw)
     return santa.Problem(**p)
 
@@ -142,3 +142,28 @@ def test_bernoulli_budget_host_checks(lib):
     assert call(0) == 2        # budget below 1
     assert call(129) == 2      # budget above d
     assert call(16, _prob(max_n_k=1000)) == 2   # feature-major tiles need max_n_k % 64 == 0
+
+
+def test_flags_and_layout_paths(lib):
+    """Unknown flag bits are rejected; problems of many shapes pass every host
+    check and reach the device query (no device here: SANTA_ERR_HIP), which
+    walks the workspace layout and launch-shape code paths on the host."""
+    import torch
+    if torch.cuda.is_available() and not os.environ.get("SANTA_ABI_SANITIZED"):
+        pytest.skip("would launch kernels on fake pointers on a GPU machine")
+    vp = ctypes.c_void_p
+    p = _prob(flags=4)
+    assert _decode(lib, p) == 3
+    for B, Hq, Hkv, d, n in ((1, 32, 8, 128, 32768), (16, 32, 8, 128, 32768), (3, 8, 4, 64, 777),
+                             (70, 1, 1, 64, 32768), (1, 4, 1, 64, 300123)):
+        for flags in (0, santa.DETERMINISTIC):
+            pr = _prob(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, max_n_k=n, flags=flags)
+            nb = santa.workspace_bytes(pr)
+            assert nb > 0 and nb % 256 == 0
+            for mode in (0, 1, 2):
+                assert _decode(lib, pr, S=64, mode=mode, ws_bytes=nb) == 6
+            assert lib.santa_dense_decode(ctypes.byref(pr), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                          vp(FAKE), nb, None) == 6
+    assert lib.santa_stream_read(None, 16, 1, vp(FAKE), None) == 1
+    assert lib.santa_stream_read(vp(FAKE), 15, 1, vp(FAKE), None) == 2
+    assert lib.santa_stream_read(vp(FAKE), 16, 9, vp(FAKE), None) == 2

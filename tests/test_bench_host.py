@@ -52,7 +52,7 @@ def test_traffic_tied_to_kernel_sources(tmp_path, monkeypatch):
 
 
 def test_more_than_one_gpu_is_refused():
-    for extra in ([], ["--model-step"]):
+    for extra in ([], ["--workload", "layers32"], ["--workload", "ceiling"]):
         r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"] + extra,
                            capture_output=True, text=True, timeout=120)
         assert r.returncode != 0

@@ -122,7 +122,19 @@ def test_paged_block_entry_out_of_range_sets_error_bit():
     bad = table.copy()
     bad[1, 3] = nb + 5
     out_g, idx_g, _ = run_paged(wl, (Kc, Vc, bad, nb), 16, 2, 4, expect_err=2)
-    out_o, idx_o = O.santa_decode_paged(wl.q, Kc, Vc, table, wl.n_k, wl.max_n_k, 16, 2, 4, wl.scale)
+    out_o, idx_o, det = O.santa_decode_paged(wl.q, Kc, Vc, table, wl.n_k, wl.max_n_k, 16, 2, 4, wl.scale,
+                                             return_detail=True)
+    flips = set()
+    rep = P.IndexReport()
     for b in (0, 2):
-        assert (idx_g[b] != idx_o[b]).mean() < 0.01
-        assert np.abs(out_g[b] - out_o[b]).max() <= 5e-2
+        rep.add(P.compare_indices(idx_g[b:b + 1], idx_o[b:b + 1],
+                                  {"t": {(0, h): det["t"][(b, h)] for h in range(wl.Hq)},
+                                   "F": {(0, h): det["F"][(b, h)] for h in range(wl.Hq)}}, P.BAND, flips))
+        est = P.oracle_estimate_from_indices(wl.V[b:b + 1], idx_g[b:b + 1], wl.n_k[b:b + 1], wl.Hq, 16)
+        assert np.abs(out_g[b] - est[0]).max() <= P.OUT_TOL
+        for h in range(wl.Hq):
+            if (0, h) not in flips:
+                assert np.abs(out_g[b, h] - out_o[b, h]).max() <= P.OUT_TOL
+        flips.clear()
+    print("   unaffected sequences: %s" % rep, flush=True)
+    assert rep.bad == 0, rep

@@ -275,6 +275,47 @@ def test_bernoulli_kept_count_expectation():
     assert abs(np.mean(counts) - pi.sum()) < 4 * sd
 
 
+def _bern_uniforms_from_core(seed, row, d):
+    """Uniform i of stream (seed, row, 'BERN') computed from the Philox core
+    itself (pinned by the generator authors' vectors): word i & 3 of the block
+    at counter (i >> 2, row, tag, 0), key (seed lo, seed hi), as (x >> 8) 2^-24."""
+    u = np.zeros(d)
+    for i in range(d):
+        words = philox.philox4x32_10(i >> 2, row, philox.TAG_BERNOULLI, 0, seed & 0xFFFFFFFF, seed >> 32)
+        u[i] = float(int(words[i & 3]) >> 8) * 2.0 ** -24
+    return u
+
+
+def test_bernoulli_queries_stream_rows_and_group_sharing():
+    """One draw of d uniforms per KV head (b, h_kv), from stream row
+    b * H_kv + h_kv, shared by the group's G query heads (a draw per query
+    head, or the row b * H_q + h, fails here)."""
+    B, Hkv, G, d = 3, 2, 4, 64
+    Hq = Hkv * G
+    rng = np.random.default_rng(23)
+    mag = np.abs(rng.standard_normal(d)).astype(np.float16)
+    signs = rng.choice([-1.0, 1.0], size=(B, Hq, d))
+    q = (mag[None, None, :] * signs).astype(np.float16)  # every head has the same |q|
+    seed = (7 << 32) | 99
+    _, kept, A = O.bernoulli_queries(q, Hkv, seed)
+    qa = np.abs(q.astype(np.float64))
+    wrong_row_differs = False
+    for b in range(B):
+        for hk in range(Hkv):
+            heads = range(hk * G, (hk + 1) * G)
+            u = _bern_uniforms_from_core(seed, b * Hkv + hk, d)
+            for h in heads:
+                # equal |q| in the group: one shared mask, the rule u A < |q| on this row
+                assert np.array_equal(kept[b, h], u * A[b, h] < qa[b, h])
+                assert np.array_equal(kept[b, h], kept[b, hk * G])
+            u_wrong = _bern_uniforms_from_core(seed, b * Hq + hk * G + 1, d)
+            wrong_row_differs |= not np.array_equal(kept[b, hk * G], u_wrong * A[b, hk * G] < qa[b, hk * G])
+    assert wrong_row_differs
+    # the same |q| in the other groups and sequences: each draws its own mask
+    masks = {kept[b, hk * G].tobytes() for b in range(B) for hk in range(Hkv)}
+    assert len(masks) == B * Hkv
+
+
 # --------------------------------------------------------------------------
 # Bernoulli budget variant: pi = min(1, m |q| / ||q||_1), kept value q / pi
 # --------------------------------------------------------------------------
