@@ -20,6 +20,12 @@ Philox4x32-10 applied to counter ``(k >> 2, row, tag, 0)`` with key
 ``(seed & 0xffffffff, seed >> 32)``.  A 32-bit word ``x`` becomes the uniform
 ``(x >> 8) * 2**-24``, an exact dyadic rational in ``[0, 1 - 2**-24]``.
 
+The Gumbel-max sampler needs one uniform per (draw, key): element ``j`` of
+draw ``k`` of stream ``(seed, row, tag)`` is output word ``j & 3`` of the
+counter ``(j >> 2, row, tag, k)`` (the fourth counter word numbers the draw),
+mapped into the open interval as ``((x >> 8) + 1/2) * 2**-24``, so that both
+logarithms of the Gumbel transform are finite.
+
 Pinned by tests/test_oracle_philox.py against the generator authors'
 published known-answer vectors (tests/golden/philox4x32_10_kat.txt).
 """
@@ -38,6 +44,7 @@ TAG_SYSTEMATIC = 0x53595354  # 'SYST'
 TAG_STRATIFIED = 0x53545254  # 'STRT'
 TAG_IID = 0x49494420  # 'IID '
 TAG_BERNOULLI = 0x4245524E  # 'BERN'
+TAG_GUMBEL = 0x47554D42  # 'GUMB'
 
 
 def philox4x32_10(c0, c1, c2, c3, k0, k1):
@@ -95,3 +102,15 @@ def words_to_uniform(words):
 def uniforms(seed, row, tag, count):
     """Uniforms 0..count-1 of stream (seed, row, tag), fp64 in [0, 1 - 2**-24]."""
     return words_to_uniform(stream_words(seed, row, tag, count))
+
+
+def draw_uniforms(seed, row, tag, draw, count):
+    """Open-interval uniforms 0..count-1 of draw ``draw`` of stream (seed, row,
+    tag): word j & 3 of counter (j >> 2, row, tag, draw), as
+    ((x >> 8) + 1/2) * 2**-24 in (0, 1), fp64 (exact)."""
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    k0, k1 = seed & MASK32, seed >> 32
+    blocks = np.arange((count + 3) // 4, dtype=np.uint64)
+    out = philox4x32_10(blocks, row, tag, draw, k0, k1)
+    words = np.stack(out, axis=-1).reshape(-1)[:count]
+    return ((words >> np.uint64(8)).astype(np.float64) + 0.5) * (2.0 ** -24)

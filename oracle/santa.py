@@ -3,17 +3,20 @@
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Source: "Stochastic Sparse Attention for Memory-Bound Inference"
-(arXiv 2605.01910), abstract.  The abstract states that
+(arXiv 2605.01910), abstract.  What the abstract fixes, in this module's
+words:
 
-* every decode step reads all n_k key and value vectors (its first sentence),
-* SANTA samples S << n_k key indices from the post-softmax distribution and
-  aggregates only those value rows (second sentence),
-* this is an unbiased estimate of the post-softmax value aggregation and
-  replaces value-stage multiply-accumulates by gather-and-add (third),
-* stratified and systematic sampling are variance-reduced variants (fourth;
-  the first arXiv version names stratified sampling only),
-* Bernoulli qK^T sampling uses stochastic ternary queries to read fewer key
-  features in the score stage (the sentence introducing it).
+* plain decoding touches every key row and every value row of the cache at
+  each step (first sentence);
+* the method draws a small number S of key positions according to the
+  softmax weights of the scores and sums only the value rows at those
+  positions (second sentence);
+* that average has the exact attention output as its expectation, and the
+  value stage reduces to fetching rows and adding them (third sentence);
+* stratified and systematic placement of the draws lower the variance
+  (fourth sentence; the first arXiv version names stratified only);
+* a randomised three-valued query lets the score stage skip key features
+  (the sentence on Bernoulli qK^T sampling).
 
 Where the abstract leaves a step open, the functions below take these
 readings: an explicit softmax scale argument; i.i.d. draws by the inverse CDF
@@ -26,7 +29,8 @@ Per-head functions take 1-D / 2-D float64 arrays and are written to be read
 against those statements; the batched drivers only loop over (b, h).
 All arithmetic is fp64 on the exactly decoded fp16 inputs.
 
-Mode numbers: 0 = i.i.d. multinomial, 1 = stratified, 2 = systematic.
+Mode numbers: 0 = i.i.d. multinomial (inverse CDF), 1 = stratified,
+2 = systematic, 3 = i.i.d. multinomial by the Gumbel-max trick.
 """
 
 import numpy as np
@@ -36,6 +40,7 @@ from . import fp8, philox
 IID = 0
 STRATIFIED = 1
 SYSTEMATIC = 2
+GUMBEL = 3
 MODES = (IID, STRATIFIED, SYSTEMATIC)
 _MODE_TAG = {
     IID: philox.TAG_IID,
@@ -110,6 +115,32 @@ def inverse_cdf(F, t):
     """
     idx = np.searchsorted(F, t, side="right")
     return np.minimum(idx, len(F) - 1)
+
+
+def gumbel_draws(s, S, seed, row):
+    """i.i.d. draws by the Gumbel-max trick (the alternative to the inverse CDF
+    named beside the budget variant): draw k selects
+    i_k = argmax_j (s_j + g_kj), g_kj = -log(-log u_kj), with u_kj the
+    open-interval uniform j of draw k of stream (seed, row, 'GUMB').  Since
+    the maximum of logits perturbed by independent standard Gumbel noise falls
+    on key j with probability softmax(s)_j, the S draws are i.i.d. from the
+    post-softmax distribution.  A tie goes to the smaller key.
+
+    Returns (idx (S,) in draw order, gap (S,)): gap_k is the difference
+    between the winning and the second largest perturbed value of draw k (inf
+    when there is one key), how close the draw came to another outcome."""
+    s = np.asarray(s, dtype=np.float64)
+    n = len(s)
+    idx = np.zeros(S, dtype=np.int64)
+    gap = np.full(S, np.inf)
+    for k in range(S):
+        u = philox.draw_uniforms(seed, row, philox.TAG_GUMBEL, k, n)
+        v = s - np.log(-np.log(u))
+        j = int(np.argmax(v))  # the first maximum: the smaller key on a tie
+        idx[k] = j
+        if n > 1:
+            gap[k] = v[j] - np.max(np.delete(v, j))
+    return idx, gap
 
 
 def gather_average(V_h, idx, S):
@@ -211,6 +242,8 @@ def santa_decode(q, K, V, n_k, S, mode, seed, scale, score_override=None,
     """
     if S < 1:
         raise ValueError("S must be >= 1")
+    if mode not in MODES + (GUMBEL,):
+        raise ValueError("unknown sampling mode %r" % (mode,))
     B, Hq, Hkv, d, max_n_k, n_k = _check_shapes(q, K, V, n_k)
     G = Hq // Hkv
     qf, Kf, Vf = _f64(q), K, V
@@ -229,13 +262,22 @@ def santa_decode(q, K, V, n_k, S, mode, seed, scale, score_override=None,
             else:
                 s = _f64(score_override[b, h, :n])
             _, _, F = distribution(s)
-            t = points(mode, S, seed, b * Hq + h)
-            idx = inverse_cdf(F, t)
+            if mode == GUMBEL:
+                idx, gap = gumbel_draws(s, S, seed, b * Hq + h)
+                order = np.argsort(idx, kind="stable")
+                idx, gap = idx[order], gap[order]
+            else:
+                t = points(mode, S, seed, b * Hq + h)
+                idx = inverse_cdf(F, t)
             out[b, h] = gather_average(Vh, idx, S)
             idx_all[b, h] = idx
             if return_detail:
-                detail["t"][(b, h)] = t
                 detail["F"][(b, h)] = F
+                if mode == GUMBEL:
+                    detail.setdefault("gap", {})[(b, h)] = gap
+                    detail.setdefault("s", {})[(b, h)] = s
+                else:
+                    detail["t"][(b, h)] = t
     if return_detail:
         return out, idx_all, detail
     return out, idx_all

@@ -90,6 +90,15 @@ int dense_capacity(int D, int G);
 
 hipError_t launch_decode(const DecodeParams& p, int key_kind, hipStream_t stream);
 hipError_t launch_dense(const DecodeParams& p, hipStream_t stream);
+}  // namespace santa
+
+struct santa_problem;
+namespace santa {
+int decode_on(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
+              int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
+              void* workspace, size_t workspace_bytes, uint32_t* err, void* stream);
+size_t sampling_workspace_bytes(const santa_problem* problem);
+
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups_per_cu, uint32_t* sink,
                               hipStream_t stream);
 hipError_t launch_pack_feature_major(const void* K, void* K_fm, int B, int Hkv, int max_n_k, int D,

@@ -38,48 +38,52 @@ bool supported(const santa_problem* p) {
 
 // Workspace layout: a 256-byte header (error bits, the dense kernel's work
 // counter, the launch counter), a 64 KiB region of the dense kernel's arrival
-// counters, then the dense kernel's partial records, the statistics slots and
-// the exact output sums of the deterministic mode.  The header's work counter
-// and the arrival counters must be zero when a launch starts (every dense
-// launch leaves them at zero; the caller zero-fills a new buffer), and no
-// region of any problem overlaps them, since the data regions start after the
-// fixed-size counter region.  Slots carry a launch tag, and partial records
-// and exact sums are written (or cleared) before they are read in every
-// launch, so problems of different sizes may share a buffer even though their
-// data regions overlap.
+// counters, then the data of the kernel that runs: the dense kernel's partial
+// records, or the sampling kernel's statistics slots and the exact output sums
+// of the deterministic mode.  The header's work counter and the arrival
+// counters must be zero when a launch starts (every dense launch leaves them at
+// zero; the caller zero-fills a new buffer), and no data region of any problem
+// overlaps them, since the data regions start after the fixed-size counter
+// region.  Slots carry a launch tag, and partial records and exact sums are
+// written (or cleared) before they are read in every launch, so calls of
+// either kind and of different sizes may share a buffer even though their data
+// regions overlap.
 constexpr size_t kCounterBytes = (size_t)santa::kMaxDenseGroups * sizeof(uint32_t);
 
 struct Layout {
-  size_t partial, stats, acc, total;
+  size_t partial, stats, acc;
+  size_t dense_total() const { return kAlign + kCounterBytes + partial; }
+  size_t sampling_total() const { return kAlign + kCounterBytes + stats + acc; }
+  size_t total() const { return dense_total() > sampling_total() ? dense_total() : sampling_total(); }
 };
 
 Layout layout_of(const santa_problem* p) {
   Layout L{};
   const size_t groups = (size_t)p->batch * p->num_kv_heads;
-  const size_t ns = ((size_t)p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
-  L.partial = round_up(groups * ns * G * (D + 2) * sizeof(float));
   const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
+  L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(float));
   L.stats = round_up(groups * ns_min * G * 2 * sizeof(uint64_t));
   L.acc = round_up(groups * G * D * sizeof(uint64_t));
-  L.total = kAlign + kCounterBytes + L.partial + L.stats + L.acc;
   return L;
 }
 
-Workspace carve(void* base, const santa_problem* p) {
+// err, if not null, takes the place of the header's error word.
+Workspace carve(void* base, const santa_problem* p, bool dense, uint32_t* err = nullptr) {
   unsigned char* b = (unsigned char*)base;
   const Layout L = layout_of(p);
-  Workspace w;
-  w.err = (uint32_t*)b;
+  Workspace w{};
+  w.err = err ? err : (uint32_t*)b;
   w.work_ctr = (uint32_t*)b + 1;
   w.launches = (uint64_t*)(b + 8);
   w.arrive = (uint32_t*)(b + kAlign);
   unsigned char* x = b + kAlign + kCounterBytes;
-  w.partial = (float*)x;
-  x += L.partial;
-  w.stats = (uint64_t*)x;
-  x += L.stats;
-  w.acc = (uint64_t*)x;
+  if (dense) {
+    w.partial = (float*)x;
+  } else {
+    w.stats = (uint64_t*)x;
+    w.acc = (uint64_t*)(x + L.stats);
+  }
   return w;
 }
 
@@ -112,6 +116,18 @@ struct Paging {
   int lg_block = 0, num_blocks = 0;
 };
 
+// Compute units of the current device (0 on failure), computed once per device.
+int g_cus[kMaxDevices];
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_cap_mutex);
+  if (g_cus[dev] == 0 &&
+      hipDeviceGetAttribute(&g_cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    g_cus[dev] = 0;
+  return g_cus[dev];
+}
+
 int capacity(int D, int G, int kind, int occ, int split = santa::kSplit) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -125,19 +141,21 @@ int capacity(int D, int G, int kind, int occ, int split = santa::kSplit) {
 }
 
 int common_checks(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
-                  const float* out, const void* ws, size_t ws_bytes) {
+                  const float* out, const void* ws, size_t ws_bytes, bool dense) {
   if (!p) return SANTA_ERR_NULL;
   if (!q || !K || !V || !n_k || !out) return SANTA_ERR_NULL;
   if (!problem_ok(p)) return SANTA_ERR_SHAPE;
   if (!supported(p)) return SANTA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 4) || !aligned(n_k, 4))
     return SANTA_ERR_ALIGN;
-  if (!ws || ws_bytes / kAlign * kAlign < layout_of(p).total || !aligned(ws, kAlign)) return SANTA_ERR_WORKSPACE;
+  const Layout L = layout_of(p);
+  const size_t need = dense ? L.dense_total() : L.sampling_total();
+  if (!ws || ws_bytes / kAlign * kAlign < need || !aligned(ws, kAlign)) return SANTA_ERR_WORKSPACE;
   return SANTA_OK;
 }
 
 DecodeParams base_params(const santa_problem* p, const void* q, const void* K, const void* V,
-                         const int32_t* n_k, float* out, void* ws, size_t ws_bytes) {
+                         const int32_t* n_k, float* out, void* ws, bool dense, uint32_t* err = nullptr) {
   DecodeParams d{};
   d.q = q;
   d.K = K;
@@ -153,16 +171,19 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
   d.scale = p->scale;
   d.ns = (p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   d.total_items = p->batch * p->num_kv_heads * d.ns;
-  d.ws = carve(ws, p);
+  d.ws = carve(ws, p, dense, err);
   d.det = (p->flags & SANTA_DETERMINISTIC) ? 1 : 0;
   return d;
 }
 
 // Launch shape.  Dense: grid = all items if they fit the resident capacity,
-// else the capacity.  Sampling kernel:
-//  - the plain fp16 cache, when splits of kSplit keys would give fewer than
-//    two per CU and splits of kMinSplit keys give at most two per CU: splits
-//    of kMinSplit keys, one per workgroup, two workgroups per CU (variant 3);
+// else the capacity (splits of kMinSplit keys for small problems).  Sampling
+// kernel:
+//  - the plain fp16 cache, when splits of kSplit keys would leave CUs idle
+//    (fewer items than CUs) and splits of kMinSplit keys fit two workgroups
+//    per CU: splits of kMinSplit keys, one per workgroup (variant 3; at the
+//    Llama layer, B=1, where kSplit items exactly fill the CUs, the shorter
+//    splits measured 19.9 us against 17.0: twice the output atomics per row);
 //  - else, when every kSplit item fits one workgroup per CU: one item per
 //    workgroup (variant 1);
 //  - else two workgroups per CU take the items in turn (variant 2); a group's
@@ -180,10 +201,16 @@ int choose_grid(DecodeParams& d, int kind) {
   int cap = capacity(d.D, d.G, kind, 1);
   if (cap <= 0) return SANTA_ERR_HIP;
   if (kind == santa::kOpDense) {
+    // splits of kMinSplit keys when kSplit items would leave CUs idle and the
+    // shorter ones fit at once (context sweep, B=4 at 4096 keys: 21.8 us
+    // against 26.7; not at the Llama layer, B=1, where kSplit items fill the
+    // CUs: 36.2 us against 31.3)
+    const long long items = groups * ((d.max_n_k + santa::kMinSplit - 1) / santa::kMinSplit);
+    if (d.total_items < cu_count() && items <= cap) set_split(santa::kMinSplit);
     d.grid = d.total_items < cap ? d.total_items : cap;
     return SANTA_OK;
   }
-  if (kind == santa::kOpDecode && d.total_items < 2 * cap) {
+  if (kind == santa::kOpDecode && d.total_items < cu_count()) {
     const int cap3 = capacity(d.D, d.G, kind, 3, santa::kMinSplit);
     const long long items = groups * ((d.max_n_k + santa::kMinSplit - 1) / santa::kMinSplit);
     if (cap3 > 0 && items <= cap3) {
@@ -206,8 +233,8 @@ int choose_grid(DecodeParams& d, int kind) {
 int sampled_step(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
                  uint8_t* kept_out, const float* k_scale, const Paging& pg, void* ws, size_t ws_bytes, void* stream,
-                 int kind, int budget = 0) {
-  int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes);
+                 int kind, int budget = 0, uint32_t* err = nullptr) {
+  int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes, false);
   if (st != SANTA_OK) return st;
   if (kind == santa::kOpDecodeF8) {
     if (!k_scale) return SANTA_ERR_NULL;
@@ -220,7 +247,7 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   const bool bern = kind == santa::kOpBernoulli || kind == santa::kOpBernoulliBudget;
   if (bern && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
   if (kind == santa::kOpBernoulliBudget && (budget < 1 || budget > p->head_dim)) return SANTA_ERR_SHAPE;
-  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, ws_bytes);
+  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, false, err);
   d.idx_out = indices_out;
   d.scores_out = scores_out;
   d.kept_out = kept_out;
@@ -240,11 +267,26 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
 
 }  // namespace
 
+namespace santa {
+// santa_decode on a workspace the library owns (the allocation-free entry
+// point): error bits go to `err` when it is not null.
+int decode_on(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
+              int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
+              void* workspace, size_t workspace_bytes, uint32_t* err, void* stream) {
+  if (err && !aligned(err, 4)) return SANTA_ERR_ALIGN;
+  return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, nullptr,
+                      Paging{}, workspace, workspace_bytes, stream, kOpDecode, 0, err);
+}
+size_t sampling_workspace_bytes(const santa_problem* problem) {
+  return problem_ok(problem) ? layout_of(problem).sampling_total() : 0;
+}
+}  // namespace santa
+
 extern "C" {
 
 size_t santa_workspace_bytes(const santa_problem* problem) {
   if (!problem_ok(problem)) return 0;
-  return layout_of(problem).total;
+  return layout_of(problem).total();
 }
 
 int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
@@ -299,10 +341,10 @@ int santa_bernoulli_qk_budget(const santa_problem* problem, const void* q, const
 
 int santa_dense_decode(const santa_problem* problem, const void* q, const void* K, const void* V,
                        const int32_t* n_k, float* out, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes);
+  int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes, true);
   if (st != SANTA_OK) return st;
   if ((long long)problem->batch * problem->num_kv_heads > santa::kMaxDenseGroups) return SANTA_ERR_UNSUPPORTED;
-  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, workspace_bytes);
+  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, true);
   st = choose_grid(d, santa::kOpDense);
   if (st != SANTA_OK) return st;
   const hipError_t e = santa::launch_dense(d, (hipStream_t)stream);

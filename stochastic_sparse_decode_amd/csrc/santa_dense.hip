@@ -2,14 +2,16 @@
 //
 // Computes softmax(scale * q K^T) V for every query head, reading all of K and
 // all of V, in the split-K style of FlashDecoding: each work item (sequence,
-// KV head, split of kSplit keys) scores its keys for the G packed query heads
-// (same score stage as the SANTA kernel), keeps the scores in LDS, forms
-// p = exp(s - local max) and streams the split's V rows once, accumulating
-// sum p * v and sum p.  The last workgroup of a KV head to finish merges the
+// KV head, split of kSplit or kMinSplit keys) streams the split's K and V rows together in
+// one pass, scoring its keys for the G packed query heads (the SANTA kernel's
+// reduce-scatter) and keeping a running maximum, sum p and sum p * v per head
+// (online softmax); the last workgroup of a KV head to finish merges the
 // per-split (max, sum, vector) triples in split order:
 //   out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
 // Scheduling: persistent workgroups take items from an atomic work counter;
 // there is no cross-workgroup wait in this kernel.
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 #include "score_stage.h"
@@ -18,13 +20,9 @@ namespace santa {
 
 namespace {
 
-constexpr int kPad = pad_of<kSplit>();
-
 template <int D, int G>
 struct DenseLds {
-  static constexpr size_t p_bytes = sizeof(float) * G * kPad;
-  static constexpr size_t red_bytes = sizeof(float) * kWaves * G * D;
-  static constexpr size_t bytes = p_bytes + red_bytes;
+  static constexpr size_t bytes = sizeof(float) * kWaves * G * D;  // the waves' accumulators; the merge's scales
 };
 
 struct DenseShared {
@@ -38,11 +36,205 @@ struct DenseShared {
 
 
 
+// Compile-time loop: f(std::integral_constant<int, j>) for j = 0 .. N-1.
+template <typename F, int... J>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Lane j of this lane's row of LPR lanes (LPR = 16: a DPP row; LPR = 8: half
+// of one), by DPP row broadcasts.
+template <int LPR, int J>
+__device__ __forceinline__ float row_lane(float v, int lane) {
+  const int x = __builtin_bit_cast(int, v);
+  if constexpr (LPR == 16) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x150 + J, 0xF, 0xF, false));
+  } else {
+    static_assert(LPR == 8, "row width");
+    const int lo = __builtin_amdgcn_update_dpp(0, x, 0x150 + J, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, x, 0x150 + 8 + J, 0xF, 0xF, false);
+    return __builtin_bit_cast(float, (lane & 8) ? hi : lo);
+  }
+}
+
+// Sum over the lanes of this lane's DPP row of 16 that are congruent to it
+// modulo G (G a power of two, at most 8), in every lane.
+template <int G>
+__device__ __forceinline__ float row_sum_mod(float v) {
+  if constexpr (G <= 1) v += dpp_row_ror<0x121>(v);
+  if constexpr (G <= 2) v += dpp_row_ror<0x122>(v);
+  if constexpr (G <= 4) v += dpp_row_ror<0x124>(v);
+  return v + dpp_row_ror<0x128>(v);
+}
+
+// One pass over a split of `len` keys of KV head (b, hk): every wave takes
+// blocks of BR consecutive rows (the waves interleave block by block),
+// streams their K and V rows together with 16-byte loads (two register
+// buffers of NB blocks in flight), scores the G query heads of the group (the
+// SANTA score stage's reduce-scatter leaves one (row, head) score per lane),
+// keeps a running maximum and sum per head (online softmax) and adds
+// exp(s - m) * v into per-head accumulators.  The four waves' states are
+// combined through LDS into the split's record (acc[D], m, l per head).
+template <int D, int G>
+__device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk, int k0, int len, float* red,
+                                           DenseShared& sh, float* rec) {
+  using Gm = Geo<D, G>;
+  constexpr int LPR = Gm::LPR, RPW = Gm::RPW, U = Gm::U, BR = Gm::BR;
+  constexpr int NB = 2;                        // blocks per register buffer
+  constexpr int STEP = NB * kWaves * BR;       // rows per iteration of the workgroup
+  constexpr int PD = D + 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane / LPR, c = lane % LPR;
+  const int my_u = c / G, my_g = c % G;       // this lane's score: row my_u * RPW + r of a block, head my_g
+  const size_t base_row = (size_t)(b * p.Hkv + hk) * p.max_n_k + k0;
+  const _Float16* Kb = (const _Float16*)p.K + base_row * D;
+  const _Float16* Vb = (const _Float16*)p.V + base_row * D;
+  const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
+  uint4 qv[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qb + g * D + c * 8);
+
+  float m[G], acc[G][8];
+  float l = 0.f;  // sum of this lane's weights (head my_g)
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  }
+  struct Buf {
+    uint4 k[NB][U], v[NB][U];
+  };
+  // rows past the split's end re-read its last row and score -inf (weight 0),
+  // so the loads are unconditional and the compiler counts them exactly
+  auto issue = [&](Buf& bf, int base) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int row = min(base + (nb * kWaves + w) * BR + u * RPW + r, len - 1);
+        bf.k[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 8));
+        bf.v[nb][u] = load_nt((const uint4*)(Vb + (size_t)row * D + c * 8));
+      }
+  };
+  auto consume = [&](const Buf& bf, int base) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float sv[LPR];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sv[u * G + g] = dot8(bf.k[nb][u], qv[g]);
+      row_reduce_scatter<LPR>(sv, lane);
+      const int row = base + (nb * kWaves + w) * BR + my_u * RPW + r;
+      const float sc = row < len ? sv[0] * p.scale : -INFINITY;
+      // block maximum of each head (lanes congruent modulo G hold one head)
+      float bm = row_max_mod<G>(sc);
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      float alpha[G], mine_m = 0.f, mine_a = 1.f;
+      bool rescale = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float bmg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm), g));
+        const float mn = fmaxf(m[g], bmg);
+        alpha[g] = mn == -INFINITY ? 1.f : __expf(m[g] - mn);
+        rescale = rescale || mn != m[g];
+        m[g] = mn;
+        mine_m = my_g == g ? mn : mine_m;
+        mine_a = my_g == g ? alpha[g] : mine_a;
+      }
+      const float pw = sc == -INFINITY ? 0.f : __expf(sc - mine_m);
+      l = fmaf(l, mine_a, pw);
+      if (rescale) {  // wave-uniform
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] *= alpha[g];
+      }
+      // the V rows of the block: this lane holds features c*8.. of rows
+      // u * RPW + r; the weight of (row u * RPW + r, head g) sits in lane
+      // j = u * G + g of this lane's row (U * G = LPR such lanes)
+      float f[U][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) unpack8(bf.v[nb][u], f[u]);
+      static_for<LPR>([&](auto jc) {
+        constexpr int J = decltype(jc)::value, u = J / G, g = J % G;
+        const float wt = row_lane<LPR, J>(pw, lane);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(wt, f[u][e], acc[g][e]);
+      });
+    }
+  };
+  Buf b0, b1;
+  issue(b0, 0);
+  for (int base = 0; base < len; base += 2 * STEP) {
+    issue(b1, base + STEP);
+    consume(b0, base);
+    issue(b0, base + 2 * STEP);
+    consume(b1, base + STEP);
+  }
+
+  // combine: the RPW key-row groups of a wave (lanes with the same c), the
+  // lanes of each head for l, then the four waves through LDS
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      for (int x = LPR; x < 64; x <<= 1) acc[g][e] += __shfl_xor(acc[g][e], x, 64);
+  float lw = row_sum_mod<G>(l);
+  lw += __shfl_xor(lw, 16, 64);
+  lw += __shfl_xor(lw, 32, 64);
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[(w * G + g) * D + c * 8 + e] = acc[g][e];
+  }
+  if (lane < G) {
+    sh.wmax[w][lane] = m[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g)
+      if (lane == g) sh.wmax[w][lane] = m[g];
+    sh.wsum[w][lane] = lw;  // lane g holds head g (lanes congruent to g modulo G)
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int g = i / D, d = i % D;
+    float M = sh.wmax[0][g];
+#pragma unroll
+    for (int x = 1; x < kWaves; ++x) M = fmaxf(M, sh.wmax[x][g]);
+    float v = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+      const float mx = sh.wmax[x][g];
+      v += mx == -INFINITY ? 0.f : red[(x * G + g) * D + d] * __expf(mx - M);
+    }
+    store_dev(rec + g * PD + d, v);
+  }
+  if (tid < G) {
+    float M = sh.wmax[0][tid];
+#pragma unroll
+    for (int x = 1; x < kWaves; ++x) M = fmaxf(M, sh.wmax[x][tid]);
+    float lt = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+      const float mx = sh.wmax[x][tid];
+      lt += mx == -INFINITY ? 0.f : sh.wsum[x][tid] * __expf(mx - M);
+    }
+    store_dev(rec + tid * PD + D, M);
+    store_dev(rec + tid * PD + D + 1, lt);
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* P = (float*)smem;                                  // [G][kPad] scores, then weights
-  float* red = (float*)(smem + DenseLds<D, G>::p_bytes);    // [kWaves][G*D]
+  float* red = (float*)smem;  // [kWaves][G][D] the waves' accumulators, then the merge's per-split scales
   __shared__ DenseShared sh;
   constexpr int LPR = D / 8, RPW = 64 / LPR, UV = 8;
   constexpr int PD = D + 2;  // partial record: acc[D], m, l
@@ -55,120 +247,15 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
     const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
     const int n = p.n_k[b];
     const bool valid = n >= 1 && n <= p.max_n_k;
-    const int nsg = valid ? (n + kSplit - 1) / kSplit : 0;
+    const int nsg = valid ? (n + p.split - 1) / p.split : 0;
 
     if (!valid) {
       if (s == 0)
         for (int i = tid; i < G * D; i += kThreads) p.out[(size_t)(b * p.Hq + h0) * D + i] = __builtin_nanf("");
     } else if (s < nsg) {
-      const int k0 = s * kSplit;
-      const int len = min(kSplit, n - k0);
-      float mx[G];
-      score_rowmajor<D, G>(p, b, hk, k0, len, P, mx);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float m = wave_max_masked(mx[g], 1);
-        if (lane == 0) sh.wmax[w][g] = m;
-      }
-      __syncthreads();
-      // weights p_j = exp(s_j - m) in place, and their sum per head
-      float m_h[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        m_h[g] = sh.wmax[0][g];
-#pragma unroll
-        for (int x = 1; x < kWaves; ++x) m_h[g] = fmaxf(m_h[g], sh.wmax[x][g]);
-      }
-      float lsum[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) lsum[g] = 0.f;
-      for (int j = tid; j < len; j += kThreads) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float e = expf(P[g * kPad + lidx(j)] - m_h[g]);
-          P[g * kPad + lidx(j)] = e;
-          lsum[g] += e;
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float v = lsum[g];
-        for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-        if (lane == 0) sh.wsum[w][g] = v;
-      }
-      __syncthreads();
-
-      // stream the split's V rows once: acc_g += p_gj * v_j
-      const _Float16* Vb = (const _Float16*)p.V + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
-      float acc[G][8];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
-      constexpr int ROWS_IT = UV * kWaves * RPW;
-      // two register buffers in a ping-pong loop: the rows of the next
-      // iteration are in flight while this iteration's FMAs run.  Loads are
-      // unconditional (rows past the end re-read the last row, weight 0), so
-      // the compiler counts outstanding loads exactly.
-      static_assert(kSplit % (2 * ROWS_IT) == 0, "iterations come in pairs");
-      uint4 va[UV], vb[UV];
-      auto issue = [&](uint4 (&bb)[UV], int base) {
-#pragma unroll
-        for (int x = 0; x < UV; ++x) {
-          const int row = min(base + (x * kWaves + w) * RPW + r, len - 1);
-          bb[x] = load_nt((const uint4*)(Vb + (size_t)row * D + c * 8));
-        }
-      };
-      auto consume = [&](const uint4 (&bb)[UV], int base) {
-#pragma unroll
-        for (int x = 0; x < UV; ++x) {
-          const int row = base + (x * kWaves + w) * RPW + r;
-          float f[8];
-          unpack8(bb[x], f);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float pw = row < len ? P[g * kPad + lidx(row)] : 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw, f[e], acc[g][e]);
-          }
-        }
-      };
-      issue(va, 0);
-      for (int base = 0; base < len; base += 2 * ROWS_IT) {
-        issue(vb, base + ROWS_IT);
-        consume(va, base);
-        issue(va, base + 2 * ROWS_IT);
-        consume(vb, base + ROWS_IT);
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          for (int m = LPR; m < 64; m <<= 1) acc[g][e] += __shfl_xor(acc[g][e], m, 64);
-      if (r == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) red[w * G * D + g * D + c * 8 + e] = acc[g][e];
-      }
-      __syncthreads();
-      float* part = p.ws.partial + (size_t)(group * p.ns + s) * G * PD;
-      for (int i = tid; i < G * D; i += kThreads) {
-        float v = red[i];
-#pragma unroll
-        for (int x = 1; x < kWaves; ++x) v += red[x * G * D + i];
-        store_dev(part + (i / D) * PD + (i % D), v);
-      }
-      if (tid < G) {
-        float l = sh.wsum[0][tid];
-#pragma unroll
-        for (int x = 1; x < kWaves; ++x) l += sh.wsum[x][tid];
-        float mh = sh.wmax[0][tid];
-#pragma unroll
-        for (int x = 1; x < kWaves; ++x) mh = fmaxf(mh, sh.wmax[x][tid]);
-        store_dev(part + tid * PD + D, mh);
-        store_dev(part + tid * PD + D + 1, l);
-      }
+      const int k0 = s * p.split;
+      const int len = min(p.split, n - k0);
+      split_pass<D, G>(p, b, hk, k0, len, red, sh, p.ws.partial + (size_t)(group * p.ns + s) * G * PD);
       wait_memory();
       __syncthreads();
       // arrival counter of the group (zero at rest: the last arrival resets it)
@@ -198,8 +285,9 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
         }
         __syncthreads();
         constexpr int CH = 32;                // splits merged per pass
-        float* scl = P;                       // [CH][G] e^(m_s - M)
-        float* lsc = P + CH * G;              // [CH][G] l_s e^(m_s - M)
+        float* scl = red;                     // [CH][G] e^(m_s - M)
+        float* lsc = red + CH * G;            // [CH][G] l_s e^(m_s - M)
+        static_assert(2 * CH * G <= kWaves * G * D, "the merge's scales fit the accumulator area");
         constexpr int OPT = (G * D + kThreads - 1) / kThreads;
         float num[OPT];
 #pragma unroll

@@ -3,6 +3,7 @@
 // Sanitizer.  No device code is built: every capacity query reports no
 // resident workgroups, so a call that passes its host checks returns
 // SANTA_ERR_HIP without launching anything.
+#include "santa.h"
 #include "launch.h"
 
 namespace santa {

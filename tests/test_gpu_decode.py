@@ -166,6 +166,17 @@ def test_group_beyond_register_chunks_parity(mode):
     check_parity(wl, 128, mode, 23, "long group")
 
 
+@pytest.mark.parametrize("mode", [2, 1, 0])
+def test_short_splits_beyond_register_chunks_parity(mode):
+    # one KV head with 391 splits of 512 keys (200000 keys: fewer than two
+    # 1024-key splits per CU, so the 512-key variant runs): more than the 256
+    # splits whose slots are read into registers at once
+    wl = W.random_case(1, 4, 1, 64, [200000], max_n_k=200000, seed=79, planted=True)
+    check_parity(wl, 128, mode, 25, "long group, short splits")
+    out_g, idx_g = run_decode_det(wl, 128, mode, 25)
+    _one_rounding(out_g, idx_g, wl, 128)
+
+
 # --------------------------------------------------------------------------
 # Llama-3.1-8B decode layer at 32k (32 q heads, 8 KV heads, d=128)
 # --------------------------------------------------------------------------
