@@ -23,8 +23,9 @@ Philox4x32-10 applied to counter ``(k >> 2, row, tag, 0)`` with key
 The Gumbel-max sampler needs one uniform per (draw, key): element ``j`` of
 draw ``k`` of stream ``(seed, row, tag)`` is output word ``j & 3`` of the
 counter ``(j >> 2, row, tag, k)`` (the fourth counter word numbers the draw),
-mapped into the open interval as ``((x >> 8) + 1/2) * 2**-24``, so that both
-logarithms of the Gumbel transform are finite.
+mapped into the open interval as ``((x >> 9) + 1/2) * 2**-23``: a value in
+[2**-24, 1 - 2**-24] that fp32 holds exactly, so that both logarithms of the
+Gumbel transform are finite on either side.
 
 Pinned by tests/test_oracle_philox.py against the generator authors'
 published known-answer vectors (tests/golden/philox4x32_10_kat.txt).
@@ -107,10 +108,10 @@ def uniforms(seed, row, tag, count):
 def draw_uniforms(seed, row, tag, draw, count):
     """Open-interval uniforms 0..count-1 of draw ``draw`` of stream (seed, row,
     tag): word j & 3 of counter (j >> 2, row, tag, draw), as
-    ((x >> 8) + 1/2) * 2**-24 in (0, 1), fp64 (exact)."""
+    ((x >> 9) + 1/2) * 2**-23 in [2**-24, 1 - 2**-24], fp64 (exact)."""
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     k0, k1 = seed & MASK32, seed >> 32
     blocks = np.arange((count + 3) // 4, dtype=np.uint64)
     out = philox4x32_10(blocks, row, tag, draw, k0, k1)
     words = np.stack(out, axis=-1).reshape(-1)[:count]
-    return ((words >> np.uint64(8)).astype(np.float64) + 0.5) * (2.0 ** -24)
+    return ((words >> np.uint64(9)).astype(np.float64) + 0.5) * (2.0 ** -23)

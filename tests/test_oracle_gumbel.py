@@ -22,7 +22,7 @@ def test_draw_uniforms_follow_the_counter_layout():
         u = philox.draw_uniforms(seed, row, philox.TAG_GUMBEL, draw, 11)
         for j in range(11):
             words = philox.philox4x32_10(j >> 2, row, philox.TAG_GUMBEL, draw, seed & 0xFFFFFFFF, seed >> 32)
-            assert u[j] == ((int(words[j & 3]) >> 8) + 0.5) * 2.0 ** -24
+            assert u[j] == ((int(words[j & 3]) >> 9) + 0.5) * 2.0 ** -23
         assert np.all((u > 0) & (u < 1))
     # the draw index moves the counter: different draws, different words
     a = philox.draw_uniforms(seed, row, philox.TAG_GUMBEL, 0, 8)
@@ -31,8 +31,8 @@ def test_draw_uniforms_follow_the_counter_layout():
 
 
 def test_dominant_logit_wins_every_draw():
-    # the Gumbel transform of an open-interval 24-bit uniform lies in
-    # (-2.9, 17.4), so a logit 40 above the others wins every draw
+    # the Gumbel transform of the open-interval 23-bit uniforms lies in
+    # [-2.82, 16.7], so a logit 40 above the others wins every draw
     s = np.zeros(50)
     s[17] = 40.0
     idx, gap = O.gumbel_draws(s, 64, 3, 0)
