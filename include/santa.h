@@ -221,6 +221,25 @@ int santa_bernoulli_qk_budget(const santa_problem* problem, const void* q, const
  * max_n_k must be a multiple of 64; K and K_fm must not overlap. */
 int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void* K_fm, void* stream);
 
+/* Allocation-free santa_decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, arguments and results as santa_decode, with
+ * the workspace in device memory that the library owns instead of a caller's
+ * buffer.  Each GPU the library runs on holds one array of
+ * SANTA_NOALLOC_SCRATCH_BYTES bytes for the rest of the process; a problem whose
+ * workspace would exceed it returns SANTA_ERR_WORKSPACE.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first call
+ * on a device takes the array's device address and enqueues a one-word clear
+ * on `stream`.  All calls on one GPU share its array: calls that overlap on one
+ * GPU (concurrent streams, threads) race and must be serialised by the caller.
+ * error_flags (nullable, device memory, 4 bytes): receives, OR-ed in, the
+ * device error bits of santa_workspace_error (the caller clears it); without
+ * it, device errors of this path are not reported. */
+#define SANTA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int santa_decode_noalloc(const santa_problem* problem, const void* q, const void* K, const void* V,
+                         const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
+                         int32_t* indices_out, float* scores_out, uint32_t* error_flags, void* stream);
+
 /* Measurement utility (not part of the decode step): read `bytes` bytes of the
  * device buffer `buf` once with the 16-byte non-temporal loads the decode
  * kernels stream K with, using workgroups_per_cu (1..8) workgroups of 256

@@ -69,6 +69,8 @@ def library():
     lib.santa_bernoulli_qk_budget.restype = ctypes.c_int
     lib.santa_pack_k_feature_major.argtypes = [P, vp, vp, vp]
     lib.santa_pack_k_feature_major.restype = ctypes.c_int
+    lib.santa_decode_noalloc.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, vp]
+    lib.santa_decode_noalloc.restype = ctypes.c_int
     lib.santa_stream_read.argtypes = [vp, sz, i32, vp, vp]
     lib.santa_stream_read.restype = ctypes.c_int
     lib.santa_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
@@ -228,6 +230,27 @@ def santa_decode(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, sco
                                 int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
                                 _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "santa_decode")
+    return out
+
+
+def santa_decode_noalloc(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, scores=None,
+                         error_flags=None, stream=None, deterministic=False):
+    """santa_decode with the library's own workspace (no allocation by the
+    library; ``out`` is allocated here only if not given).  ``error_flags``:
+    an optional int32 tensor of one element on the GPU that receives the
+    device error bits (OR-ed in)."""
+    _check_q(q)
+    _kv_pair(q, K, V)
+    extra = ((error_flags, "error_flags", torch.int32, (1,)),) if error_flags is not None else ()
+    _check_step(q, (K, V), ("K", "V"), n_k, out, indices, scores, S, K.shape[2], extra=extra)
+    prob = problem(q, K, scale, deterministic)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    mode = MODES.get(mode, mode)
+    st = library().santa_decode_noalloc(ctypes.byref(prob), _ptr(q), _ptr(K), _ptr(V), _ptr(n_k), int(S), int(mode),
+                                        int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
+                                        _ptr(error_flags), _stream(stream))
+    _check(st, "santa_decode_noalloc")
     return out
 
 
