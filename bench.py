@@ -72,7 +72,7 @@ def parse():
                              "batched-paged", "ceiling", "layers32", "bernoulli-stats"])
     ap.add_argument("--n-k", type=int, default=131072, help="sweep workload: keys per sequence")
     ap.add_argument("--r", type=float, default=1.0, help="sweep workload: logit standard deviation")
-    ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid"])
+    ap.add_argument("--mode", default="systematic", choices=["systematic", "stratified", "iid", "gumbel"])
     ap.add_argument("--S", type=int, default=128)
     ap.add_argument("--budget", type=int, default=0,
                     help="Bernoulli workload: 0 = ternary queries, m > 0 = the budget variant with m features")

@@ -45,16 +45,20 @@
  *  the caller keeps all buffers alive until the stream has completed them.
  *
  *  Workspace: a 256-byte aligned device buffer of at least
- *  santa_workspace_bytes(problem) bytes, zero-filled by the caller once
- *  before first use.  The first 256 bytes hold the error bits and the
- *  counters; partial results follow them; the per-split statistics slots and
- *  arrival flags sit at the end of the buffer.  Statistics slots are tagged
- *  with a launch number taken from a counter that every sampling call
- *  advances, and the arrival flags return to zero when a call finishes, so
- *  one buffer serves any sequence of calls whose problems each fit in it
- *  (including replays of a captured HIP graph).  Calls that share one
- *  workspace must not run concurrently.  After a call that reported a device
- *  error (santa_workspace_error != 0) the workspace must be zero-filled again.
+ *  santa_workspace_bytes(problem, S) bytes, zero-filled by the caller once
+ *  before first use.  The first 256 bytes hold the error bits and counters, a
+ *  64 KiB region of the dense kernel's arrival counters follows, then the data
+ *  of the call (the dense kernel's per-split records, or the sampling
+ *  kernel's per-split statistics slots, exact sums and Gumbel-max winners).
+ *  Only the header counters and the arrival counters must be zero when a call
+ *  starts, every call leaves them at zero, and no data region overlaps them;
+ *  statistics slots carry a launch number taken from a counter that every
+ *  sampling call advances, and every other data word is written (or cleared)
+ *  before it is read within a call.  So one buffer serves any sequence of
+ *  calls, of any entry point, whose problems each fit in it (including
+ *  replays of a captured HIP graph).  Calls that share one workspace must not
+ *  run concurrently.  After a call that reported a device error
+ *  (santa_workspace_error != 0) the workspace must be zero-filled again.
  *
  *  Errors: every entry point returns a santa_status.  Arguments are checked
  *  on the host before any HIP call; on a check failure nothing is enqueued.
@@ -70,12 +74,14 @@
  *  seed high 32 bits), mapped to (word >> 8) * 2^-24.  row = b * H_q + h for
  *  value sampling; tags are the ASCII codes 'SYST' (systematic offset),
  *  'STRT' (stratified), 'IID ' (i.i.d.), 'BERN' (Bernoulli features, row
- *  b * H_kv + h_kv).  Equal inputs and seed give bit-identical sampled
- *  indices; santa_decode / santa_bernoulli_qk outputs may differ between runs
- *  in the last bits, because the splits of the key sequence add their shares
- *  into `out` with fp32 atomics in whatever order they finish
- *  (santa_dense_decode merges its splits in a fixed order and is
- *  bit-reproducible).
+ *  b * H_kv + h_kv), 'GUMB' (Gumbel-max draws; see SANTA_GUMBEL).  Equal
+ *  inputs and seed give bit-identical sampled indices.  Outputs of the
+ *  sampling calls are bit-reproducible with the SANTA_DETERMINISTIC flag (and
+ *  always in the SANTA_GUMBEL mode); without it the splits of the key
+ *  sequence add their fp32 shares into `out` atomically in whatever order
+ *  they finish, so outputs may differ between runs in the last bits.
+ *  santa_dense_decode merges its splits in a fixed order and is
+ *  bit-reproducible.
  */
 #ifndef SANTA_H_
 #define SANTA_H_
@@ -104,8 +110,16 @@ typedef enum santa_status {
  *  SANTA_STRATIFIED: t_k = (k + u_k) / S, one uniform per stratum;
  *  SANTA_SYSTEMATIC: t_k = (k + u) / S, one uniform offset for all strata.
  * Point t selects the key j with F_{j-1} <= t < F_j, F the CDF of the
- * post-softmax distribution in key order (F_{-1} = 0). */
-typedef enum santa_mode { SANTA_IID = 0, SANTA_STRATIFIED = 1, SANTA_SYSTEMATIC = 2 } santa_mode;
+ * post-softmax distribution in key order (F_{-1} = 0).
+ *  SANTA_GUMBEL:     S i.i.d. draws by the Gumbel-max trick instead of the
+ *                    inverse CDF (santa_decode only): draw k selects
+ *                    argmax_j (s_j - log(-log u_kj)), u_kj = ((x >> 9) + 1/2)
+ *                    * 2^-23 with x = word (j & 3) of Philox4x32-10 at counter
+ *                    (j >> 2, row, 'GUMB', k); the smaller key on a tie; the
+ *                    indices are returned ascending and `out` is the exact sum
+ *                    of the rows rounded once (bit-reproducible).  It costs
+ *                    S * n_k generator words and logarithms per query head. */
+typedef enum santa_mode { SANTA_IID = 0, SANTA_STRATIFIED = 1, SANTA_SYSTEMATIC = 2, SANTA_GUMBEL = 3 } santa_mode;
 
 /* Problem description (host memory, read during the call only). */
 typedef struct santa_problem {
@@ -130,9 +144,10 @@ typedef struct santa_problem {
 /* Largest sample count accepted by santa_decode / santa_bernoulli_qk. */
 #define SANTA_MAX_S 1024
 
-/* Bytes of device workspace needed by every entry point for `problem`
- * (0 if the problem is invalid). */
-size_t santa_workspace_bytes(const santa_problem* problem);
+/* Bytes of device workspace that every entry point needs for `problem` and
+ * sample count S (1 .. SANTA_MAX_S; 0 if the problem or S is invalid).  A
+ * buffer of this size serves calls with any S' <= S. */
+size_t santa_workspace_bytes(const santa_problem* problem, int32_t S);
 
 /* SANTA decode step (the abstract's estimator, its second to fourth sentences).
  *   out[b][h] = (1/S) * sum_k V[b][h/G][i_k],  i_k drawn by `mode` from the
@@ -140,9 +155,10 @@ size_t santa_workspace_bytes(const santa_problem* problem);
  * S in [1, SANTA_MAX_S] (S may exceed n_k: sampling is with replacement).
  * indices_out (nullable): the S sampled key indices per head, ascending.
  * scores_out (nullable, debug): the fp32 scores the sampler used.
- * ceil(max_n_k / 1024) may not exceed the device's resident-workgroup count
- * for this kernel (>= 256 on MI355X, i.e. max_n_k >= 262144 is always
- * accepted); larger caches return SANTA_ERR_UNSUPPORTED. */
+ * When the problem has more splits of 1024 keys than the device keeps
+ * resident workgroups, ceil(max_n_k / 1024) may not exceed that resident
+ * count (at least 256 on MI355X, so max_n_k <= 262144 is always accepted);
+ * larger caches return SANTA_ERR_UNSUPPORTED. */
 int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V,
                  const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
                  int32_t* indices_out, float* scores_out, void* workspace, size_t workspace_bytes,
@@ -260,7 +276,7 @@ int santa_workspace_error(const void* workspace, uint32_t* flags, void* stream);
 const char* santa_status_string(int status);
 
 /* ABI version of this header (incremented on incompatible changes). */
-#define SANTA_ABI_VERSION 2
+#define SANTA_ABI_VERSION 3
 int32_t santa_abi_version(void);
 
 #ifdef __cplusplus

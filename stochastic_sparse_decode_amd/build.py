@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsanta.so")
 SOURCES = ["santa_api.cpp", "santa_decode.hip", "santa_dense.hip", "santa_pack.hip", "santa_ceiling.hip",
-           "santa_noalloc.hip"]
+           "santa_noalloc.hip", "santa_gumbel.hip"]
 ARCH = os.environ.get("SANTA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -36,6 +36,7 @@ struct Workspace {
   uint64_t* stats;      // [groups][G][ns][2] (tag:32 | split max bits, tag:32 | split mass bits); sized for
                         // splits of kMinSplit keys
   uint64_t* acc;        // [groups][G][D] exact output sums of the deterministic mode (cleared by split 0 per launch)
+  uint64_t* win;        // [B][H_q][S] Gumbel-max draws: (order bits of the value, ~key) winners (cleared per call)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
 };
 
@@ -97,8 +98,9 @@ namespace santa {
 int decode_on(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
               int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
               void* workspace, size_t workspace_bytes, uint32_t* err, void* stream);
-size_t sampling_workspace_bytes(const santa_problem* problem);
+size_t sampling_workspace_bytes(const santa_problem* problem, int32_t S);
 
+hipError_t launch_gumbel(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups_per_cu, uint32_t* sink,
                               hipStream_t stream);
 hipError_t launch_pack_feature_major(const void* K, void* K_fm, int B, int Hkv, int max_n_k, int D,

@@ -51,13 +51,15 @@ bool supported(const santa_problem* p) {
 constexpr size_t kCounterBytes = (size_t)santa::kMaxDenseGroups * sizeof(uint32_t);
 
 struct Layout {
-  size_t partial, stats, acc;
+  size_t partial, stats, acc, win;
   size_t dense_total() const { return kAlign + kCounterBytes + partial; }
-  size_t sampling_total() const { return kAlign + kCounterBytes + stats + acc; }
+  size_t sampling_total() const { return kAlign + kCounterBytes + stats + acc + win; }
   size_t total() const { return dense_total() > sampling_total() ? dense_total() : sampling_total(); }
 };
 
-Layout layout_of(const santa_problem* p) {
+// S: the sample count of the call (the Gumbel-max draws keep one winner per
+// query head and draw).
+Layout layout_of(const santa_problem* p, int32_t S) {
   Layout L{};
   const size_t groups = (size_t)p->batch * p->num_kv_heads;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
@@ -65,13 +67,14 @@ Layout layout_of(const santa_problem* p) {
   L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(float));
   L.stats = round_up(groups * ns_min * G * 2 * sizeof(uint64_t));
   L.acc = round_up(groups * G * D * sizeof(uint64_t));
+  L.win = round_up((size_t)p->batch * p->num_q_heads * (size_t)S * sizeof(uint64_t));
   return L;
 }
 
 // err, if not null, takes the place of the header's error word.
-Workspace carve(void* base, const santa_problem* p, bool dense, uint32_t* err = nullptr) {
+Workspace carve(void* base, const santa_problem* p, int32_t S, bool dense, uint32_t* err = nullptr) {
   unsigned char* b = (unsigned char*)base;
-  const Layout L = layout_of(p);
+  const Layout L = layout_of(p, S);
   Workspace w{};
   w.err = err ? err : (uint32_t*)b;
   w.work_ctr = (uint32_t*)b + 1;
@@ -83,6 +86,7 @@ Workspace carve(void* base, const santa_problem* p, bool dense, uint32_t* err = 
   } else {
     w.stats = (uint64_t*)x;
     w.acc = (uint64_t*)(x + L.stats);
+    w.win = (uint64_t*)(x + L.stats + L.acc);
   }
   return w;
 }
@@ -141,21 +145,21 @@ int capacity(int D, int G, int kind, int occ, int split = santa::kSplit) {
 }
 
 int common_checks(const santa_problem* p, const void* q, const void* K, const void* V, const int32_t* n_k,
-                  const float* out, const void* ws, size_t ws_bytes, bool dense) {
+                  const float* out, const void* ws, size_t ws_bytes, bool dense, int32_t S = 1) {
   if (!p) return SANTA_ERR_NULL;
   if (!q || !K || !V || !n_k || !out) return SANTA_ERR_NULL;
   if (!problem_ok(p)) return SANTA_ERR_SHAPE;
   if (!supported(p)) return SANTA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 4) || !aligned(n_k, 4))
     return SANTA_ERR_ALIGN;
-  const Layout L = layout_of(p);
+  const Layout L = layout_of(p, S);
   const size_t need = dense ? L.dense_total() : L.sampling_total();
   if (!ws || ws_bytes / kAlign * kAlign < need || !aligned(ws, kAlign)) return SANTA_ERR_WORKSPACE;
   return SANTA_OK;
 }
 
 DecodeParams base_params(const santa_problem* p, const void* q, const void* K, const void* V,
-                         const int32_t* n_k, float* out, void* ws, bool dense, uint32_t* err = nullptr) {
+                         const int32_t* n_k, float* out, void* ws, int32_t S, bool dense, uint32_t* err = nullptr) {
   DecodeParams d{};
   d.q = q;
   d.K = K;
@@ -171,7 +175,7 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
   d.scale = p->scale;
   d.ns = (p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   d.total_items = p->batch * p->num_kv_heads * d.ns;
-  d.ws = carve(ws, p, dense, err);
+  d.ws = carve(ws, p, S, dense, err);
   d.det = (p->flags & SANTA_DETERMINISTIC) ? 1 : 0;
   return d;
 }
@@ -234,20 +238,22 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
                  int32_t S, int32_t mode, uint64_t seed, float* out, int32_t* indices_out, float* scores_out,
                  uint8_t* kept_out, const float* k_scale, const Paging& pg, void* ws, size_t ws_bytes, void* stream,
                  int kind, int budget = 0, uint32_t* err = nullptr) {
-  int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes, false);
+  if (S < 1 || S > SANTA_MAX_S) return p && q && K && V && n_k && out ? SANTA_ERR_SHAPE : SANTA_ERR_NULL;
+  int st = common_checks(p, q, K, V, n_k, out, ws, ws_bytes, false, S);
   if (st != SANTA_OK) return st;
   if (kind == santa::kOpDecodeF8) {
     if (!k_scale) return SANTA_ERR_NULL;
     if (!aligned(k_scale, 4)) return SANTA_ERR_ALIGN;
     if (group_size(p) > p->head_dim / 16) return SANTA_ERR_UNSUPPORTED;  // d = 64 with G = 8
   }
-  if (S < 1 || S > SANTA_MAX_S) return SANTA_ERR_SHAPE;
-  if (mode != SANTA_IID && mode != SANTA_STRATIFIED && mode != SANTA_SYSTEMATIC) return SANTA_ERR_MODE;
+  if (mode != SANTA_IID && mode != SANTA_STRATIFIED && mode != SANTA_SYSTEMATIC && mode != SANTA_GUMBEL)
+    return SANTA_ERR_MODE;
+  if (mode == SANTA_GUMBEL && kind != santa::kOpDecode) return SANTA_ERR_UNSUPPORTED;
   if ((indices_out && !aligned(indices_out, 4)) || (scores_out && !aligned(scores_out, 4))) return SANTA_ERR_ALIGN;
   const bool bern = kind == santa::kOpBernoulli || kind == santa::kOpBernoulliBudget;
   if (bern && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
   if (kind == santa::kOpBernoulliBudget && (budget < 1 || budget > p->head_dim)) return SANTA_ERR_SHAPE;
-  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, false, err);
+  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, S, false, err);
   d.idx_out = indices_out;
   d.scores_out = scores_out;
   d.kept_out = kept_out;
@@ -259,6 +265,14 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   d.S = S;
   d.mode = mode;
   d.seed = seed;
+  if (mode == SANTA_GUMBEL) {
+    // no cross-workgroup wait: any grid; four workgroups per CU at most
+    const int cus = cu_count();
+    if (cus <= 0) return SANTA_ERR_HIP;
+    d.grid = d.total_items < 4 * cus ? d.total_items : 4 * cus;
+    const hipError_t e = santa::launch_gumbel(d, (hipStream_t)stream);
+    return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
+  }
   st = choose_grid(d, kind);
   if (st != SANTA_OK) return st;
   const hipError_t e = santa::launch_decode(d, key_kind(kind), (hipStream_t)stream);
@@ -277,16 +291,16 @@ int decode_on(const santa_problem* problem, const void* q, const void* K, const 
   return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, nullptr,
                       Paging{}, workspace, workspace_bytes, stream, kOpDecode, 0, err);
 }
-size_t sampling_workspace_bytes(const santa_problem* problem) {
-  return problem_ok(problem) ? layout_of(problem).sampling_total() : 0;
+size_t sampling_workspace_bytes(const santa_problem* problem, int32_t S) {
+  return problem_ok(problem) && S >= 1 && S <= SANTA_MAX_S ? layout_of(problem, S).sampling_total() : 0;
 }
 }  // namespace santa
 
 extern "C" {
 
-size_t santa_workspace_bytes(const santa_problem* problem) {
-  if (!problem_ok(problem)) return 0;
-  return layout_of(problem).total();
+size_t santa_workspace_bytes(const santa_problem* problem, int32_t S) {
+  if (!problem_ok(problem) || S < 1 || S > SANTA_MAX_S) return 0;
+  return layout_of(problem, S).total();
 }
 
 int santa_decode(const santa_problem* problem, const void* q, const void* K, const void* V, const int32_t* n_k,
@@ -344,7 +358,7 @@ int santa_dense_decode(const santa_problem* problem, const void* q, const void* 
   int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes, true);
   if (st != SANTA_OK) return st;
   if ((long long)problem->batch * problem->num_kv_heads > santa::kMaxDenseGroups) return SANTA_ERR_UNSUPPORTED;
-  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, true);
+  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, 1, true);
   st = choose_grid(d, santa::kOpDense);
   if (st != SANTA_OK) return st;
   const hipError_t e = santa::launch_dense(d, (hipStream_t)stream);

@@ -54,7 +54,7 @@ extern "C" int santa_decode_noalloc(const santa_problem* problem, const void* q,
                                     const int32_t* n_k, int32_t S, int32_t mode, uint64_t seed, float* out,
                                     int32_t* indices_out, float* scores_out, uint32_t* error_flags, void* stream) {
   if (!problem) return SANTA_ERR_NULL;
-  const size_t need = santa::sampling_workspace_bytes(problem);
+  const size_t need = santa::sampling_workspace_bytes(problem, S);
   if (need == 0) return SANTA_ERR_SHAPE;
   if (need > kScratchBytes) return SANTA_ERR_WORKSPACE;  // beyond the library's array
   void* ws = scratch_on_current_device((hipStream_t)stream);

@@ -14,8 +14,8 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsanta.so")
 
-IID, STRATIFIED, SYSTEMATIC = 0, 1, 2
-MODES = {"iid": IID, "stratified": STRATIFIED, "systematic": SYSTEMATIC}
+IID, STRATIFIED, SYSTEMATIC, GUMBEL = 0, 1, 2, 3
+MODES = {"iid": IID, "stratified": STRATIFIED, "systematic": SYSTEMATIC, "gumbel": GUMBEL}
 MAX_S = 1024
 DETERMINISTIC = 1  # santa_problem.flags: bit-reproducible out (exact sum, one rounding)
 ERR_SPIN_TIMEOUT = 1
@@ -53,7 +53,7 @@ def library():
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.POINTER(Problem)
     vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
-    lib.santa_workspace_bytes.argtypes = [P]
+    lib.santa_workspace_bytes.argtypes = [P, i32]
     lib.santa_workspace_bytes.restype = sz
     lib.santa_decode.argtypes = [P, vp, vp, vp, vp, i32, i32, u64, vp, vp, vp, vp, sz, vp]
     lib.santa_decode.restype = ctypes.c_int
@@ -114,13 +114,14 @@ def problem_fm(q, K_fm, scale, deterministic=False):
                    DETERMINISTIC if deterministic else 0)
 
 
-def workspace_bytes(prob):
-    return int(library().santa_workspace_bytes(ctypes.byref(prob)))
+def workspace_bytes(prob, S=MAX_S):
+    """santa_workspace_bytes for calls with sample counts up to S."""
+    return int(library().santa_workspace_bytes(ctypes.byref(prob), int(S)))
 
 
-def new_workspace(prob, device):
-    """Zero-filled workspace tensor of santa_workspace_bytes(prob) bytes."""
-    n = workspace_bytes(prob)
+def new_workspace(prob, device, S=MAX_S):
+    """Zero-filled workspace tensor of santa_workspace_bytes(prob, S) bytes."""
+    n = workspace_bytes(prob, S)
     if n == 0:
         raise SantaError(2, "santa_workspace_bytes")
     return torch.zeros(n, dtype=torch.uint8, device=device)
@@ -182,8 +183,8 @@ def _check_step(q, kv, kv_names, n_k, out, indices, scores, S, max_n_k, extra=()
     _on_gpu(q)
 
 
-def _check_workspace(workspace, prob, dev):
-    need = workspace_bytes(prob)
+def _check_workspace(workspace, prob, dev, S=1):
+    need = workspace_bytes(prob, S)
     if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 vector (see new_workspace)")
     if workspace.device != dev:
@@ -223,8 +224,8 @@ def santa_decode(q, K, V, n_k, S, mode, seed, scale, out=None, indices=None, sco
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = new_workspace(prob, dev)
-    _check_workspace(workspace, prob, dev)
+        workspace = new_workspace(prob, dev, S)
+    _check_workspace(workspace, prob, dev, S)
     mode = MODES.get(mode, mode)
     st = library().santa_decode(ctypes.byref(prob), _ptr(q), _ptr(K), _ptr(V), _ptr(n_k), int(S), int(mode),
                                 int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices), _ptr(scores),
@@ -272,8 +273,8 @@ def santa_decode_fp8k(q, K8, k_scale, V, n_k, S, mode, seed, scale, out=None, in
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = new_workspace(prob, dev)
-    _check_workspace(workspace, prob, dev)
+        workspace = new_workspace(prob, dev, S)
+    _check_workspace(workspace, prob, dev, S)
     mode = MODES.get(mode, mode)
     st = library().santa_decode_fp8k(ctypes.byref(prob), _ptr(q), _ptr(K8), _ptr(k_scale), _ptr(V), _ptr(n_k),
                                      int(S), int(mode), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(indices),
@@ -316,8 +317,8 @@ def santa_decode_paged(q, K_cache, V_cache, block_table, n_k, S, mode, seed, sca
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = new_workspace(prob, dev)
-    _check_workspace(workspace, prob, dev)
+        workspace = new_workspace(prob, dev, S)
+    _check_workspace(workspace, prob, dev, S)
     mode = MODES.get(mode, mode)
     st = library().santa_decode_paged(ctypes.byref(prob), _ptr(q), _ptr(K_cache), _ptr(V_cache), _ptr(block_table),
                                       int(K_cache.shape[2]), int(K_cache.shape[0]), _ptr(n_k), int(S), int(mode),
@@ -387,8 +388,8 @@ def santa_bernoulli_qk(q, K_fm, V, n_k, S, mode, seed, scale, out=None, indices=
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = new_workspace(prob, dev)
-    _check_workspace(workspace, prob, dev)
+        workspace = new_workspace(prob, dev, S)
+    _check_workspace(workspace, prob, dev, S)
     mode = MODES.get(mode, mode)
     if budget:
         st = library().santa_bernoulli_qk_budget(ctypes.byref(prob), _ptr(q), _ptr(K_fm), _ptr(V), _ptr(n_k),

@@ -13,15 +13,16 @@ hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return hipErro
 hipError_t launch_dense(const DecodeParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_pack_feature_major(const void*, void*, int, int, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_stream_read(const void*, size_t, int, uint32_t*, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_gumbel(const DecodeParams&, hipStream_t) { return hipErrorNoDevice; }
 }  // namespace santa
 
 // The allocation-free entry point needs the library's device array; here it
 // runs its host-side checks and stops where the array would be used.
 extern "C" int santa_decode_noalloc(const santa_problem* problem, const void*, const void*, const void*,
-                                    const int32_t*, int32_t, int32_t, uint64_t, float*, int32_t*, float*,
+                                    const int32_t*, int32_t S, int32_t, uint64_t, float*, int32_t*, float*,
                                     uint32_t*, void*) {
   if (!problem) return SANTA_ERR_NULL;
-  const size_t need = santa::sampling_workspace_bytes(problem);
+  const size_t need = santa::sampling_workspace_bytes(problem, S);
   if (need == 0) return SANTA_ERR_SHAPE;
   if (need > SANTA_NOALLOC_SCRATCH_BYTES) return SANTA_ERR_WORKSPACE;
   return SANTA_ERR_HIP;

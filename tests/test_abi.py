@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert santa.santa_abi_version() == 2
+    assert santa.santa_abi_version() == 3
     for code in range(8):
         assert santa.status_string(code).startswith("SANTA_")
     assert "unknown" in santa.status_string(99)
@@ -51,6 +51,10 @@ def test_workspace_bytes(lib):
     assert santa.workspace_bytes(_prob(num_q_heads=30)) == 0  # not a multiple of H_kv
     assert santa.workspace_bytes(_prob(batch=0)) == 0
     assert santa.workspace_bytes(_prob(scale=float("inf"))) == 0
+    # the sample count sizes the Gumbel-max winners (B * H_q * S words)
+    assert santa.workspace_bytes(_prob(), 0) == 0 and santa.workspace_bytes(_prob(), santa.MAX_S + 1) == 0
+    short = _prob(batch=8, max_n_k=1024)  # the sampling layout (with the winners) dominates here
+    assert santa.workspace_bytes(short, 1024) - santa.workspace_bytes(short, 1) >= 8 * 32 * 1023 * 8
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails its host checks
@@ -76,7 +80,8 @@ def test_host_checks_return_status_without_touching_the_gpu(lib):
     assert _decode(lib, p, ws=0) == 5
     assert _decode(lib, p, S=0) == 2
     assert _decode(lib, p, S=santa.MAX_S + 1) == 2
-    assert _decode(lib, p, mode=3) == 7
+    assert _decode(lib, p, mode=4) == 7
+    assert _decode(lib, p, mode=-1) == 7
     vp = ctypes.c_void_p
     # Bernoulli needs max_n_k % 64 == 0
     pb = _prob(max_n_k=1000)
@@ -109,6 +114,8 @@ def test_fp8k_host_checks(lib):
     p64 = _prob(head_dim=64, num_q_heads=64, num_kv_heads=8)
     assert call(p64, FAKE, santa.workspace_bytes(p64)) == 3   # d = 64 with G = 8 is not built
     assert call(p, FAKE, 16) == 5              # workspace too small
+    assert lib.santa_decode_fp8k(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 128, 3, 0,
+                                 vp(FAKE), None, None, vp(FAKE), nb, None) == 3  # Gumbel draws: santa_decode only
 
 
 def test_paged_host_checks(lib):
