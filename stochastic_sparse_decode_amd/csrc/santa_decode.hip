@@ -354,6 +354,24 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t u, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Inclusive prefix sum over segments of SEG lanes (SEG = 8 or 16; i = lane
+// index in its segment) of doubles that hold integers below 2^53, so every
+// partial sum is exact: DPP row shifts by 1, 2, 4 (and 8), a lane taking
+// nothing from across its segment's start.
+template <int SEG>
+__device__ __forceinline__ double seg_scan_exact(double c, int i) {
+  static_assert(SEG == 8 || SEG == 16, "segment width");
+  auto step = [&](auto ctrl, int k) {
+    const double sh = __builtin_bit_cast(double, dpp_u64<decltype(ctrl)::value, 0xF>(__builtin_bit_cast(uint64_t, c)));
+    c += (SEG == 16 || i >= k) ? sh : 0.0;
+  };
+  step(std::integral_constant<int, 0x111>{}, 1);
+  step(std::integral_constant<int, 0x112>{}, 2);
+  step(std::integral_constant<int, 0x114>{}, 4);
+  if constexpr (SEG == 16) step(std::integral_constant<int, 0x118>{}, 8);
+  return c;
+}
+
 // Number of keys j < len with c_j <= tau (c nondecreasing): the first key
 // whose CDF value exceeds tau, clamped to len - 1.  Branch-free radix-4
 // search over the split's SPLIT slots: each level reads three probes together
@@ -722,24 +740,27 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
           for (int c = 0; c < kRegChunks; ++c) Mloc = fmaxf(Mloc, v[c].x);
           for (int c0 = kRegChunks * 64; c0 < nsg; c0 += 64) Mloc = fmaxf(Mloc, far_slot(c0 + lane).x);
           const float M = wave_max(Mloc);
-          uint64_t carry = 0;
+          // Split masses in the units of M: Q_s = trunc(mass_s r_s), an integer
+          // (the product of two fp32 values is exact in fp64), below 2^41 each
+          // and 2^49 in total, so the double scan is exact.
+          double carry = 0.0;
           auto merge_chunk = [&](int c0, float2 sv) {
             const int x = c0 + lane;
-            const float r = x < nsg ? expf(sv.x - M) : 0.f;
-            const uint64_t Q = x < nsg ? (uint64_t)((double)sv.y * (double)r) : 0ull;  // integer split mass
-            const uint64_t inc = wave_incl_scan_u64(Q) + carry;
+            const float r = x < nsg ? exp_nonpos(sv.x - M) : 0.f;
+            const double Q = x < nsg ? trunc((double)sv.y * (double)r) : 0.0;
+            const double inc = wave_incl_scan_exact(Q) + carry;
             if (s >= c0 && s < c0 + 64) {
-              Olo = (double)readlane_u64(inc - Q, s - c0);
-              Ohi = (double)readlane_u64(inc, s - c0);
+              Olo = readlane_f64(inc - Q, s - c0);
+              Ohi = readlane_f64(inc, s - c0);
               rs = (double)__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), s - c0));
             }
-            carry = readlane_u64(inc, 63);
+            carry = readlane_f64(inc, 63);
           };
 #pragma unroll
           for (int c = 0; c < kRegChunks; ++c)
             if (c * 64 < nsg) merge_chunk(c * 64, v[c]);
           for (int c0 = kRegChunks * 64; c0 < nsg; c0 += 64) merge_chunk(c0, far_slot(c0 + lane));
-          Z = (double)carry;
+          Z = carry;
         }
 
         // 4. points per key and the list of selected keys (key | count << 16),
@@ -851,40 +872,34 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
             // the lane's two edges: points nL .. nR - 1 fall in its keys
             const int nL = n_at(lane * kPer - 1, wt.excl);
             const int nR = n_at(lane * kPer + kPer - 1, wt.excl + wt.lsum);
-            // Only lanes with points need their keys' edges.  Four such lanes
-            // at a time, one per row of 16 lanes: lane i of row r takes key i
-            // of the r-th lane, whose exact CDF value comes from a scan of the
-            // weights over the row.
+            // Only lanes with points need their keys' edges.  NSRC = 64 / kPer
+            // such source lanes at a time: lane j * kPer + i takes key i of the
+            // j-th of them, whose exact CDF value comes from a scan of the
+            // weights over its segment of kPer lanes; the source lane's prefix
+            // and left-edge count are fetched by a lane permutation.
+            constexpr int NSRC = 64 / kPer;
             uint64_t act = __ballot(nR > nL);
-            const int r = lane >> 4, i = lane & 15;
+            const int jsrc = lane / kPer, i = lane % kPer;
+            const uint64_t exu = __builtin_bit_cast(uint64_t, wt.excl);
             while (act != 0ull) {
-              int src[4];
+              int sl = -1;
 #pragma unroll
-              for (int x = 0; x < 4; ++x) {
-                src[x] = act != 0ull ? __ffsll((unsigned long long)act) - 1 : -1;
+              for (int x = 0; x < NSRC; ++x) {
+                const int f = act != 0ull ? __ffsll((unsigned long long)act) - 1 : -1;
+                sl = jsrc == x ? f : sl;
                 act &= act - 1ull;  // (no effect once empty)
               }
-              const int sl = r == 0 ? src[0] : r == 1 ? src[1] : r == 2 ? src[2] : src[3];
-              const bool valid = sl >= 0 && i < kPer;  // rows of 16 lanes, kPer <= 16 keys per source lane
+              const bool valid = sl >= 0;
               const int key = (valid ? sl : 0) * kPer + i;
               const uint32_t qk = list[lidx(key)];  // the key's weight
-              double c = valid ? (double)qk : 0.0;
-              c += __builtin_bit_cast(double, dpp_u64<0x111, 0xF>(__builtin_bit_cast(uint64_t, c)));
-              c += __builtin_bit_cast(double, dpp_u64<0x112, 0xF>(__builtin_bit_cast(uint64_t, c)));
-              c += __builtin_bit_cast(double, dpp_u64<0x114, 0xF>(__builtin_bit_cast(uint64_t, c)));
-              c += __builtin_bit_cast(double, dpp_u64<0x118, 0xF>(__builtin_bit_cast(uint64_t, c)));
-              double ex = 0.0;
-              int nl0 = 0;
-#pragma unroll
-              for (int x = 0; x < 4; ++x) {
-                const int sx = src[x] >= 0 ? src[x] : 0;
-                const double e = readlane_f64(wt.excl, sx);
-                const int n0 = __builtin_amdgcn_readlane(nL, sx);
-                ex = r == x ? e : ex;
-                nl0 = r == x ? n0 : nl0;
-              }
+              const double c = seg_scan_exact<kPer>(valid ? (double)qk : 0.0, i);
+              const int baddr = (valid ? sl : 0) * 4;
+              const uint32_t elo = (uint32_t)__builtin_amdgcn_ds_bpermute(baddr, (int)(uint32_t)exu);
+              const uint32_t ehi = (uint32_t)__builtin_amdgcn_ds_bpermute(baddr, (int)(uint32_t)(exu >> 32));
+              const double ex = __builtin_bit_cast(double, ((uint64_t)ehi << 32) | elo);
+              const int nl0 = __builtin_amdgcn_ds_bpermute(baddr, nL);
               const int nr = n_at(key, ex + c);  // right edge of the key
-              const int up = __builtin_amdgcn_update_dpp(0, nr, 0x111, 0xF, 0xF, true);  // right edge of key - 1
+              const int up = __builtin_amdgcn_update_dpp(0, nr, 0x111, 0xF, 0xF, true);  // right edge of key - 1 (i > 0)
               const int nl = i == 0 ? nl0 : up;
               const int cnt = valid ? nr - nl : 0;
               const uint64_t selm = __ballot(cnt > 0);
@@ -1026,9 +1041,11 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
           float a8[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) a8[e] = 0.f;
-          auto add_rows = [&](const uint4 (&vv)[kVU], const uint32_t (&ee)[kVU]) {
+          // rounds past the list (nsel is the same in every lane) are skipped
+          auto add_rows = [&](const uint4 (&vv)[kVU], const uint32_t (&ee)[kVU], int i0) {
 #pragma unroll
             for (int u = 0; u < kVU; ++u) {
+              if (i0 + u * RPW >= nsel) break;
               const float cf = (float)(ee[u] >> 16);
               float f8[8];
               unpack8(vv[u], f8);
@@ -1036,7 +1053,7 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
               for (int e = 0; e < 8; ++e) a8[e] = fmaf(cf, f8[e], a8[e]);
             }
           };
-          add_rows(gt.vv, gt.ee);
+          add_rows(gt.vv, gt.ee, 0);
           for (int i0 = RPW * kVU; i0 < nsel; i0 += RPW * kVU) {
             uint4 vv[kVU];
             uint32_t ee[kVU];
@@ -1047,22 +1064,46 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
               vv[u] = i < nsel ? *(const uint4*)(row_of(p.V, it, wb, (int)(ee[u] & 0xffffu)) + c * 8)
                                : make_uint4(0, 0, 0, 0);
             }
-            add_rows(vv, ee);
+            add_rows(vv, ee, i0);
           }
-          // sum the RPW row slots through LDS (the head's uniform row, free by
-          // now) so that lane l ends with features l, l + 64, ...: each atomic
-          // instruction then covers 64 consecutive floats
-          float* part = (float*)(uni + g * kUniRow);  // [RPW][D]
-          wave_lds_sync();
-          *(float4*)(part + r * D + c * 8) = make_float4(a8[0], a8[1], a8[2], a8[3]);
-          *(float4*)(part + r * D + c * 8 + 4) = make_float4(a8[4], a8[5], a8[6], a8[7]);
-          wave_lds_sync();
+          // Sum the RPW row slots in registers (reduce-scatter).  Lane (r, c)
+          // holds features c*8 .. c*8+7 of row slot r.  A swap of the wave's
+          // halves pairs feature e with e + 4 (the lower half keeps the sums of
+          // 0..3, the upper those of 4..7) and a swap of odd and even rows of
+          // 16 pairs the remaining j with j + 2: lane (r, c) then holds the
+          // totals of features c*8 + 2r and c*8 + 2r + 1 (D = 128).  For D = 64
+          // (rows of 8 lanes) a rotation adds the two halves of each row of 16,
+          // and lane (r, c) keeps feature c*8 + r.  For D = 128 a lane
+          // permutation gives lane l features l and 64 + l, so that each atomic
+          // instruction covers 64 consecutive floats (two cache lines, not four:
+          // the splits of a head all add into the same row).
+          float h4[4], h2[2];
 #pragma unroll
-          for (int f = 0; f < D / 64; ++f) {
-            float v = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(a8[e]), __float_as_uint(a8[e + 4]), false, false);
+            h4[e] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+          }
 #pragma unroll
-            for (int x = 0; x < RPW; ++x) v += part[x * D + f * 64 + lane];
-            atomic_add_dev(orow + f * 64 + lane, v / (float)S);
+          for (int e = 0; e < 2; ++e) {
+            const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[e]), __float_as_uint(h4[e + 2]), false, false);
+            h2[e] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+          }
+          const float inv_s = 1.0f / (float)S;  // exact for a power of two S, else one more rounding
+          if constexpr (D == 128) {
+            // lane l takes features l and 64 + l: feature F = c*8 + 2R + e sits in lane 16R + c, value e
+            const int e = lane & 1, R = (lane & 7) >> 1, cc = lane >> 3;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+              const int src_lane = 16 * R + cc + 8 * f;
+              const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane * 4, __float_as_int(h2[0])));
+              const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane * 4, __float_as_int(h2[1])));
+              atomic_add_dev(orow + f * 64 + lane, (e ? v1 : v0) * inv_s);
+            }
+          } else {
+            static_assert(D == 64, "head dimension");
+            const float s0 = h2[0] + dpp_row_ror<0x128>(h2[0]);
+            const float s1 = h2[1] + dpp_row_ror<0x128>(h2[1]);
+            atomic_add_dev(orow + c * 8 + r, ((r & 1) ? s1 : s0) * inv_s);
           }
         }
   };
