@@ -46,14 +46,15 @@
  *
  *  Workspace: a 256-byte aligned device buffer of at least
  *  santa_workspace_bytes(problem, S) bytes, zero-filled by the caller once
- *  before first use.  The first 256 bytes hold the error bits and counters, a
+ *  before first use.  The first 1 KiB holds the error bits and counters, a
  *  64 KiB region of the dense kernel's arrival counters follows, then the data
  *  of the call (the dense kernel's per-split records, or the sampling
  *  kernel's per-split statistics slots, exact sums and Gumbel-max winners).
- *  Only the header counters and the arrival counters must be zero when a call
- *  starts, every call leaves them at zero, and no data region overlaps them;
- *  statistics slots carry a launch number taken from a counter that every
- *  sampling call advances, and every other data word is written (or cleared)
+ *  The dense kernel's work counter and arrival counters must be zero when a
+ *  call starts and every call leaves them at zero; the launch counters only
+ *  grow; no data region overlaps the header or the arrival counters.
+ *  Statistics slots carry a launch number taken from the launch counters,
+ *  which every sampling call advances, and every other data word is written (or cleared)
  *  before it is read within a call.  So one buffer serves any sequence of
  *  calls, of any entry point, whose problems each fit in it (including
  *  replays of a captured HIP graph).  Calls that share one workspace must not
@@ -259,7 +260,9 @@ int santa_decode_noalloc(const santa_problem* problem, const void* q, const void
 /* Measurement utility (not part of the decode step): read `bytes` bytes of the
  * device buffer `buf` once with the 16-byte non-temporal loads the decode
  * kernels stream K with, using workgroups_per_cu (1..8) workgroups of 256
- * threads per compute unit, each reading one contiguous range.  Nothing is
+ * threads per compute unit, each reading one contiguous range with two
+ * buffers of 16, 8 or 4 loads per lane in flight (1, 2, or more workgroups
+ * per CU: the same bytes in flight per CU).  Nothing is
  * written except, practically never, one word of `sink` (device memory, 4
  * bytes): the loaded words are folded into a value that is stored only if it
  * equals a fixed constant, so the loads cannot be optimised away.  It gives

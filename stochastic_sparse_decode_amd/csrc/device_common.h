@@ -315,6 +315,13 @@ __device__ __forceinline__ float2 load_dev(const float2* p) {
 __device__ __forceinline__ void store_dev(float2* p, float2 v) {
   __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte read that bypasses the caches between this CU and the device's
+// coherence point (global_load_dwordx4 sc0 sc1), for polling a 16-byte slot
+// whose halves another workgroup writes with device-scope stores: each half
+// is read as one value, and a reader that sees a half not yet written retries.
+__device__ __forceinline__ u32x4 load_dev16(const void* p) {
+  return *(const volatile __attribute__((address_space(1))) u32x4*)p;
+}
 // Workgroup barrier that orders LDS accesses only: global loads and stores
 // in flight stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -15,6 +15,8 @@ constexpr int kMaxS = 1024;     // largest sample count
 constexpr int kTile = 64;       // keys per feature-major tile (Bernoulli mode)
 constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait: ~1 s, then error flag
 constexpr uint64_t kLaunchUnit = 1ull << 20;  // launch counter increment per launch (> any grid)
+constexpr int kLaunchCounters = 7;     // the launch count is the sum of 7 counters, one per 128-byte line
+constexpr int kLaunchStride = 16;      // uint64 words between the counters
 
 // Error bits written by kernels into the workspace header.
 constexpr uint32_t kErrSpinTimeout = 1u;
@@ -31,7 +33,7 @@ constexpr int kMaxDenseGroups = 16384;  // B * H_kv of a dense step (its counter
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dense kernel: dynamic work-item counter, returns to 0 at kernel end
-  uint64_t* launches;   // launch counter of the sampling kernel: kLaunchUnit added per launch
+  uint64_t* launches;   // launch counters of the sampling kernel (their sum grows by kLaunchUnit per launch)
   uint32_t* arrive;     // [groups] dense kernel: splits of the group that stored their record, back to 0
   uint64_t* stats;      // [groups][G][ns][2] (tag:32 | split max bits, tag:32 | split mass bits); sized for
                         // splits of kMinSplit keys
@@ -75,9 +77,18 @@ struct DecodeParams {
                         // turn (two workgroups per CU), 3 = one item per workgroup (two per CU)
   int split;            // keys per work item of the sampling kernel: kSplit, or 512 (variant 3, plain fp16 cache)
   int det;              // 1: out is the exact sum of the gathered rows rounded once (bit-reproducible)
+  int slot_words;       // 8-byte words per statistics slot: 2, or 16 (one slot per 128-byte line)
   Workspace ws;
 };
 static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");
+
+// Statistics slots: 16 bytes each, or one per 128-byte line when the padded
+// region of a problem stays within kPaddedSlotBytes.  A head's slots are
+// polled by every workgroup of its group; with one slot per line, the reads of
+// one line come only from the lanes that wait for that slot, and the split
+// that writes it shares the line with no other.
+constexpr size_t kPaddedSlotBytes = 1u << 20;
+inline int slot_words_for(size_t slots) { return slots * 128 <= kPaddedSlotBytes ? 16 : 2; }
 
 enum Op { kOpDecode = 0, kOpDense = 1, kOpBernoulli = 2, kOpDecodeF8 = 3, kOpDecodePaged = 4, kOpBernoulliBudget = 5 };
 

@@ -49,11 +49,12 @@ bool supported(const santa_problem* p) {
 // either kind and of different sizes may share a buffer even though their data
 // regions overlap.
 constexpr size_t kCounterBytes = (size_t)santa::kMaxDenseGroups * sizeof(uint32_t);
+constexpr size_t kHeaderBytes = 1024;  // error bits, work counter, kLaunchCounters launch counters (one per 128 bytes)
 
 struct Layout {
   size_t partial, stats, acc, win;
-  size_t dense_total() const { return kAlign + kCounterBytes + partial; }
-  size_t sampling_total() const { return kAlign + kCounterBytes + stats + acc + win; }
+  size_t dense_total() const { return kHeaderBytes + kCounterBytes + partial; }
+  size_t sampling_total() const { return kHeaderBytes + kCounterBytes + stats + acc + win; }
   size_t total() const { return dense_total() > sampling_total() ? dense_total() : sampling_total(); }
 };
 
@@ -65,7 +66,7 @@ Layout layout_of(const santa_problem* p, int32_t S) {
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
   const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
   L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(float));
-  L.stats = round_up(groups * ns_min * G * 2 * sizeof(uint64_t));
+  L.stats = round_up(groups * ns_min * G * (size_t)santa::slot_words_for(groups * ns_min * G) * sizeof(uint64_t));
   L.acc = round_up(groups * G * D * sizeof(uint64_t));
   L.win = round_up((size_t)p->batch * p->num_q_heads * (size_t)S * sizeof(uint64_t));
   return L;
@@ -78,9 +79,9 @@ Workspace carve(void* base, const santa_problem* p, int32_t S, bool dense, uint3
   Workspace w{};
   w.err = err ? err : (uint32_t*)b;
   w.work_ctr = (uint32_t*)b + 1;
-  w.launches = (uint64_t*)(b + 8);
-  w.arrive = (uint32_t*)(b + kAlign);
-  unsigned char* x = b + kAlign + kCounterBytes;
+  w.launches = (uint64_t*)(b + 128);  // counter i at launches + i * kLaunchStride
+  w.arrive = (uint32_t*)(b + kHeaderBytes);
+  unsigned char* x = b + kHeaderBytes + kCounterBytes;
   if (dense) {
     w.partial = (float*)x;
   } else {
@@ -177,6 +178,8 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
   d.total_items = p->batch * p->num_kv_heads * d.ns;
   d.ws = carve(ws, p, S, dense, err);
   d.det = (p->flags & SANTA_DETERMINISTIC) ? 1 : 0;
+  const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
+  d.slot_words = santa::slot_words_for((size_t)p->batch * p->num_kv_heads * ns_min * d.G);  // as layout_of
   return d;
 }
 

@@ -436,15 +436,20 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int S = p.S;
-  // Launch tag of the statistics slots.  Every launch adds exactly
-  // kLaunchUnit to the workspace's 64-bit launch counter: workgroup 0 adds
-  // kLaunchUnit - (grid - 1), every other workgroup 1, each only after its own
-  // read of the counter has completed.  So every read made during launch L
-  // returns a value in [L kLaunchUnit, (L + 1) kLaunchUnit), all workgroups of
-  // a launch derive the same launch number, and a slot left by an earlier
-  // launch (or an earlier replay of a captured graph) never carries this
-  // launch's tag.  No workgroup waits for the add.
-  uint64_t lc = 0ull;  // thread 0: the counter value read (issued with the first item)
+  // Launch tag of the statistics slots.  The launch count is the sum of the
+  // workspace's kLaunchCounters 64-bit counters (one per 128-byte line, so that
+  // the adds of a launch do not all queue on one address), and every launch
+  // adds exactly kLaunchUnit to that sum: workgroup 0 adds kLaunchUnit -
+  // (grid - 1) to counter 0, every other workgroup x adds 1 to counter
+  // x mod kLaunchCounters, each only after its own reads of all the counters
+  // have completed.  The counters only grow, so a sum read during launch L,
+  // even from values read one at a time, is at least L kLaunchUnit and lacks
+  // at least the reader's own add: it lies in [L kLaunchUnit, (L + 1)
+  // kLaunchUnit).  All workgroups of a launch derive the same launch number,
+  // and a slot left by an earlier launch (or an earlier replay of a captured
+  // graph) never carries this launch's tag.  No workgroup waits for the add.
+  uint64_t lc = 0ull;  // lane i < kLaunchCounters of wave 0: counter i as read (issued with the first item)
+  bool tagged = false;  // the launch tag is in sh.epoch
   // One field of each 64-byte line of the arguments is fetched here, so all
   // lines arrive in one scalar round trip instead of one after another where
   // their fields are first used (the first K load waits for them).
@@ -478,7 +483,7 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     const int n = p.n_k[it.b];
     // the counter read is issued after the length read, so waiting for the
     // length does not wait for it; it is first needed after the score stage
-    if (tid == 0 && !counted) lc = load_dev(p.ws.launches);
+    if (tid < kLaunchCounters && !tagged) lc = load_dev(p.ws.launches + tid * kLaunchStride);
     it.valid = n >= 1 && n <= p.max_n_k;
     it.nsg = it.valid ? (n + SPLIT - 1) / SPLIT : 0;
     it.active = it.valid && it.s < it.nsg;
@@ -573,9 +578,11 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     wt.total = readlane_f64(incl, 63);
   };
 
-  // Statistics slots of head g of an item's group: [group][head][split][2].
+  // Statistics slots of head g of an item's group: [group][head][split], each
+  // slot (tag:32 | max bits, tag:32 | mass bits) at the start of p.slot_words
+  // 8-byte words.
   auto slot_row = [&](const uint64_t* base, const ItemCtx& it, int g) -> const uint64_t* {
-    return base + ((size_t)it.group * G + g) * p.ns * 2;
+    return base + ((size_t)it.group * G + g) * p.ns * p.slot_words;
   };
   // Publish head g's (split max, split mass).
   auto publish = [&](const ItemCtx& it, int g, const Weights& wt) {
@@ -589,14 +596,14 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
         if (it.s == 0) wait_memory();
         if (lane < 2) {
           const uint64_t t = (uint64_t)tag << 32;
-          uint64_t* sl = const_cast<uint64_t*>(slot_row(p.ws.stats, it, g)) + it.s * 2 + lane;
+          uint64_t* sl = const_cast<uint64_t*>(slot_row(p.ws.stats, it, g)) + it.s * p.slot_words + lane;
           store_dev(sl, t | __float_as_uint(lane == 0 ? wt.m : (float)wt.total));
         }
         // this workgroup's share of the launch counter (its read has completed:
         // the value is in LDS); issued after the publish so that no wait before
         // a publish covers its round trip
         if (tid == 0 && !counted) {
-          atomic_add_noret(p.ws.launches, my_add);
+          atomic_add_noret(p.ws.launches + (blockIdx.x % kLaunchCounters) * kLaunchStride, my_add);
           counted = true;
         }
   };
@@ -613,13 +620,16 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     uint4 vv[kVU];
   };
   // One round of reads of head g's statistics slots: the first kRegChunks * 64
-  // splits, issued together (so a round is one round trip) and kept in
-  // registers; a lane past the last split reads the last split's slot.  The
-  // reads are unconditional, so the compiler knows exactly how many loads
-  // are younger than any earlier one it waits for.
+  // splits, one 16-byte read per slot (both halves, each carrying the launch
+  // tag), issued together so that a round is one round trip, and kept in
+  // registers.  A lane whose slot already carries this launch's tag, or lies
+  // past the group's last split, reads nothing: the waiting waves request
+  // only the slots still missing, so the polls load the memory system less
+  // while the last splits finish.
   constexpr int kRegChunks = 4;
   struct Poll {
-    uint64_t ra[kRegChunks], rc[kRegChunks];
+    u32x4 sl[kRegChunks];  // (m bits, tag, mass bits, tag)
+    bool seen[kRegChunks];
   };
   // Chunks past the group's last split are not read.
   auto poll_issue = [&](const ItemCtx& it, int g, Poll& pl) {
@@ -627,9 +637,7 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
 #pragma unroll
     for (int c = 0; c < kRegChunks; ++c) {
       if (c > 0 && c * 64 >= it.nsg) break;
-      const int x = min(c * 64 + lane, it.nsg - 1);
-      pl.ra[c] = load_dev(slots + x * 2);
-      pl.rc[c] = load_dev(slots + x * 2 + 1);
+      if (!pl.seen[c]) pl.sl[c] = load_dev16(slots + (c * 64 + lane) * p.slot_words);
     }
   };
   auto tail_a = [&](const ItemCtx& it, int g, float* scb, int wb, const Weights& wt, Gather& gt, bool stashed) {
@@ -675,24 +683,25 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
           // are up to that bound); splits beyond it are polled and re-read a
           // chunk of 64 at a time.
           auto read_slot = [&](int x, bool& ok) -> float2 {
-            const uint64_t a = load_dev(slots + x * 2);
-            const uint64_t c = load_dev(slots + x * 2 + 1);
-            ok = (uint32_t)(a >> 32) == tag && (uint32_t)(c >> 32) == tag;
-            return make_float2(__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)c));
+            const u32x4 a = load_dev16(slots + x * p.slot_words);
+            ok = a.y == tag && a.w == tag;
+            return make_float2(__uint_as_float(a.x), __uint_as_float(a.z));
           };
           float2 v[kRegChunks];
           {
             Poll pl;
 #pragma unroll
-            for (int c = 0; c < kRegChunks; ++c) v[c] = make_float2(-INFINITY, 0.f);
+            for (int c = 0; c < kRegChunks; ++c) {
+              pl.seen[c] = c * 64 + lane >= nsg;
+              pl.sl[c] = u32x4{0u, 0u, 0u, 0u};
+            }
             auto test = [&]() -> bool {
               bool all = true;
 #pragma unroll
               for (int c = 0; c < kRegChunks; ++c) {
                 if (c > 0 && c * 64 >= nsg) break;
-                v[c] = make_float2(__uint_as_float((uint32_t)pl.ra[c]), __uint_as_float((uint32_t)pl.rc[c]));
-                const bool ok = (uint32_t)(pl.ra[c] >> 32) == tag && (uint32_t)(pl.rc[c] >> 32) == tag;
-                all = all && (ok || c * 64 + lane >= nsg);
+                pl.seen[c] = pl.seen[c] || (pl.sl[c].y == tag && pl.sl[c].w == tag);
+                all = all && pl.seen[c];
               }
               return __ballot(!all) == 0ull;
             };
@@ -711,7 +720,8 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
             }
 #pragma unroll
             for (int c = 0; c < kRegChunks; ++c)
-              if (c * 64 + lane >= nsg) v[c] = make_float2(-INFINITY, 0.f);
+              v[c] = c * 64 + lane < nsg ? make_float2(__uint_as_float(pl.sl[c].x), __uint_as_float(pl.sl[c].z))
+                                         : make_float2(-INFINITY, 0.f);
           }
           // Beyond the register chunks: a lane stops reading once its slot
           // carries this launch's tag, and the wave sleeps between rounds, so
@@ -1178,11 +1188,15 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
       m = row_max_mod<G>(m);
       if ((lane & 15) < G) sh.wmax[wb][w * 4 + (lane >> 4)][lane & 15] = m;
     }
-    if (tid == 0 && !counted) {
-      uint64_t c = lc;
-      asm volatile("" : "+v"(c));  // keeps the wait for the counter read here, after the stream
-      sh.epoch = tag_of(c);
+    if (w == 0 && !tagged) {
+      uint64_t c = tid < kLaunchCounters ? lc : 0ull;
+      asm volatile("" : "+v"(c));  // keeps the wait for the counter reads here, after the stream
+      uint64_t sum = 0ull;
+#pragma unroll
+      for (int i = 0; i < kLaunchCounters; ++i) sum += readlane_u64(c, i);
+      if (tid == 0) sh.epoch = tag_of(sum);
     }
+    tagged = true;
     lds_barrier();
     if (p.scores_out) {
       write_scores<G, SPLIT>(p, it.b, it.hk, it.k0, it.len, scb);
@@ -1213,7 +1227,7 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     // a group are consecutive items, so with nsg <= grid they fall in at most
     // two consecutive rounds; every workgroup publishes its item of round r
     // before it waits for any item of round r or later, so the waits end.
-    if (tid == 0 && !counted) lc = load_dev(p.ws.launches);
+    if (tid < kLaunchCounters && !tagged) lc = load_dev(p.ws.launches + tid * kLaunchStride);
     // sequences with an invalid length: NaN outputs, indices -1
     for (int bq = blockIdx.x; bq < p.B; bq += p.grid) {
       const int n = p.n_k[bq];
@@ -1277,7 +1291,8 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
   }
   // ---- a workgroup that scored nothing still adds its share ----------------
   // (the amount is computed from the value read, so the add follows the read)
-  if (tid == 0 && !counted) atomic_add_noret(p.ws.launches, lc == ~0ull ? 0ull : my_add);
+  if (tid == 0 && !counted)
+    atomic_add_noret(p.ws.launches + (blockIdx.x % kLaunchCounters) * kLaunchStride, lc == ~0ull ? 0ull : my_add);
 }
 
 // The one-item variant with two workgroups per CU asks for 56 KiB of LDS so
