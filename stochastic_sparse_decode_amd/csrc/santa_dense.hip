@@ -61,6 +61,16 @@ __device__ __forceinline__ float row_lane(float v, int lane) {
   }
 }
 
+// Maximum over the four rows of 16 lanes at the same position, in every
+// lane: a swap of the wave's halves, then of odd and even rows (VALU lane
+// swaps, no LDS round trip).
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Sum over the lanes of this lane's DPP row of 16 that are congruent to it
 // modulo G (G a power of two, at most 8), in every lane.
 template <int G>
@@ -134,8 +144,7 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
       const float sc = row < len ? sv[0] * p.scale : -INFINITY;
       // block maximum of each head (lanes congruent modulo G hold one head)
       float bm = row_max_mod<G>(sc);
-      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      bm = max_over_rows(bm);
       float alpha[G], mine_m = 0.f, mine_a = 1.f;
       bool rescale = false;
 #pragma unroll
@@ -180,20 +189,42 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
   }
 
   // combine: the RPW key-row groups of a wave (lanes with the same c), the
-  // lanes of each head for l, then the four waves through LDS
+  // lanes of each head for l, then the four waves through LDS.  The row
+  // groups are summed in registers (reduce-scatter): a swap of the wave's
+  // halves pairs feature e with e + 4 (the lower half keeps the sums of 0..3,
+  // the upper those of 4..7), a swap of odd and even rows of 16 pairs the
+  // remaining j with j + 2, and for D = 64 (rows of 8 lanes) a rotation adds
+  // the two halves of each row of 16.  Lane (r, c) then holds the wave's
+  // totals of features c*8 + 2r, c*8 + 2r + 1 (D = 128) or c*8 + r (D = 64).
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+  for (int g = 0; g < G; ++g) {
+    float h4[4], h2[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      for (int x = LPR; x < 64; x <<= 1) acc[g][e] += __shfl_xor(acc[g][e], x, 64);
+    for (int e = 0; e < 4; ++e) {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[g][e]), __float_as_uint(acc[g][e + 4]), false, false);
+      h4[e] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(h4[e]), __float_as_uint(h4[e + 2]), false, false);
+      h2[e] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+    float* dst = red + (w * G + g) * D + c * 8;
+    if constexpr (D == 128) {
+      *(float2*)(dst + 2 * r) = make_float2(h2[0], h2[1]);
+    } else {
+      static_assert(D == 64, "head dimension");
+      const float s0 = h2[0] + dpp_row_ror<0x128>(h2[0]);
+      const float s1 = h2[1] + dpp_row_ror<0x128>(h2[1]);
+      dst[r] = (r & 1) ? s1 : s0;
+    }
+  }
   float lw = row_sum_mod<G>(l);
-  lw += __shfl_xor(lw, 16, 64);
-  lw += __shfl_xor(lw, 32, 64);
-  if (r == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red[(w * G + g) * D + c * 8 + e] = acc[g][e];
+  {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lw), __float_as_uint(lw), false, false);
+    lw = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(lw), __float_as_uint(lw), false, false);
+    lw = __uint_as_float(b[0]) + __uint_as_float(b[1]);
   }
   if (lane < G) {
     sh.wmax[w][lane] = m[0];
@@ -264,17 +295,41 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
       if (sh.last) {
         // out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s, split order
         const float* gp = p.ws.partial + (size_t)group * p.ns * G * PD;
-        float mg[G];
+        constexpr int CH = 32;                // splits merged per pass
+        constexpr int OPT = (G * D + kThreads - 1) / kThreads;
+        float t[OPT][CH];  // one pass's partial vectors, all loads in flight at once
+        auto load_pass = [&](int x0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) mg[g] = -INFINITY;
-        for (int x = tid; x < nsg; x += kThreads)
+          for (int o = 0; o < OPT; ++o) {
+            const int i = min(tid + o * kThreads, G * D - 1);
+            const int g = i / D, d = i % D;
 #pragma unroll
-          for (int g = 0; g < G; ++g) mg[g] = fmaxf(mg[g], load_dev(gp + (size_t)x * G * PD + g * PD + D));
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float m = wave_max_masked(mg[g], 1);
-          if (lane == 0) sh.wmax[w][g] = m;
-        }
+            for (int u = 0; u < CH; ++u) t[o][u] = load_dev(gp + (size_t)min(x0 + u, nsg - 1) * G * PD + g * PD + d);
+          }
+        };
+        // the first pass's vectors and its splits' (m, l) are requested
+        // together, with the maxima of the later splits, so that all of them
+        // arrive in one round trip: thread tid < CH * G holds (m, l) of split
+        // x0 + tid / G, head tid % G of the pass
+        load_pass(0);
+        auto load_ml = [&](int x0, float& mx, float& lx) {
+          const int x = x0 + tid / G, g = tid % G;
+          mx = -INFINITY;
+          lx = 0.f;
+          if (tid < CH * G && x < nsg) {
+            const float* rec = gp + (size_t)x * G * PD + g * PD;
+            mx = load_dev(rec + D);
+            lx = load_dev(rec + D + 1);
+          }
+        };
+        float mx, lx;
+        load_ml(0, mx, lx);
+        // the maximum over every split: this pass's from mx, later ones read here
+        float mo = mx;
+        for (int x = CH + tid / G; x < nsg; x += kThreads / G) mo = fmaxf(mo, load_dev(gp + (size_t)x * G * PD + (tid % G) * PD + D));
+        // lanes congruent modulo G hold one head: rows of 16, then across rows
+        mo = max_over_rows(row_max_mod<G>(mo));
+        if (lane < G) sh.wmax[w][lane] = mo;
         if (tid < G) sh.den[tid] = 0.f;
         __syncthreads();
         if (tid < G) {
@@ -284,33 +339,21 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
           sh.M[tid] = m;
         }
         __syncthreads();
-        constexpr int CH = 32;                // splits merged per pass
         float* scl = red;                     // [CH][G] e^(m_s - M)
         float* lsc = red + CH * G;            // [CH][G] l_s e^(m_s - M)
         static_assert(2 * CH * G <= kWaves * G * D, "the merge's scales fit the accumulator area");
-        constexpr int OPT = (G * D + kThreads - 1) / kThreads;
         float num[OPT];
 #pragma unroll
         for (int o = 0; o < OPT; ++o) num[o] = 0.f;
         for (int x0 = 0; x0 < nsg; x0 += CH) {
-          float t[OPT][CH];  // this pass's partial vectors, all loads in flight at once
-#pragma unroll
-          for (int o = 0; o < OPT; ++o) {
-            const int i = min(tid + o * kThreads, G * D - 1);
-            const int g = i / D, d = i % D;
-#pragma unroll
-            for (int u = 0; u < CH; ++u) t[o][u] = load_dev(gp + (size_t)min(x0 + u, nsg - 1) * G * PD + g * PD + d);
+          if (x0 > 0) {
+            load_pass(x0);
+            load_ml(x0, mx, lx);
           }
           if (tid < CH * G) {
-            const int x = x0 + tid / G, g = tid % G;
-            float sc = 0.f, l = 0.f;
-            if (x < nsg) {
-              const float* rec = gp + (size_t)x * G * PD + g * PD;
-              sc = expf(load_dev(rec + D) - sh.M[g]);
-              l = load_dev(rec + D + 1);
-            }
+            const float sc = mx == -INFINITY ? 0.f : expf(mx - sh.M[tid % G]);
             scl[tid] = sc;
-            lsc[tid] = l * sc;
+            lsc[tid] = lx * sc;
           }
           __syncthreads();
 #pragma unroll
