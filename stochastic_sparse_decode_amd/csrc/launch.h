@@ -17,6 +17,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;  // bounded wait: ~1 s, then error fla
 constexpr uint64_t kLaunchUnit = 1ull << 20;  // launch counter increment per launch (> any grid)
 constexpr int kLaunchCounters = 7;     // the launch count is the sum of 7 counters, one per 128-byte line
 constexpr int kLaunchStride = 16;      // uint64 words between the counters
+constexpr int kBernRecord = 291;       // 16-byte words of one group's prepared Bernoulli query
 
 // Error bits written by kernels into the workspace header.
 constexpr uint32_t kErrSpinTimeout = 1u;
@@ -40,6 +41,8 @@ struct Workspace {
   uint64_t* acc;        // [groups][G][D] exact output sums of the deterministic mode (cleared by split 0 per launch)
   uint64_t* win;        // [B][H_q][S] Gumbel-max draws: (order bits of the value, ~key) winners (cleared per call)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
+  uint4* bern;          // [groups][kBernRecord] Bernoulli step: each group's ternary (or budget) query, prepared once
+                        // per call: nu | A[8] | kept-feature list[128] | weights[128] | clipped values[128]
 };
 
 // Kernel arguments.  The fields a workgroup needs before its first K load
@@ -100,6 +103,8 @@ constexpr int kMaxBlocksPerSplit = kSplit / 16;  // smallest block: 16 keys
 int decode_capacity(int D, int G, int key_kind, int variant, int split);
 int dense_capacity(int D, int G);
 
+// Bernoulli step: prepares every group's query (one workgroup per group), then the decode kernel.
+hipError_t launch_bernoulli_prep(const DecodeParams& p, int key_kind, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int key_kind, hipStream_t stream);
 hipError_t launch_dense(const DecodeParams& p, hipStream_t stream);
 }  // namespace santa

@@ -52,9 +52,9 @@ constexpr size_t kCounterBytes = (size_t)santa::kMaxDenseGroups * sizeof(uint32_
 constexpr size_t kHeaderBytes = 1024;  // error bits, work counter, kLaunchCounters launch counters (one per 128 bytes)
 
 struct Layout {
-  size_t partial, stats, acc, win;
+  size_t partial, stats, acc, win, bern;
   size_t dense_total() const { return kHeaderBytes + kCounterBytes + partial; }
-  size_t sampling_total() const { return kHeaderBytes + kCounterBytes + stats + acc + win; }
+  size_t sampling_total() const { return kHeaderBytes + kCounterBytes + stats + acc + win + bern; }
   size_t total() const { return dense_total() > sampling_total() ? dense_total() : sampling_total(); }
 };
 
@@ -69,6 +69,7 @@ Layout layout_of(const santa_problem* p, int32_t S) {
   L.stats = round_up(groups * ns_min * G * (size_t)santa::slot_words_for(groups * ns_min * G) * sizeof(uint64_t));
   L.acc = round_up(groups * G * D * sizeof(uint64_t));
   L.win = round_up((size_t)p->batch * p->num_q_heads * (size_t)S * sizeof(uint64_t));
+  L.bern = round_up(groups * santa::kBernRecord * 16);
   return L;
 }
 
@@ -88,6 +89,7 @@ Workspace carve(void* base, const santa_problem* p, int32_t S, bool dense, uint3
     w.stats = (uint64_t*)x;
     w.acc = (uint64_t*)(x + L.stats);
     w.win = (uint64_t*)(x + L.stats + L.acc);
+    w.bern = (uint4*)(x + L.stats + L.acc + L.win);
   }
   return w;
 }
@@ -278,6 +280,11 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   }
   st = choose_grid(d, kind);
   if (st != SANTA_OK) return st;
+  if (bern) {
+    // every group's ternary (or budget) query, drawn once per call
+    const hipError_t e = santa::launch_bernoulli_prep(d, key_kind(kind), (hipStream_t)stream);
+    if (e != hipSuccess) return SANTA_ERR_HIP;
+  }
   const hipError_t e = santa::launch_decode(d, key_kind(kind), (hipStream_t)stream);
   return e == hipSuccess ? SANTA_OK : SANTA_ERR_HIP;
 }

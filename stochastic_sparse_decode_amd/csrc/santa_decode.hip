@@ -209,6 +209,75 @@ __device__ __forceinline__ void bernoulli_setup(const DecodeParams& p, int b, in
   __syncthreads();
 }
 
+// The prepared query of a group (written by bernoulli_prep earlier in the
+// same stream) into the workgroup's LDS: the union's size, the heads' scale
+// factors, the kept-feature list and the heads' weights (the budget variant:
+// and the clipped features' exact values).  Entry i of the record:
+template <bool BUDGET>
+__device__ __forceinline__ void bernoulli_put(int i, const uint4& v, Shared& sh, uint32_t* info, uint4* wt,
+                                              uint4* wt2) {
+  if (i == 0) {
+    sh.nu = (int)v.x;
+  } else if (i < 3) {
+    sh.A[(i - 1) * 4 + 0] = __uint_as_float(v.x);
+    sh.A[(i - 1) * 4 + 1] = __uint_as_float(v.y);
+    sh.A[(i - 1) * 4 + 2] = __uint_as_float(v.z);
+    sh.A[(i - 1) * 4 + 3] = __uint_as_float(v.w);
+  } else if (i < 35) {
+    info[(i - 3) * 4 + 0] = v.x;
+    info[(i - 3) * 4 + 1] = v.y;
+    info[(i - 3) * 4 + 2] = v.z;
+    info[(i - 3) * 4 + 3] = v.w;
+  } else if (i < 163) {
+    wt[i - 35] = v;
+  } else {
+    if constexpr (BUDGET) wt2[i - 163] = v;
+  }
+}
+template <bool BUDGET>
+constexpr int bern_words() { return BUDGET ? kBernRecord : 163; }
+template <bool BUDGET>
+__device__ __forceinline__ void bernoulli_load(const DecodeParams& p, int group, Shared& sh, uint32_t* info,
+                                               uint4* wt, uint4* wt2) {
+  const uint4* rec = p.ws.bern + (size_t)group * kBernRecord;
+  for (int i = threadIdx.x; i < bern_words<BUDGET>(); i += kThreads) bernoulli_put<BUDGET>(i, rec[i], sh, info, wt, wt2);
+  __syncthreads();
+}
+// Draws every group's ternary (or budget) query once per call: one workgroup
+// per (sequence, KV head) runs bernoulli_setup and stores its result as the
+// group's record (and the kept-feature masks, when asked for, of every
+// sequence); each work item of the decode kernel then loads its group's
+// record instead of drawing the query again for every split.
+template <int D, int G, bool BUDGET>
+__global__ __launch_bounds__(kThreads) void bernoulli_prep(DecodeParams p) {
+  __shared__ Shared sh;
+  __shared__ uint32_t info[128];
+  __shared__ uint4 wt[128];
+  __shared__ uint4 wt2[BUDGET ? 128 : 1];
+  const int group = blockIdx.x, b = group / p.Hkv, hk = group % p.Hkv;
+  bernoulli_setup<D, G, BUDGET>(p, b, hk, p.kept_out != nullptr, sh, info, wt, wt2);  // ends with a barrier
+  uint4* rec = p.ws.bern + (size_t)group * kBernRecord;
+  constexpr int n = BUDGET ? kBernRecord : 163;
+  auto a_of = [&](int g) -> uint32_t { return g < G ? __float_as_uint(sh.A[g]) : 0u; };
+  for (int i = threadIdx.x; i < n; i += kThreads) {
+    uint4 v;
+    if (i == 0) {
+      v = make_uint4((uint32_t)sh.nu, 0u, 0u, 0u);
+    } else if (i < 3) {
+      const int g0 = (i - 1) * 4;
+      v = make_uint4(a_of(g0), a_of(g0 + 1), a_of(g0 + 2), a_of(g0 + 3));
+    } else if (i < 35) {
+      const int j = (i - 3) * 4;  // entries past the union are never read
+      v = make_uint4(info[j], info[j + 1], info[j + 2], info[j + 3]);
+    } else if (i < 163) {
+      v = wt[i - 35];
+    } else {
+      v = BUDGET ? wt2[i - 163] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    rec[i] = v;
+  }
+}
+
 template <int D, int G, bool BUDGET>
 __device__ __forceinline__ void score_bernoulli(const DecodeParams& p, int b, int hk, int k0, int len,
                                                 float* cdf, float* mx, const Shared& sh, const uint32_t* info,
@@ -1146,7 +1215,7 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     // ---- score stage: all keys of the split, G query heads ----------------
     float mx[G];
     if constexpr (BERN) {
-      bernoulli_setup<D, G, BUDGET>(p, it.b, it.hk, p.kept_out != nullptr && it.s == 0, sh, binfo, bwt, bwt2);
+      bernoulli_load<BUDGET>(p, it.group, sh, binfo, bwt, bwt2);
       score_bernoulli<D, G, BUDGET>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt, bwt2);
     } else if constexpr (KIND == kKeyF8) {
       score_rowmajor_f8<D, G, OCC == 2 ? (G > kWaves ? 4 : 8) : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
@@ -1377,6 +1446,22 @@ hipError_t dispatch_kind(const DecodeParams& p, int key_kind, hipStream_t stream
 }
 
 }  // namespace
+
+hipError_t launch_bernoulli_prep(const DecodeParams& p, int key_kind, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.B * p.Hkv)), block(kThreads);
+#define SANTA_CASE(DD, GG)                                                                                   \
+  if (p.D == DD && p.G == GG) {                                                                             \
+    if (key_kind == kKeyBernoulliBudget)                                                                    \
+      hipLaunchKernelGGL((bernoulli_prep<DD, GG, true>), grid, block, 0, stream, p);                        \
+    else                                                                                                    \
+      hipLaunchKernelGGL((bernoulli_prep<DD, GG, false>), grid, block, 0, stream, p);                       \
+    return hipGetLastError();                                                                               \
+  }
+  SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
+  SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
+#undef SANTA_CASE
+  return hipErrorInvalidValue;
+}
 
 int decode_capacity(int D, int G, int key_kind, int variant, int split) {
   if (split == 512) return variant == kOneItemTwo ? capacity_kind<kOneItemTwo, 512>(D, G, key_kind) : 0;

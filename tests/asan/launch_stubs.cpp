@@ -9,6 +9,7 @@
 namespace santa {
 int decode_capacity(int, int, int, int, int) { return 0; }
 int dense_capacity(int, int) { return 0; }
+hipError_t launch_bernoulli_prep(const DecodeParams&, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_dense(const DecodeParams&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_pack_feature_major(const void*, void*, int, int, int, int, hipStream_t) { return hipErrorNoDevice; }
