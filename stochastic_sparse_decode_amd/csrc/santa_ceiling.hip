@@ -1,6 +1,8 @@
 // Plain streaming read of a device buffer: the bandwidth one launch draws
 // from HBM when it does nothing but read, with the 16-byte non-temporal loads
-// and the two-buffer schedule of the decode kernels' score stage.  This is a
+// and the two-buffer schedule of the decode kernels' score stage, and as many
+// bytes in flight per CU at every occupancy (16 loads per lane and buffer at
+// one workgroup per CU, 8 at two, 4 at four).  This is a
 // measurement kernel: the decode step's effective bandwidth is compared with
 // what a bare read of the same bytes reaches in one launch.
 #include "device_common.h"
@@ -10,13 +12,12 @@ namespace santa {
 
 namespace {
 
-constexpr int kReadLB = 8;  // 16-byte loads per lane per buffer (two buffers in flight)
-
 // Workgroup x reads the contiguous range [x per, (x+1) per) of 16-byte words;
 // the four waves interleave at 16-byte granularity (1 KiB per wave load).  The
 // words are folded into one XOR, which is stored only if it equals a fixed
 // value (practically never), so the loads cannot be dropped and nothing else
 // is written.
+template <int kReadLB>  // 16-byte loads per lane per buffer (two buffers in flight)
 __global__ __launch_bounds__(kThreads) void read_kernel(const uint4* buf, size_t n16, uint32_t* sink) {
   const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
   const size_t lo = (size_t)blockIdx.x * per;
@@ -56,8 +57,13 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, int workgroups_per_
   if (e != hipSuccess) return e;
   const size_t n16 = bytes / 16;
   if (n16 == 0) return hipSuccess;
-  hipLaunchKernelGGL(read_kernel, dim3((unsigned)(cus * workgroups_per_cu)), dim3(kThreads), 0, stream,
-                     (const uint4*)buf, n16, sink);
+  const dim3 grid((unsigned)(cus * workgroups_per_cu));
+  if (workgroups_per_cu <= 1)
+    hipLaunchKernelGGL(read_kernel<16>, grid, dim3(kThreads), 0, stream, (const uint4*)buf, n16, sink);
+  else if (workgroups_per_cu == 2)
+    hipLaunchKernelGGL(read_kernel<8>, grid, dim3(kThreads), 0, stream, (const uint4*)buf, n16, sink);
+  else
+    hipLaunchKernelGGL(read_kernel<4>, grid, dim3(kThreads), 0, stream, (const uint4*)buf, n16, sink);
   return hipGetLastError();
 }
 
