@@ -298,6 +298,32 @@ def test_determinism_and_workspace_reuse(llama32k):
     assert santa.santa_workspace_error(ws) == 0
 
 
+def test_launch_tags_across_variants_and_grids(llama32k):
+    """One workspace serves, in turn, launches of every sampling variant with
+    different grids: one workgroup per CU (the Llama layer), two per CU with
+    512-key splits (B = 4 at 4096 keys; B = 2, 3100 keys), and the persistent
+    variant (B = 6, up to 20480 keys).  Each launch derives its tag from the
+    workspace's launch counters and must accept no statistics slot of an
+    earlier launch: every repeat reproduces its problem's first result bit for
+    bit (deterministic mode)."""
+    wls = [llama32k,
+           W.sweep(B=4, n_k=4096, r=1.0, seed=1003),
+           persistent_case((6, 32, 8, 128, 20480, ())),
+           W.random_case(2, 8, 2, 128, [3000, 1500], max_n_k=3100, seed=2)]
+    probs = [santa.problem(torch.from_numpy(w.q), torch.from_numpy(w.K), w.scale) for w in wls]
+    nbytes = max(santa.workspace_bytes(pr) for pr in probs)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    first = [run_decode_det(w, 128, 2, 9, workspace=ws) for w in wls]
+    for _ in range(3):
+        for w, ref in zip(wls, first):
+            _same(run_decode_det(w, 128, 2, 9, workspace=ws), ref)
+    # and the first results are the oracle's draw (band rule)
+    for w, (out_g, idx_g) in zip(wls[1:], first[1:]):
+        out_o, idx_o, det = O.santa_decode(w.q, w.K, w.V, w.n_k, 128, 2, 9, w.scale, return_detail=True)
+        rep = P.compare_indices(idx_g, idx_o, det, P.BAND)
+        assert rep.bad == 0, rep
+
+
 def _one_rounding(out_g, idx_g, wl, S):
     """out equals the fp64 estimate on the GPU's own index list (an exact sum
     divided by S) after one rounding to fp32: within half an fp32 ulp of it."""
