@@ -7,7 +7,9 @@
 // offset), and only those value rows are gathered and added, divided by S,
 // which estimates softmax(qK^T)V without bias.  In the Bernoulli qK^T mode
 // the query is replaced by a stochastic ternary vector so that only the kept
-// key features are read.
+// key features are read; a preparation kernel (bernoulli_prep, below) draws
+// each group's query once per call.  (The Gumbel-max i.i.d. draws have their
+// own kernels, santa_gumbel.hip.)
 //
 // Work decomposition (one GPU, gfx950):
 //   work item = (sequence b, KV head, split of SPLIT keys).  Items of one KV
@@ -16,8 +18,8 @@
 //   the G query heads of the group from one read (GQA packing); the scores
 //   stay in LDS.  After one barrier (the split maximum of each head), wave g
 //   owns query head g for the rest of the item, with no further barriers:
-//     1. fixed-point weights of its 1024 keys, 16 consecutive keys per lane,
-//        kept in registers with their exact running sums;
+//     1. fixed-point weights of its SPLIT keys (1024, or 512), SPLIT / 64
+//        consecutive keys per lane, kept in registers with their exact sums;
 //     2. publishes the split's (max, mass) as soon as the wave scan gives the
 //        total, then polls the other splits' slots of the same head;
 //     3. merges them: global max, exact integer split offsets, normaliser;
@@ -27,11 +29,15 @@
 //        CDF;
 //     5. gathers each selected value row once, weighted by its count, and
 //        adds the split's share of the estimate to the output row with fp32
-//        device atomics (split 0 clears the row before it publishes).
+//        device atomics (split 0 clears the row before it publishes), or, in
+//        the deterministic mode, exactly in 64-bit integers that the group's
+//        last split rounds once.
 //
 // Scheduling: `grid` workgroups are all resident (grid <= occupancy capacity).
-// One item per workgroup when the items fit (OCC = 1); otherwise (OCC = 2,
-// two workgroups per CU) workgroup x takes the valid splits x, x + grid,
+// One item per workgroup when the items fit (VAR kOneItem: one workgroup per
+// CU; kOneItemTwo: two per CU, with 512-key splits when 1024-key items would
+// leave CUs idle); otherwise (kPersistent, two workgroups per CU) workgroup x
+// takes the valid splits x, x + grid,
 // x + 2 grid, ... and streams item k before it finishes item k - 1, so its
 // wait for the other splits of item k - 1 overlaps its own K stream.  A wave
 // only waits for splits of its own group, and every workgroup publishes its
@@ -542,21 +548,27 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     int group, s, b, hk, h0, nsg, k0, len;
     bool valid, active, is_last;
   };
-  auto describe = [&](int item) -> ItemCtx {
+  // The item's fields.  `first_rows` runs between the read of the sequence
+  // length and its first use: loads it issues are younger than the length's,
+  // so waiting for the length does not wait for them.
+  auto describe = [&](int item, auto&& first_rows) -> ItemCtx {
     ItemCtx it;
     it.group = item / p.ns;
     it.s = item % p.ns;
     it.b = it.group / p.Hkv;
     it.hk = it.group % p.Hkv;
     it.h0 = it.hk * G;
-    const int n = p.n_k[it.b];
+    // a scalar read (the lengths do not change during the kernel): waiting for
+    // it does not wait for vector loads issued after it
+    const int n = *(const __attribute__((address_space(4))) int32_t*)(p.n_k + it.b);
     // the counter read is issued after the length read, so waiting for the
     // length does not wait for it; it is first needed after the score stage
     if (tid < kLaunchCounters && !tagged) lc = load_dev(p.ws.launches + tid * kLaunchStride);
+    it.k0 = it.s * SPLIT;
+    first_rows(it);
     it.valid = n >= 1 && n <= p.max_n_k;
     it.nsg = it.valid ? (n + SPLIT - 1) / SPLIT : 0;
     it.active = it.valid && it.s < it.nsg;
-    it.k0 = it.s * SPLIT;
     it.len = it.active ? min(SPLIT, n - it.k0) : 0;
     it.is_last = it.s == it.nsg - 1;
     return it;
@@ -1188,7 +1200,19 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
   };
 
   // ---- stream one split, publish its statistics (all waves) -----------------
-  auto start_item = [&](const ItemCtx& it, float* scb, int wb, bool finish_now) {
+  // K loads per lane and buffer of the row-major score stages: two workgroups
+  // per CU take half (the CU still has 16 KiB per wave in flight, and the
+  // registers saved avoid spills)
+  constexpr int kRowLB = OCC == 2 ? (G > kWaves ? 4 : 8) : 16;
+  // One item per workgroup, plain fp16 cache: the query and the first K rows
+  // are requested before the sequence length has arrived (the rows are
+  // clamped to the K block, not to the length), so the stream starts one
+  // round trip earlier.
+  constexpr bool kEarlyRows = KIND == kKeyF16 && !LOOP;
+  using EarlyRows = RowScore<D, G, kRowLB, SPLIT>;
+  auto start_item = [&](const ItemCtx& it, float* scb, int wb, bool finish_now, EarlyRows& early) {
+    if constexpr (kEarlyRows)
+      if (!it.active) early.drop();
     if (!it.valid) {
       if (it.s == 0) {  // invalid sequence length: NaN output, indices -1
         for (int i = tid; i < G * D; i += kThreads) p.out[(size_t)(it.b * p.Hq + it.h0) * D + i] = __builtin_nanf("");
@@ -1218,10 +1242,8 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
       bernoulli_load<BUDGET>(p, it.group, sh, binfo, bwt, bwt2);
       score_bernoulli<D, G, BUDGET>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt, bwt2);
     } else if constexpr (KIND == kKeyF8) {
-      score_rowmajor_f8<D, G, OCC == 2 ? (G > kWaves ? 4 : 8) : 16>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+      score_rowmajor_f8<D, G, kRowLB>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     } else {
-      // two workgroups per CU: half the loads per buffer (the CU still has
-      // 16 KiB per wave in flight, and the registers saved avoid spills)
       if constexpr (PAGED) {
         // the split's block entries, checked against the pool
         const int nbl = (it.len + (1 << p.lg_block) - 1) >> p.lg_block;
@@ -1235,11 +1257,13 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
         }
         lds_barrier();
       }
-      constexpr int LB = OCC == 2 ? (G > kWaves ? 4 : 8) : 16;
       if constexpr (PAGED)
-        score_rowmajor_rows<D, G, LB>(p, it.b, it.hk, it.len, scb, mx, [&](int j) { return row_of(p.K, it, wb, j); });
+        score_rowmajor_rows<D, G, kRowLB>(p, it.b, it.hk, it.len, scb, mx,
+                                          [&](int j) { return row_of(p.K, it, wb, j); });
+      else if constexpr (kEarlyRows)
+        early.run(p, it.len, scb, mx);
       else
-        score_rowmajor<D, G, LB, SPLIT>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+        score_rowmajor<D, G, kRowLB, SPLIT>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     }
     if constexpr (BERN) {
 #pragma unroll
@@ -1287,7 +1311,11 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
   };
 
   if constexpr (!LOOP) {
-    start_item(describe(blockIdx.x), score_buf(0), 0, true);
+    EarlyRows early;
+    const ItemCtx it = describe((int)blockIdx.x, [&](const ItemCtx& c) {
+      if constexpr (kEarlyRows) early.begin(p, c.b, c.hk, c.k0, min(SPLIT, p.max_n_k - c.k0));
+    });
+    start_item(it, score_buf(0), 0, true, early);
   } else {
     // Only valid splits are items, numbered sequence by sequence: sequence b
     // has H_kv * nsg_b of them (nsg_b = ceil(n_k[b] / SPLIT) for a valid
@@ -1343,7 +1371,8 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     for (int t = blockIdx.x;; t += p.grid) {
       ItemCtx cur{};
       const bool have = find(t, cur);
-      if (have) start_item(cur, score_buf(cb), cb, false);
+      EarlyRows unused;  // (the persistent variant scores through score_rowmajor)
+      if (have) start_item(cur, score_buf(cb), cb, false, unused);
       if (prev.active)  // the previous item's statistics are published by now, or soon
         for (int g = w; g < G; g += kWaves) {
           Weights wt;

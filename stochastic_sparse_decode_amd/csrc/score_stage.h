@@ -35,59 +35,89 @@ struct Geo {
 // products of a lane reduce-scatter to exactly one (row, head) score per lane.
 // ---------------------------------------------------------------------------
 template <int D, int G, int LB = 16, int SPLIT = kSplit>
-__device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int hk, int k0, int len,
-                                               float* cdf, float* mx) {
+struct RowScore {
   using Gm = Geo<D, G, LB, SPLIT>;
-  constexpr int kPad = pad_of<SPLIT>();
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = lane / Gm::LPR, c = lane % Gm::LPR;
-  const _Float16* Kb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
-  const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
-  uint4 qv[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qb + g * D + c * 8);
-
-  const int my_u = c / G, my_g = c % G;
-  float m_run = -INFINITY;
-
+  static constexpr int kPad = pad_of<SPLIT>();
   // A split is always streamed in NIT = SPLIT / ROWS_IT fully unrolled
   // iterations with two register buffers: the loads of iteration i+1 are in
   // flight while iteration i is reduced.  Loads are unconditional (rows past
   // the split's end re-read its last row, an L1 hit) so that the compiler
   // counts outstanding loads exactly and never waits for the prefetch.
-  constexpr int NIT = SPLIT / Gm::ROWS_IT;
+  static constexpr int NIT = SPLIT / Gm::ROWS_IT;
   uint4 buf[2][Gm::NB][Gm::U];
-  auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
+  uint4 qv[G];
+  const _Float16* Kb;
+  int lane, w, r, c;
+
+  __device__ __forceinline__ void issue(int slot, int base, int lim) {
 #pragma unroll
     for (int nb = 0; nb < Gm::NB; ++nb)
 #pragma unroll
       for (int u = 0; u < Gm::U; ++u) {
-        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, len - 1);
-        bb[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 8));
+        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, lim - 1);
+        buf[slot][nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 8));
       }
-  };
-  issue(buf[0], 0);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int base = it * Gm::ROWS_IT;
-    if (it + 1 < NIT) issue(buf[(it + 1) & 1], base + Gm::ROWS_IT);
-#pragma unroll
-    for (int nb = 0; nb < Gm::NB; ++nb) {
-      float v[Gm::LPR];
-#pragma unroll
-      for (int u = 0; u < Gm::U; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g) v[u * G + g] = dot8(buf[it & 1][nb][u], qv[g]);
-      row_reduce_scatter<Gm::LPR>(v, lane);
-      // rows < SPLIT always; rows >= len land in unused LDS slots
-      const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
-      const float s = v[0] * p.scale;
-      cdf[my_g * kPad + lidx(row)] = s;
-      m_run = fmaxf(m_run, row < len ? s : -INFINITY);
-    }
   }
+  // The query and the first iteration's rows, clamped to the first `lim`
+  // rows of the split.  lim may exceed the split's valid length, up to the
+  // rows the K block holds (max_n_k - k0): the first loads can then go out
+  // before the sequence length has arrived; rows past the length are scored
+  // into LDS slots nothing reads and are left out of the maximum.
+  __device__ __forceinline__ void begin(const DecodeParams& p, int b, int hk, int k0, int lim) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    w = tid >> 6;
+    r = lane / Gm::LPR;
+    c = lane % Gm::LPR;
+    Kb = (const _Float16*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
+    const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
 #pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+    for (int g = 0; g < G; ++g) qv[g] = *(const uint4*)(qb + g * D + c * 8);
+    issue(0, 0, lim);
+  }
+  // For an item found to have nothing to score after begin(): the first
+  // rows are taken as used (and waited for) on that path only, so that the
+  // compiler issues them before it tests the item, not after.
+  __device__ __forceinline__ void drop() {
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb)
+#pragma unroll
+      for (int u = 0; u < Gm::U; ++u) asm volatile("" ::"v"(buf[0][nb][u].x));
+  }
+  // The rest of the stage for a split of `len` valid keys.
+  __device__ __forceinline__ void run(const DecodeParams& p, int len, float* cdf, float* mx) {
+    const int my_u = c / G, my_g = c % G;
+    float m_run = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int base = it * Gm::ROWS_IT;
+      if (it + 1 < NIT) issue((it + 1) & 1, base + Gm::ROWS_IT, len);
+#pragma unroll
+      for (int nb = 0; nb < Gm::NB; ++nb) {
+        float v[Gm::LPR];
+#pragma unroll
+        for (int u = 0; u < Gm::U; ++u)
+#pragma unroll
+          for (int g = 0; g < G; ++g) v[u * G + g] = dot8(buf[it & 1][nb][u], qv[g]);
+        row_reduce_scatter<Gm::LPR>(v, lane);
+        // rows < SPLIT always; rows >= len land in unused LDS slots
+        const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
+        const float sc = v[0] * p.scale;
+        cdf[my_g * kPad + lidx(row)] = sc;
+        m_run = fmaxf(m_run, row < len ? sc : -INFINITY);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+  }
+};
+
+template <int D, int G, int LB = 16, int SPLIT = kSplit>
+__device__ __forceinline__ void score_rowmajor(const DecodeParams& p, int b, int hk, int k0, int len,
+                                               float* cdf, float* mx) {
+  RowScore<D, G, LB, SPLIT> rs;
+  rs.begin(p, b, hk, k0, len);
+  rs.run(p, len, cdf, mx);
 }
 
 // The same stage for a paged (block table) cache: row_ptr(j) points at key
