@@ -45,6 +45,8 @@
 // one, so the waits always end as long as a group has no more splits than
 // there are workgroups.  Every wait is bounded (kSpinLimit polls); a timeout
 // sets an error bit instead of hanging.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "score_stage.h"
@@ -533,8 +535,12 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
     const int32_t* nk_ptr = p.n_k;
     const void* v_ptr = p.V;
     const uint32_t* err_ptr = p.ws.err;
+    const void* q_ptr = p.q;
+    const uint64_t* lc_ptr = p.ws.launches;
+    const float* ks_ptr = p.k_scale;
     const int ns_ = p.ns, mnk = p.max_n_k, hkv = p.Hkv, items = p.total_items;
-    asm volatile("" ::"s"(k_ptr), "s"(nk_ptr), "s"(v_ptr), "s"(err_ptr), "s"(ns_), "s"(mnk), "s"(hkv), "s"(items));
+    asm volatile("" ::"s"(k_ptr), "s"(nk_ptr), "s"(q_ptr), "s"(v_ptr), "s"(err_ptr), "s"(lc_ptr), "s"(ks_ptr), "s"(ns_),
+                 "s"(mnk), "s"(hkv), "s"(items));
   }
   auto tag_of = [](uint64_t c) -> uint32_t {
     const uint32_t t = (uint32_t)(c / kLaunchUnit) + 1u;
@@ -1204,12 +1210,13 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
   // per CU take half (the CU still has 16 KiB per wave in flight, and the
   // registers saved avoid spills)
   constexpr int kRowLB = OCC == 2 ? (G > kWaves ? 4 : 8) : 16;
-  // One item per workgroup, plain fp16 cache: the query and the first K rows
-  // are requested before the sequence length has arrived (the rows are
-  // clamped to the K block, not to the length), so the stream starts one
-  // round trip earlier.
-  constexpr bool kEarlyRows = KIND == kKeyF16 && !LOOP;
-  using EarlyRows = RowScore<D, G, kRowLB, SPLIT>;
+  // One item per workgroup, fp16 or fp8 row-major cache: the query and the
+  // first K rows are requested before the sequence length has arrived (the
+  // rows are clamped to the K block, not to the length), so the stream
+  // starts one round trip earlier.
+  constexpr bool kEarlyRows = (KIND == kKeyF16 || (KIND == kKeyF8 && fp8_supported<D, G>())) && !LOOP;
+  using EarlyRows = typename std::conditional<KIND == kKeyF8, RowScoreF8<D, G, kRowLB, SPLIT>,
+                                              RowScore<D, G, kRowLB, SPLIT>>::type;
   auto start_item = [&](const ItemCtx& it, float* scb, int wb, bool finish_now, EarlyRows& early) {
     if constexpr (kEarlyRows)
       if (!it.active) early.drop();
@@ -1242,7 +1249,10 @@ __global__ __launch_bounds__(kThreads, VAR == kOneItem ? 1 : 2) void decode_kern
       bernoulli_load<BUDGET>(p, it.group, sh, binfo, bwt, bwt2);
       score_bernoulli<D, G, BUDGET>(p, it.b, it.hk, it.k0, it.len, scb, mx, sh, binfo, bwt, bwt2);
     } else if constexpr (KIND == kKeyF8) {
-      score_rowmajor_f8<D, G, kRowLB>(p, it.b, it.hk, it.k0, it.len, scb, mx);
+      if constexpr (kEarlyRows)
+        early.run(p, it.len, scb, mx);
+      else
+        score_rowmajor_f8<D, G, kRowLB>(p, it.b, it.hk, it.k0, it.len, scb, mx);
     } else {
       if constexpr (PAGED) {
         // the split's block entries, checked against the pool

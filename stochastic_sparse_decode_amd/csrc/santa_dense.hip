@@ -81,6 +81,49 @@ __device__ __forceinline__ float row_sum_mod(float v) {
   return v + dpp_row_ror<0x128>(v);
 }
 
+// K and V rows of one iteration of split_pass: NB blocks of U 16-byte loads
+// each, per lane.
+template <int D, int G>
+struct DenseBuf {
+  using Gm = Geo<D, G>;
+  static constexpr int NB = 2;  // blocks per register buffer
+  uint4 k[NB][Gm::U], v[NB][Gm::U];
+};
+
+// Requests the K and V rows of iteration `base` of the split at k0 of KV
+// head (b, hk), rows clamped to the first `lim` of the split.  The first
+// iteration is requested with lim = the rows the K block holds past k0,
+// before the sequence length has arrived; rows past the length get weight 0.
+template <int D, int G>
+__device__ __forceinline__ void dense_issue(const DecodeParams& p, int b, int hk, int k0, DenseBuf<D, G>& bf,
+                                            int base, int lim) {
+  using Gm = Geo<D, G>;
+  constexpr int LPR = Gm::LPR, RPW = Gm::RPW, U = Gm::U, BR = Gm::BR, NB = DenseBuf<D, G>::NB;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane / LPR, c = lane % LPR;
+  const size_t base_row = (size_t)(b * p.Hkv + hk) * p.max_n_k + k0;
+  const _Float16* Kb = (const _Float16*)p.K + base_row * D;
+  const _Float16* Vb = (const _Float16*)p.V + base_row * D;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(base + (nb * kWaves + w) * BR + u * RPW + r, lim - 1);
+      bf.k[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 8));
+      bf.v[nb][u] = load_nt((const uint4*)(Vb + (size_t)row * D + c * 8));
+    }
+}
+
+// The first iteration's rows taken as used (and waited for) on a path that
+// scores nothing, so that the compiler requests them before it tests the item.
+template <int D, int G>
+__device__ __forceinline__ void dense_drop(const DenseBuf<D, G>& bf) {
+#pragma unroll
+  for (int nb = 0; nb < DenseBuf<D, G>::NB; ++nb)
+#pragma unroll
+    for (int u = 0; u < Geo<D, G>::U; ++u) asm volatile("" ::"v"(bf.k[nb][u].x), "v"(bf.v[nb][u].x));
+}
+
 // One pass over a split of `len` keys of KV head (b, hk): every wave takes
 // blocks of BR consecutive rows (the waves interleave block by block),
 // streams their K and V rows together with 16-byte loads (two register
@@ -91,10 +134,10 @@ __device__ __forceinline__ float row_sum_mod(float v) {
 // combined through LDS into the split's record (acc[D], m, l per head).
 template <int D, int G>
 __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk, int k0, int len, float* red,
-                                           DenseShared& sh, float* rec) {
+                                           DenseShared& sh, float* rec, const DenseBuf<D, G>& first) {
   using Gm = Geo<D, G>;
   constexpr int LPR = Gm::LPR, RPW = Gm::RPW, U = Gm::U, BR = Gm::BR;
-  constexpr int NB = 2;                        // blocks per register buffer
+  constexpr int NB = DenseBuf<D, G>::NB;       // blocks per register buffer
   constexpr int STEP = NB * kWaves * BR;       // rows per iteration of the workgroup
   constexpr int PD = D + 2;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -116,21 +159,10 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
   }
-  struct Buf {
-    uint4 k[NB][U], v[NB][U];
-  };
+  using Buf = DenseBuf<D, G>;
   // rows past the split's end re-read its last row and score -inf (weight 0),
   // so the loads are unconditional and the compiler counts them exactly
-  auto issue = [&](Buf& bf, int base) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = min(base + (nb * kWaves + w) * BR + u * RPW + r, len - 1);
-        bf.k[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 8));
-        bf.v[nb][u] = load_nt((const uint4*)(Vb + (size_t)row * D + c * 8));
-      }
-  };
+  auto issue = [&](Buf& bf, int base) { dense_issue<D, G>(p, b, hk, k0, bf, base, len); };
   auto consume = [&](const Buf& bf, int base) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -171,6 +203,7 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
       float f[U][8];
 #pragma unroll
       for (int u = 0; u < U; ++u) unpack8(bf.v[nb][u], f[u]);
+
       static_for<LPR>([&](auto jc) {
         constexpr int J = decltype(jc)::value, u = J / G, g = J % G;
         const float wt = row_lane<LPR, J>(pw, lane);
@@ -179,8 +212,12 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
       });
     }
   };
-  Buf b0, b1;
-  issue(b0, 0);
+  // The first iteration's rows were requested by the caller, clamped to the
+  // K block.  A split shorter than one iteration then holds rows past its end
+  // whose values are not ours to multiply (0 * NaN is NaN): its first rows
+  // are requested again, clamped to the split.
+  Buf b0 = first, b1;
+  if (len < STEP) issue(b0, 0);
   for (int base = 0; base < len; base += 2 * STEP) {
     issue(b1, base + STEP);
     consume(b0, base);
@@ -276,17 +313,25 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
   while (item < p.total_items) {
     const int group = item / p.ns, s = item % p.ns;
     const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
-    const int n = p.n_k[b];
+    // the length is a scalar read (it does not change during the kernel), and
+    // the split's first K and V rows are requested before it is used: they
+    // need only the item's place and the K block's row count
+    const int n = *(const __attribute__((address_space(4))) int32_t*)(p.n_k + b);
+    const int k0 = s * p.split;
+    DenseBuf<D, G> first;
+    dense_issue<D, G>(p, b, hk, k0, first, 0, min(p.split, p.max_n_k - k0));
     const bool valid = n >= 1 && n <= p.max_n_k;
     const int nsg = valid ? (n + p.split - 1) / p.split : 0;
 
     if (!valid) {
+      dense_drop<D, G>(first);
       if (s == 0)
         for (int i = tid; i < G * D; i += kThreads) p.out[(size_t)(b * p.Hq + h0) * D + i] = __builtin_nanf("");
-    } else if (s < nsg) {
-      const int k0 = s * p.split;
+    } else if (s >= nsg) {
+      dense_drop<D, G>(first);
+    } else {
       const int len = min(p.split, n - k0);
-      split_pass<D, G>(p, b, hk, k0, len, red, sh, p.ws.partial + (size_t)(group * p.ns + s) * G * PD);
+      split_pass<D, G>(p, b, hk, k0, len, red, sh, p.ws.partial + (size_t)(group * p.ns + s) * G * PD, first);
       wait_memory();
       __syncthreads();
       // arrival counter of the group (zero at rest: the last arrival resets it)

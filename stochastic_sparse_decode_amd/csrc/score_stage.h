@@ -202,72 +202,97 @@ template <int D, int G>
 constexpr bool fp8_supported() { return G <= D / 16; }
 
 template <int D, int G, int LB = 16, int SPLIT = kSplit>
-__device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, int hk, int k0, int len,
-                                                  float* cdf, float* mx) {
+struct RowScoreF8 {
   using Gm = GeoF8<D, G, LB, SPLIT>;
-  constexpr int kPad = pad_of<SPLIT>();
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = lane / Gm::LPR, c = lane % Gm::LPR;
-  const uint8_t* Kb = (const uint8_t*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
-  const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
-  uint4 qv[G][2];  // features c*16 .. c*16+15 of each head, as fp16 pairs
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    qv[g][0] = *(const uint4*)(qb + g * D + c * 16);
-    qv[g][1] = *(const uint4*)(qb + g * D + c * 16 + 8);
-  }
-  const float sc = p.scale * p.k_scale[b * p.Hkv + hk];
-
-  const int my_u = c / G, my_g = c % G;
-  float m_run = -INFINITY;
-  constexpr int NIT = SPLIT / Gm::ROWS_IT;
+  static constexpr int kPad = pad_of<SPLIT>();
+  static constexpr int NIT = SPLIT / Gm::ROWS_IT;
   uint4 buf[2][Gm::NB][Gm::U];
-  auto issue = [&](uint4 (&bb)[Gm::NB][Gm::U], int base) {
+  uint4 qv[G][2];  // features c*16 .. c*16+15 of each head, as fp16 pairs
+  const uint8_t* Kb;
+  float sc;
+  int lane, w, r, c;
+
+  __device__ __forceinline__ void issue(int slot, int base, int lim) {
 #pragma unroll
     for (int nb = 0; nb < Gm::NB; ++nb)
 #pragma unroll
       for (int u = 0; u < Gm::U; ++u) {
-        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, len - 1);
-        bb[nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 16));
+        const int row = min(base + (nb * kWaves + w) * Gm::BR + u * Gm::RPW + r, lim - 1);
+        buf[slot][nb][u] = load_nt((const uint4*)(Kb + (size_t)row * D + c * 16));
       }
-  };
-  issue(buf[0], 0);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int base = it * Gm::ROWS_IT;
-    if (it + 1 < NIT) issue(buf[(it + 1) & 1], base + Gm::ROWS_IT);
-#pragma unroll
-    for (int nb = 0; nb < Gm::NB; ++nb) {
-      float v[Gm::LPR];
-#pragma unroll
-      for (int u = 0; u < Gm::U; ++u) {
-        // fp16 pairs of features (2m, 2m+1) of the lane's 16
-        uint32_t kh[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t wd = word_of(buf[it & 1][nb][u], i);
-          kh[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.0f, false));
-          kh[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.0f, true));
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < 8; ++m)
-            acc = __builtin_amdgcn_fdot2(as_h2(kh[m]), as_h2(word_of(qv[g][m >> 2], m & 3)), acc, false);
-          v[u * G + g] = acc;
-        }
-      }
-      row_reduce_scatter<Gm::LPR>(v, lane);
-      // rows < SPLIT always; rows >= len land in unused LDS slots
-      const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
-      const float s = v[0] * sc;
-      cdf[my_g * kPad + lidx(row)] = s;
-      m_run = fmaxf(m_run, row < len ? s : -INFINITY);
-    }
   }
+  // The query, the key scale and the first iteration's rows, clamped to the
+  // first `lim` rows of the split (as RowScore::begin).
+  __device__ __forceinline__ void begin(const DecodeParams& p, int b, int hk, int k0, int lim) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    w = tid >> 6;
+    r = lane / Gm::LPR;
+    c = lane % Gm::LPR;
+    Kb = (const uint8_t*)p.K + ((size_t)(b * p.Hkv + hk) * p.max_n_k + k0) * D;
+    const _Float16* qb = (const _Float16*)p.q + (size_t)(b * p.Hq + hk * G) * D;
 #pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+    for (int g = 0; g < G; ++g) {
+      qv[g][0] = *(const uint4*)(qb + g * D + c * 16);
+      qv[g][1] = *(const uint4*)(qb + g * D + c * 16 + 8);
+    }
+    sc = p.scale * p.k_scale[b * p.Hkv + hk];
+    issue(0, 0, lim);
+  }
+  __device__ __forceinline__ void drop() {
+#pragma unroll
+    for (int nb = 0; nb < Gm::NB; ++nb)
+#pragma unroll
+      for (int u = 0; u < Gm::U; ++u) asm volatile("" ::"v"(buf[0][nb][u].x));
+  }
+  __device__ __forceinline__ void run(const DecodeParams& p, int len, float* cdf, float* mx) {
+    const int my_u = c / G, my_g = c % G;
+    float m_run = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int base = it * Gm::ROWS_IT;
+      if (it + 1 < NIT) issue((it + 1) & 1, base + Gm::ROWS_IT, len);
+#pragma unroll
+      for (int nb = 0; nb < Gm::NB; ++nb) {
+        float v[Gm::LPR];
+#pragma unroll
+        for (int u = 0; u < Gm::U; ++u) {
+          // fp16 pairs of features (2m, 2m+1) of the lane's 16
+          uint32_t kh[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t wd = word_of(buf[it & 1][nb][u], i);
+            kh[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.0f, false));
+            kh[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, 1.0f, true));
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+              acc = __builtin_amdgcn_fdot2(as_h2(kh[m]), as_h2(word_of(qv[g][m >> 2], m & 3)), acc, false);
+            v[u * G + g] = acc;
+          }
+        }
+        row_reduce_scatter<Gm::LPR>(v, lane);
+        // rows < SPLIT always; rows >= len land in unused LDS slots
+        const int row = base + (nb * kWaves + w) * Gm::BR + my_u * Gm::RPW + r;
+        const float s = v[0] * sc;
+        cdf[my_g * kPad + lidx(row)] = s;
+        m_run = fmaxf(m_run, row < len ? s : -INFINITY);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) mx[g] = (g == my_g) ? m_run : -INFINITY;
+  }
+};
+
+template <int D, int G, int LB = 16, int SPLIT = kSplit>
+__device__ __forceinline__ void score_rowmajor_f8(const DecodeParams& p, int b, int hk, int k0, int len,
+                                                  float* cdf, float* mx) {
+  RowScoreF8<D, G, LB, SPLIT> rs;
+  rs.begin(p, b, hk, k0, len);
+  rs.run(p, len, cdf, mx);
 }
 
 // Copy the split's scores from LDS to scores_out (debug output), coalesced.
