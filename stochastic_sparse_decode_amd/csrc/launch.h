@@ -30,17 +30,23 @@ constexpr uint32_t kErrBlockTable = 2u;  // a block-table entry out of range (re
 // problem ever overlaps; statistics slots carry the launch's tag and partial
 // records are written before they are read, so a buffer can serve problems of
 // different sizes.
+// Dense kernel: splits per group up to which the resident grid merges by
+// exchange (each split merges F / ns of the group's G * D features).
+constexpr int kMaxExchSplits = 128;
 constexpr int kMaxDenseGroups = 16384;  // B * H_kv of a dense step (its counters fill 64 KiB)
 struct Workspace {
   uint32_t* err;        // error bits (never cleared by kernels)
   uint32_t* work_ctr;   // dense kernel: dynamic work-item counter, returns to 0 at kernel end
-  uint64_t* launches;   // launch counters of the sampling kernel (their sum grows by kLaunchUnit per launch)
+  uint64_t* launches;   // launch counters of the tagged launches, sampling and dense (their sum grows by
+                        // kLaunchUnit per launch)
   uint32_t* arrive;     // [groups] dense kernel: splits of the group that stored their record, back to 0
   uint64_t* stats;      // [groups][G][ns][2] (tag:32 | split max bits, tag:32 | split mass bits); sized for
                         // splits of kMinSplit keys
   uint64_t* acc;        // [groups][G][D] exact output sums of the deterministic mode (cleared by split 0 per launch)
   uint64_t* win;        // [B][H_q][S] Gumbel-max draws: (order bits of the value, ~key) winners (cleared per call)
   float* partial;       // [groups][ns][G][D + 2] partial outputs of the dense kernel (acc, m, l)
+  uint64_t* xrec;       // the same memory as [groups][ns][G][D + 2] words (tag:32 | value bits): the dense
+                        // kernel's records when its splits merge each other's (exch = 1)
   uint4* bern;          // [groups][kBernRecord] Bernoulli step: each group's ternary (or budget) query, prepared once
                         // per call: nu | A[8] | kept-feature list[128] | weights[128] | clipped values[128]
 };
@@ -81,6 +87,8 @@ struct DecodeParams {
   int split;            // keys per work item of the sampling kernel: kSplit, or 512 (variant 3, plain fp16 cache)
   int det;              // 1: out is the exact sum of the gathered rows rounded once (bit-reproducible)
   int slot_words;       // 8-byte words per statistics slot: 2, or 16 (one slot per 128-byte line)
+  int exch;             // dense kernel: 1 = every item has its own resident workgroup, and the splits of a
+                        // group exchange tagged records and each merges a share of the features
   Workspace ws;
 };
 static_assert(offsetof(DecodeParams, V) == 64, "the fields read first fill one 64-byte line");

@@ -36,15 +36,17 @@ bool supported(const santa_problem* p) {
   return (p->head_dim == 64 || p->head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
-// Workspace layout: a 256-byte header (error bits, the dense kernel's work
-// counter, the launch counter), a 64 KiB region of the dense kernel's arrival
+// Workspace layout: a 1 KiB header (error bits, the dense kernel's work
+// counter, the launch counters), a 64 KiB region of the dense kernel's arrival
 // counters, then the data of the kernel that runs: the dense kernel's partial
-// records, or the sampling kernel's statistics slots and the exact output sums
-// of the deterministic mode.  The header's work counter and the arrival
+// records (floats, or tagged 8-byte words when its splits exchange them), or
+// the sampling kernel's statistics slots and the exact output sums of the
+// deterministic mode.  The header's work counter and the arrival
 // counters must be zero when a launch starts (every dense launch leaves them at
 // zero; the caller zero-fills a new buffer), and no data region of any problem
 // overlaps them, since the data regions start after the fixed-size counter
-// region.  Slots carry a launch tag, and partial records and exact sums are
+// region.  Slots and exchanged records carry a launch tag, and float partial
+// records and exact sums are
 // written (or cleared) before they are read in every launch, so calls of
 // either kind and of different sizes may share a buffer even though their data
 // regions overlap.
@@ -65,7 +67,7 @@ Layout layout_of(const santa_problem* p, int32_t S) {
   const size_t groups = (size_t)p->batch * p->num_kv_heads;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
   const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
-  L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(float));
+  L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(uint64_t));  // tagged words at either split
   L.stats = round_up(groups * ns_min * G * (size_t)santa::slot_words_for(groups * ns_min * G) * sizeof(uint64_t));
   L.acc = round_up(groups * G * D * sizeof(uint64_t));
   L.win = round_up((size_t)p->batch * p->num_q_heads * (size_t)S * sizeof(uint64_t));
@@ -85,6 +87,7 @@ Workspace carve(void* base, const santa_problem* p, int32_t S, bool dense, uint3
   unsigned char* x = b + kHeaderBytes + kCounterBytes;
   if (dense) {
     w.partial = (float*)x;
+    w.xrec = (uint64_t*)x;
   } else {
     w.stats = (uint64_t*)x;
     w.acc = (uint64_t*)(x + L.stats);
@@ -217,6 +220,9 @@ int choose_grid(DecodeParams& d, int kind) {
     const long long items = groups * ((d.max_n_k + santa::kMinSplit - 1) / santa::kMinSplit);
     if (d.total_items < cu_count() && items <= cap) set_split(santa::kMinSplit);
     d.grid = d.total_items < cap ? d.total_items : cap;
+    // every item resident at once: the splits of a group merge each other's
+    // records (no last-arrival merge)
+    d.exch = d.grid == d.total_items && d.ns <= santa::kMaxExchSplits ? 1 : 0;
     return SANTA_OK;
   }
   if (kind == santa::kOpDecode && d.total_items < cu_count()) {

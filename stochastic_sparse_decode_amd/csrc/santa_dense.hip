@@ -5,11 +5,18 @@
 // KV head, split of kSplit or kMinSplit keys) streams the split's K and V rows together in
 // one pass, scoring its keys for the G packed query heads (the SANTA kernel's
 // reduce-scatter) and keeping a running maximum, sum p and sum p * v per head
-// (online softmax); the last workgroup of a KV head to finish merges the
-// per-split (max, sum, vector) triples in split order:
+// (online softmax).  The per-split (max, sum, vector) triples merge in split
+// order:
 //   out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s.
-// Scheduling: persistent workgroups take items from an atomic work counter;
-// there is no cross-workgroup wait in this kernel.
+// Two schedules:
+//  - every item resident at once (one workgroup each): the splits of a KV
+//    head store their triples as tagged words and each split merges a 1/ns
+//    share of the head group's features from all of them (a bounded wait on
+//    the other splits' records, which are all being computed);
+//  - else persistent workgroups take items from an atomic work counter, and
+//    the last split of a KV head to finish merges every triple (no
+//    cross-workgroup wait).
+#include <algorithm>
 #include <utility>
 
 #include "device_common.h"
@@ -32,6 +39,7 @@ struct DenseShared {
   float den[8];
   int last;
   int next_item;
+  uint32_t epoch;  // launch tag (exchange merge)
 };
 
 
@@ -130,16 +138,16 @@ __device__ __forceinline__ void dense_drop(const DenseBuf<D, G>& bf) {
 // buffers of NB blocks in flight), scores the G query heads of the group (the
 // SANTA score stage's reduce-scatter leaves one (row, head) score per lane),
 // keeps a running maximum and sum per head (online softmax) and adds
-// exp(s - m) * v into per-head accumulators.  The four waves' states are
-// combined through LDS into the split's record (acc[D], m, l per head).
+// exp(s - m) * v into per-head accumulators.  Each wave leaves its state in
+// LDS (accumulators in red, maximum and sum per head in sh); finish_split
+// combines the four.
 template <int D, int G>
 __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk, int k0, int len, float* red,
-                                           DenseShared& sh, float* rec, const DenseBuf<D, G>& first) {
+                                           DenseShared& sh, const DenseBuf<D, G>& first) {
   using Gm = Geo<D, G>;
   constexpr int LPR = Gm::LPR, RPW = Gm::RPW, U = Gm::U, BR = Gm::BR;
   constexpr int NB = DenseBuf<D, G>::NB;       // blocks per register buffer
   constexpr int STEP = NB * kWaves * BR;       // rows per iteration of the workgroup
-  constexpr int PD = D + 2;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane / LPR, c = lane % LPR;
   const int my_u = c / G, my_g = c % G;       // this lane's score: row my_u * RPW + r of a block, head my_g
@@ -270,7 +278,42 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
       if (lane == g) sh.wmax[w][lane] = m[g];
     sh.wsum[w][lane] = lw;  // lane g holds head g (lanes congruent to g modulo G)
   }
-  __syncthreads();
+}
+
+// Where a split's combined state goes.
+enum Finish { kFloatRecord = 0, kTaggedRecord = 1, kOutput = 2 };
+
+// After split_pass and a barrier: the four waves' states combine into the
+// split's maximum M, sum l and vector acc per head, written as a float record
+// (acc[D], M, l per head), as the same record in tagged words (tag:32 | value
+// bits), or, when the split is its group's only one, as the output acc / l.
+template <int D, int G>
+__device__ __forceinline__ void finish_split(const float* red, DenseShared& sh, int how, float* rec, uint64_t* xr,
+                                             uint32_t tag, float* outp) {
+  constexpr int PD = D + 2;
+  const int tid = threadIdx.x;
+  const uint64_t t = (uint64_t)tag << 32;
+  if (tid < G) {
+    float M = sh.wmax[0][tid];
+#pragma unroll
+    for (int x = 1; x < kWaves; ++x) M = fmaxf(M, sh.wmax[x][tid]);
+    float lt = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) {
+      const float mx = sh.wmax[x][tid];
+      lt += mx == -INFINITY ? 0.f : sh.wsum[x][tid] * __expf(mx - M);
+    }
+    if (how == kFloatRecord) {
+      store_dev(rec + tid * PD + D, M);
+      store_dev(rec + tid * PD + D + 1, lt);
+    } else if (how == kTaggedRecord) {
+      store_dev(xr + tid * PD + D, t | __float_as_uint(M));
+      store_dev(xr + tid * PD + D + 1, t | __float_as_uint(lt));
+    } else {
+      sh.den[tid] = lt;
+    }
+  }
+  if (how == kOutput) __syncthreads();
   for (int i = tid; i < G * D; i += kThreads) {
     const int g = i / D, d = i % D;
     float M = sh.wmax[0][g];
@@ -282,37 +325,165 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
       const float mx = sh.wmax[x][g];
       v += mx == -INFINITY ? 0.f : red[(x * G + g) * D + d] * __expf(mx - M);
     }
-    store_dev(rec + g * PD + d, v);
-  }
-  if (tid < G) {
-    float M = sh.wmax[0][tid];
-#pragma unroll
-    for (int x = 1; x < kWaves; ++x) M = fmaxf(M, sh.wmax[x][tid]);
-    float lt = 0.f;
-#pragma unroll
-    for (int x = 0; x < kWaves; ++x) {
-      const float mx = sh.wmax[x][tid];
-      lt += mx == -INFINITY ? 0.f : sh.wsum[x][tid] * __expf(mx - M);
-    }
-    store_dev(rec + tid * PD + D, M);
-    store_dev(rec + tid * PD + D + 1, lt);
+    if (how == kFloatRecord) store_dev(rec + g * PD + d, v);
+    else if (how == kTaggedRecord) store_dev(xr + g * PD + d, t | __float_as_uint(v));
+    else outp[i] = v / sh.den[g];
   }
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Merge by exchange, for split s of a group of nsg > 1 splits whose
+// workgroups are all resident: split s produces features [f0, f1) of the
+// group's F = G * D outputs (head f / D, feature f mod D) from every split's
+// tagged record,
+//   out_f = sum_x e^(m_x - M) acc_x,f / sum_x e^(m_x - M) l_x  (x in split order).
+// Every split stores its record before it reads, so every wait ends; a wait
+// is bounded regardless (kSpinLimit rounds, then an error bit).  A word is
+// accepted only with this launch's tag; a thread re-reads only the words it
+// has not yet seen.
 template <int D, int G>
+__device__ __forceinline__ void exchange_merge(const DecodeParams& p, const uint64_t* grec, int s, int nsg,
+                                               uint32_t tag, float* vals, float2* xml, float* scl, float* den,
+                                               float* outp) {
+  constexpr int F = G * D, PD = D + 2, RW = G * PD;  // 8-byte words per split record
+  constexpr int NV = (F + kMaxExchSplits + kThreads - 1) / kThreads;  // value words per thread
+  static_assert(2 * kMaxExchSplits <= kThreads, "one (m, l) pair per thread");
+  static_assert(kMaxExchSplits <= 3 * 64, "the values fit the accumulator area");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int f0 = s * F / nsg, f1 = (s + 1) * F / nsg, chunk = f1 - f0;
+  if (chunk == 0) return;
+  const int g0 = f0 / D, nh = (f1 - 1) / D - g0 + 1;
+  const int nv = nsg * chunk, nm = nsg * nh;  // value words; (m, l) pairs (nm <= 2 nsg, or <= G * G)
+  uint64_t vw[NV];
+  bool vs[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    vw[k] = 0ull;
+    vs[k] = tid + k * kThreads >= nv;
+  }
+  u32x4 mw = u32x4{0u, 0u, 0u, 0u};
+  bool ms = tid >= nm;
+  auto issue = [&]() {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (!vs[k]) {
+        const int idx = tid + k * kThreads, x = idx / chunk, f = f0 + idx % chunk;
+        vw[k] = load_dev(grec + (size_t)x * RW + (f / D) * PD + f % D);
+      }
+    }
+    if (!ms) {
+      const int x = tid / nh, g = g0 + tid % nh;
+      mw = load_dev16(grec + (size_t)x * RW + g * PD + D);
+    }
+  };
+  auto test = [&]() -> bool {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      vs[k] = vs[k] || (uint32_t)(vw[k] >> 32) == tag;
+      all = all && vs[k];
+    }
+    ms = ms || (mw.y == tag && mw.w == tag);
+    return __ballot(!(all && ms)) == 0ull;
+  };
+  issue();
+  if (!test()) {
+    uint32_t spins = 0;
+    while (true) {
+      __builtin_amdgcn_s_sleep(4);
+      if (++spins > kSpinLimit) {
+        if (lane == 0) atomicOr(p.ws.err, kErrSpinTimeout);
+        break;
+      }
+      issue();
+      if (test()) break;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    if (tid + k * kThreads < nv) vals[tid + k * kThreads] = __uint_as_float((uint32_t)vw[k]);
+  if (tid < nm) xml[tid] = make_float2(__uint_as_float(mw.x), __uint_as_float(mw.z));
+  __syncthreads();
+  // per head: the maximum over the splits, each split's scale e^(m_x - M) and
+  // the denominator (lanes hold splits lane and lane + 64)
+  for (int gi = w; gi < nh; gi += kWaves) {
+    float mx[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int x = lane + 64 * c;
+      mx[c] = x < nsg ? xml[x * nh + gi].x : -INFINITY;
+    }
+    const float M = wave_max(fmaxf(mx[0], mx[1]));
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int x = lane + 64 * c;
+      if (x < nsg) {
+        const float sc = mx[c] == -INFINITY ? 0.f : expf(mx[c] - M);
+        scl[x * nh + gi] = sc;
+        part = fmaf(xml[x * nh + gi].y, sc, part);
+      }
+    }
+    const float dsum = wave_sum(part);
+    if (lane == 0) den[gi] = dsum;
+  }
+  __syncthreads();
+  for (int fo = tid; fo < chunk; fo += kThreads) {
+    const int gi = (f0 + fo) / D - g0;
+    float num = 0.f;
+    for (int x = 0; x < nsg; ++x) num = fmaf(vals[x * chunk + fo], scl[x * nh + gi], num);
+    outp[f0 + fo] = num / den[gi];
+  }
+}
+
+// X: every item has its own resident workgroup (grid = items) and the splits
+// of a group merge by exchange; else workgroups take items in turn and the
+// last split of a group to arrive merges its records.
+template <int D, int G, bool X>
 __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = (float*)smem;  // [kWaves][G][D] the waves' accumulators, then the merge's per-split scales
   __shared__ DenseShared sh;
-  constexpr int LPR = D / 8, RPW = 64 / LPR, UV = 8;
+  __shared__ float2 xml[X ? kThreads : 1];  // exchange: (m, l) of the splits
+  __shared__ float xscl[X ? kThreads : 1];  // exchange: e^(m - M) of the splits
   constexpr int PD = D + 2;  // partial record: acc[D], m, l
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = lane / LPR, c = lane % LPR;
   int item = blockIdx.x;
+  // Launch tag of the exchanged records (X): the launch count is the sum of
+  // the kLaunchCounters launch counters, shared with the sampling kernel, and
+  // every tagged launch adds exactly kLaunchUnit to it (workgroup 0 adds
+  // kLaunchUnit - (grid - 1) to counter 0, workgroup x adds 1 to counter
+  // x mod kLaunchCounters, each after its own reads of the counters have
+  // returned).  The sum a workgroup reads is then at least L kLaunchUnit and
+  // lacks its own add, so all workgroups of launch L derive the same tag, and
+  // no record of an earlier launch carries it.
+  uint64_t lc = 0ull;  // wave 0, lane i < kLaunchCounters: counter i as read
+  if constexpr (X) {
+    if (tid < kLaunchCounters) lc = load_dev(p.ws.launches + tid * kLaunchStride);
+  }
+  auto take_tag = [&]() {  // wave 0
+    uint64_t c = tid < kLaunchCounters ? lc : 0ull;
+    asm volatile("" : "+v"(c));
+    uint64_t sum = 0ull;
+#pragma unroll
+    for (int i = 0; i < kLaunchCounters; ++i)
+      sum += ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(c >> 32), i) << 32) |
+             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)c, i);
+    if (tid == 0) {
+      const uint32_t t = (uint32_t)(sum / kLaunchUnit) + 1u;
+      sh.epoch = t == 0u ? 1u : t;
+    }
+  };
 
   while (item < p.total_items) {
     const int group = item / p.ns, s = item % p.ns;
     const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
+    float* outp = p.out + (size_t)(b * p.Hq + h0) * D;
     // the length is a scalar read (it does not change during the kernel), and
     // the split's first K and V rows are requested before it is used: they
     // need only the item's place and the K block's row count
@@ -326,12 +497,29 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
     if (!valid) {
       dense_drop<D, G>(first);
       if (s == 0)
-        for (int i = tid; i < G * D; i += kThreads) p.out[(size_t)(b * p.Hq + h0) * D + i] = __builtin_nanf("");
+        for (int i = tid; i < G * D; i += kThreads) outp[i] = __builtin_nanf("");
+      if (X && w == 0) take_tag();
     } else if (s >= nsg) {
       dense_drop<D, G>(first);
+      if (X && w == 0) take_tag();
+    } else if (X) {
+      const int len = min(p.split, n - k0);
+      split_pass<D, G>(p, b, hk, k0, len, red, sh, first);
+      if (w == 0) take_tag();
+      __syncthreads();
+      uint64_t* grec = p.ws.xrec + (size_t)group * p.ns * G * PD;
+      finish_split<D, G>(red, sh, nsg == 1 ? kOutput : kTaggedRecord, nullptr, grec + (size_t)s * G * PD, sh.epoch,
+                         outp);
+      if (nsg > 1) {
+        __syncthreads();  // the accumulator area is reused for the merge
+        exchange_merge<D, G>(p, grec, s, nsg, sh.epoch, red, xml, xscl, sh.den, outp);
+      }
     } else {
       const int len = min(p.split, n - k0);
-      split_pass<D, G>(p, b, hk, k0, len, red, sh, p.ws.partial + (size_t)(group * p.ns + s) * G * PD, first);
+      split_pass<D, G>(p, b, hk, k0, len, red, sh, first);
+      __syncthreads();
+      finish_split<D, G>(red, sh, kFloatRecord, p.ws.partial + (size_t)(group * p.ns + s) * G * PD, nullptr, 0u,
+                         nullptr);
       wait_memory();
       __syncthreads();
       // arrival counter of the group (zero at rest: the last arrival resets it)
@@ -423,6 +611,13 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
       }
     }
 
+    if constexpr (X) {
+      // this workgroup's share of the launch count (its counter reads have
+      // returned: the tag was derived from them)
+      const uint64_t my_add = blockIdx.x == 0 ? kLaunchUnit - (uint64_t)(p.grid - 1) : 1ull;
+      if (tid == 0) atomic_add_noret(p.ws.launches + (blockIdx.x % kLaunchCounters) * kLaunchStride,
+                                     lc == ~0ull ? 0ull : my_add);
+    }
     if (p.grid >= p.total_items) break;
     __syncthreads();
     if (tid == 0) {
@@ -435,12 +630,12 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool X>
 int capacity_t() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  auto fn = dense_kernel<D, G>;
+  auto fn = dense_kernel<D, G, X>;
   const size_t lds = DenseLds<D, G>::bytes;
   (void)hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess) return 0;
@@ -450,15 +645,20 @@ int capacity_t() {
 template <int D, int G>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   const size_t lds = DenseLds<D, G>::bytes;
-  hipLaunchKernelGGL((dense_kernel<D, G>), dim3(p.grid), dim3(kThreads), lds, stream, p);
+  if (p.exch)
+    hipLaunchKernelGGL((dense_kernel<D, G, true>), dim3(p.grid), dim3(kThreads), lds, stream, p);
+  else
+    hipLaunchKernelGGL((dense_kernel<D, G, false>), dim3(p.grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// The smaller of the two variants' resident capacities, so that a grid
+// within it is resident with either.
 int dense_capacity(int D, int G) {
 #define SANTA_CASE(DD, GG) \
-  if (D == DD && G == GG) return capacity_t<DD, GG>();
+  if (D == DD && G == GG) return std::min(capacity_t<DD, GG, false>(), capacity_t<DD, GG, true>());
   SANTA_CASE(64, 1) SANTA_CASE(64, 2) SANTA_CASE(64, 4) SANTA_CASE(64, 8)
   SANTA_CASE(128, 1) SANTA_CASE(128, 2) SANTA_CASE(128, 4) SANTA_CASE(128, 8)
 #undef SANTA_CASE
