@@ -53,9 +53,10 @@
  *  The dense kernel's work counter and arrival counters must be zero when a
  *  call starts and every call leaves them at zero; the launch counters only
  *  grow; no data region overlaps the header or the arrival counters.
- *  Statistics slots carry a launch number taken from the launch counters,
- *  which every sampling call advances, and every other data word is written (or cleared)
- *  before it is read within a call.  So one buffer serves any sequence of
+ *  Statistics slots, and the dense kernel's records when its splits exchange
+ *  them (every work item resident at once), carry a launch number taken from
+ *  the launch counters, which every such call advances; every other data
+ *  word is written (or cleared) before it is read within a call.  So one buffer serves any sequence of
  *  calls, of any entry point, whose problems each fit in it (including
  *  replays of a captured HIP graph).  Calls that share one workspace must not
  *  run concurrently.  After a call that reported a device error
