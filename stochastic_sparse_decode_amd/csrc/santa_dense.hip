@@ -143,7 +143,7 @@ __device__ __forceinline__ void dense_drop(const DenseBuf<D, G>& bf) {
 // combines the four.
 template <int D, int G>
 __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk, int k0, int len, float* red,
-                                           DenseShared& sh, const DenseBuf<D, G>& first) {
+                                           DenseShared& sh, const DenseBuf<D, G>& first, bool first_to_block) {
   using Gm = Geo<D, G>;
   constexpr int LPR = Gm::LPR, RPW = Gm::RPW, U = Gm::U, BR = Gm::BR;
   constexpr int NB = DenseBuf<D, G>::NB;       // blocks per register buffer
@@ -221,11 +221,12 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
     }
   };
   // The first iteration's rows were requested by the caller, clamped to the
-  // K block.  A split shorter than one iteration then holds rows past its end
-  // whose values are not ours to multiply (0 * NaN is NaN): its first rows
-  // are requested again, clamped to the split.
+  // split, or (first_to_block) to the K block.  A split shorter than one
+  // iteration then holds rows past its end whose values are not ours to
+  // multiply (0 * NaN is NaN): its first rows are requested again, clamped to
+  // the split.
   Buf b0 = first, b1;
-  if (len < STEP) issue(b0, 0);
+  if (first_to_block && len < STEP) issue(b0, 0);
   for (int base = 0; base < len; base += 2 * STEP) {
     issue(b1, base + STEP);
     consume(b0, base);
@@ -484,27 +485,30 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
     const int group = item / p.ns, s = item % p.ns;
     const int b = group / p.Hkv, hk = group % p.Hkv, h0 = hk * G;
     float* outp = p.out + (size_t)(b * p.Hq + h0) * D;
-    // the length is a scalar read (it does not change during the kernel), and
-    // the split's first K and V rows are requested before it is used: they
-    // need only the item's place and the K block's row count
+    // The length is a scalar read (it does not change during the kernel).  On
+    // the resident grid (X), where every item starts with the launch, the
+    // split's first K and V rows are requested before the length is used:
+    // they need only the item's place and the K block's row count.  Items
+    // taken in turn request them after it, and not at all for a split past
+    // the sequence's end (a ragged batch has many).
     const int n = *(const __attribute__((address_space(4))) int32_t*)(p.n_k + b);
     const int k0 = s * p.split;
     DenseBuf<D, G> first;
-    dense_issue<D, G>(p, b, hk, k0, first, 0, min(p.split, p.max_n_k - k0));
+    if constexpr (X) dense_issue<D, G>(p, b, hk, k0, first, 0, min(p.split, p.max_n_k - k0));
     const bool valid = n >= 1 && n <= p.max_n_k;
     const int nsg = valid ? (n + p.split - 1) / p.split : 0;
 
     if (!valid) {
-      dense_drop<D, G>(first);
+      if constexpr (X) dense_drop<D, G>(first);
       if (s == 0)
         for (int i = tid; i < G * D; i += kThreads) outp[i] = __builtin_nanf("");
       if (X && w == 0) take_tag();
     } else if (s >= nsg) {
-      dense_drop<D, G>(first);
+      if constexpr (X) dense_drop<D, G>(first);
       if (X && w == 0) take_tag();
     } else if (X) {
       const int len = min(p.split, n - k0);
-      split_pass<D, G>(p, b, hk, k0, len, red, sh, first);
+      split_pass<D, G>(p, b, hk, k0, len, red, sh, first, true);
       if (w == 0) take_tag();
       __syncthreads();
       uint64_t* grec = p.ws.xrec + (size_t)group * p.ns * G * PD;
@@ -516,7 +520,8 @@ __global__ __launch_bounds__(kThreads) void dense_kernel(DecodeParams p) {
       }
     } else {
       const int len = min(p.split, n - k0);
-      split_pass<D, G>(p, b, hk, k0, len, red, sh, first);
+      dense_issue<D, G>(p, b, hk, k0, first, 0, len);
+      split_pass<D, G>(p, b, hk, k0, len, red, sh, first, false);
       __syncthreads();
       finish_split<D, G>(red, sh, kFloatRecord, p.ws.partial + (size_t)(group * p.ns + s) * G * PD, nullptr, 0u,
                          nullptr);
