@@ -90,11 +90,12 @@ __device__ __forceinline__ float row_sum_mod(float v) {
 }
 
 // K and V rows of one iteration of split_pass: NB blocks of U 16-byte loads
-// each, per lane.
+// each, per lane.  A block of G = 1 at d = 128 is already 64 rows (16 loads
+// of K and 16 of V per lane), so its buffer holds one.
 template <int D, int G>
 struct DenseBuf {
   using Gm = Geo<D, G>;
-  static constexpr int NB = 2;  // blocks per register buffer
+  static constexpr int NB = Gm::U >= 16 ? 1 : 2;  // blocks per register buffer
   uint4 k[NB][Gm::U], v[NB][Gm::U];
 };
 
@@ -208,16 +209,29 @@ __device__ __forceinline__ void split_pass(const DecodeParams& p, int b, int hk,
       // the V rows of the block: this lane holds features c*8.. of rows
       // u * RPW + r; the weight of (row u * RPW + r, head g) sits in lane
       // j = u * G + g of this lane's row (U * G = LPR such lanes)
-      float f[U][8];
+      if constexpr (G == 1) {
+        // one head: each row's values are unpacked where they are used (the
+        // 16 rows of a lane unpacked at once would take 128 registers)
+        static_for<LPR>([&](auto jc) {
+          constexpr int J = decltype(jc)::value;
+          const float wt = row_lane<LPR, J>(pw, lane);
+          float fj[8];
+          unpack8(bf.v[nb][J], fj);
 #pragma unroll
-      for (int u = 0; u < U; ++u) unpack8(bf.v[nb][u], f[u]);
+          for (int e = 0; e < 8; ++e) acc[0][e] = fmaf(wt, fj[e], acc[0][e]);
+        });
+      } else {
+        float f[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) unpack8(bf.v[nb][u], f[u]);
 
-      static_for<LPR>([&](auto jc) {
-        constexpr int J = decltype(jc)::value, u = J / G, g = J % G;
-        const float wt = row_lane<LPR, J>(pw, lane);
+        static_for<LPR>([&](auto jc) {
+          constexpr int J = decltype(jc)::value, u = J / G, g = J % G;
+          const float wt = row_lane<LPR, J>(pw, lane);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(wt, f[u][e], acc[g][e]);
-      });
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(wt, f[u][e], acc[g][e]);
+        });
+      }
     }
   };
   // The first iteration's rows were requested by the caller, clamped to the

@@ -26,6 +26,7 @@ CASES = [
                                           pad_value=np.float16(np.nan))),
     ("d64_g2", lambda: W.random_case(3, 4, 2, 64, [1, 1030, 2048], max_n_k=2048, seed=4)),
     ("g8", lambda: W.random_case(1, 16, 2, 128, [5000], seed=6, planted=True)),
+    ("g1_d128", lambda: W.random_case(2, 4, 4, 128, [3000, 777], max_n_k=3072, seed=9, planted=True)),
     ("llama32k", lambda: W.llama(B=1, n_k=32768, seed=1001)),
 ]
 
