@@ -346,10 +346,22 @@ __device__ __forceinline__ void finish_split(const float* red, DenseShared& sh, 
   }
 }
 
+// Sum over the 64 lanes of a wave, returned in every lane, in a fixed order:
+// DPP row shifts (an empty source adds 0) and row broadcasts leave the sum in
+// lane 63, which is then read as a scalar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add_step(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                   0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = dpp_add_step<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add_step<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add_step<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add_step<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add_step<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_add_step<0x143, 0xC>(v);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Merge by exchange, for split s of a group of nsg > 1 splits whose
