@@ -62,6 +62,15 @@
  *  run concurrently.  After a call that reported a device error
  *  (santa_workspace_error != 0) the workspace must be zero-filled again.
  *
+ *  Waits between workgroups: a sampling call, and santa_dense_decode when
+ *  every work item has its own resident workgroup, has workgroups of one
+ *  launch wait for statistics that other workgroups of that launch publish.
+ *  The grid is sized to what the device keeps resident, so the waits end
+ *  when the launch has the device to itself; one that shares it with other
+ *  work waits until that work leaves room.  Every wait is bounded: after
+ *  about 2^20 polling rounds a workgroup sets bit 0 of the workspace error
+ *  bits and goes on, so no call hangs, and its results are then invalid.
+ *
  *  Errors: every entry point returns a santa_status.  Arguments are checked
  *  on the host before any HIP call; on a check failure nothing is enqueued.
  *  n_k lives in device memory and cannot be checked without a sync: a
