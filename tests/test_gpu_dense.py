@@ -126,3 +126,18 @@ def test_dense_exchange_tags_and_repeats():
         santa.santa_decode(q, K, V, nk, 64, 2, 5 + rep, wls[1].scale, workspace=ws)
         torch.cuda.synchronize()
         assert santa.santa_workspace_error(ws) == 0
+
+
+def test_dense_exchange_mixed_groups_in_one_launch():
+    """One resident launch whose groups take every exchange case: an invalid
+    length (NaN rows), one split (the output written directly), two splits
+    and eighteen (shares straddling heads)."""
+    wl = W.random_case(4, 8, 2, 128, [0, 300, 700, 9000], max_n_k=9216, seed=41, planted=True)
+    got = run_dense(wl)
+    assert np.isnan(got[0]).all()
+    for b in range(1, 4):
+        n = int(wl.n_k[b])
+        ref = O.dense_decode(wl.q[b:b + 1], wl.K[b:b + 1, :, :n], wl.V[b:b + 1, :, :n], wl.n_k[b:b + 1], wl.scale)
+        err = np.abs(got[b] - ref[0]).max()
+        print("   b=%d n_k=%d max abs err %.3g" % (b, n, err), flush=True)
+        assert err <= P.DENSE_TOL
