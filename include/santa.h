@@ -46,19 +46,29 @@
  *
  *  Workspace: a 256-byte aligned device buffer of at least
  *  santa_workspace_bytes(problem, S) bytes, zero-filled by the caller once
- *  before first use.  The first 1 KiB holds the error bits and counters, a
- *  64 KiB region of the dense kernel's arrival counters follows, then the data
- *  of the call (the dense kernel's per-split records, or the sampling
- *  kernel's per-split statistics slots, exact sums and Gumbel-max winners).
- *  The dense kernel's work counter and arrival counters must be zero when a
- *  call starts and every call leaves them at zero; the launch counters only
- *  grow; no data region overlaps the header or the arrival counters.
- *  Statistics slots, and the dense kernel's records when its splits exchange
- *  them (every work item resident at once), carry a launch number taken from
- *  the launch counters, which every such call advances; every other data
- *  word is written (or cleared) before it is read within a call.  So one buffer serves any sequence of
- *  calls, of any entry point, whose problems each fit in it (including
- *  replays of a captured HIP graph).  Calls that share one workspace must not
+ *  before first use.  The first 1 KiB holds the error bits and counters, and
+ *  a 64 KiB region of the dense kernel's arrival counters follows.  The data
+ *  of a call comes in two parts:
+ *   - words tagged with a launch number: the sampling kernel's per-split
+ *     statistics slots, or the dense kernel's records when its splits
+ *     exchange them (every work item resident at once).  They grow from the
+ *     start of the data area;
+ *   - untagged data, placed at the end of the buffer as passed: the exact
+ *     sums, Gumbel-max winners, prepared Bernoulli queries, or the dense
+ *     kernel's float records.  Each call writes (or clears) this data before
+ *     reading it.
+ *  The launch number comes from the launch counters, which every tagged call
+ *  advances; a tagged word is accepted only with the current number.  The
+ *  dense kernel's work counter and arrival counters must be zero when a call
+ *  starts, and every call leaves them at zero; the launch counters only grow.
+ *  No data region overlaps the header or the arrival counters.
+ *  santa_workspace_bytes(P, S) leaves room for the larger tagged part and the
+ *  larger untagged part of P's calls of every kind.  So a buffer of that size
+ *  serves any sequence of calls, of any entry point, whose problems are no
+ *  larger than P in any dimension and whose S is at most S.  This includes
+ *  replays of a captured HIP graph.  Every call must pass the same
+ *  workspace_bytes; the tagged words of one call then never overlap the
+ *  untagged data of another.  Calls that share one workspace must not
  *  run concurrently.  After a call that reported a device error
  *  (santa_workspace_error != 0) the workspace must be zero-filled again.
  *
@@ -253,8 +263,11 @@ int santa_pack_k_feature_major(const santa_problem* problem, const void* K, void
  * hipMalloc): the same computation, arguments and results as santa_decode, with
  * the workspace in device memory that the library owns instead of a caller's
  * buffer.  Each GPU the library runs on holds one array of
- * SANTA_NOALLOC_SCRATCH_BYTES bytes for the rest of the process; a problem whose
- * workspace would exceed it returns SANTA_ERR_WORKSPACE.  The call allocates
+ * SANTA_NOALLOC_SCRATCH_BYTES bytes for the rest of the process.  Its data area
+ * past the 65 KiB of header and counters is split in two halves, one for the
+ * tagged part of every call and one for the untagged part, so that calls of
+ * any size can follow each other.  A problem whose statistics slots or whose
+ * other data would exceed a half returns SANTA_ERR_WORKSPACE.  The call allocates
  * nothing (no hipMalloc, hipFree or allocating library routine); its first call
  * on a device takes the array's device address and enqueues a one-word clear
  * on `stream`.  All calls on one GPU share its array: calls that overlap on one

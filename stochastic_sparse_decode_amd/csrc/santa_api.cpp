@@ -38,26 +38,34 @@ bool supported(const santa_problem* p) {
 
 // Workspace layout: a 1 KiB header (error bits, the dense kernel's work
 // counter, the launch counters), a 64 KiB region of the dense kernel's arrival
-// counters, then the data of the kernel that runs: the dense kernel's partial
-// records (floats, or tagged 8-byte words when its splits exchange them), or
-// the sampling kernel's statistics slots and the exact output sums of the
-// deterministic mode.  The header's work counter and the arrival
-// counters must be zero when a launch starts (every dense launch leaves them at
-// zero; the caller zero-fills a new buffer), and no data region of any problem
-// overlaps them, since the data regions start after the fixed-size counter
-// region.  Slots and exchanged records carry a launch tag, and float partial
-// records and exact sums are
-// written (or cleared) before they are read in every launch, so calls of
-// either kind and of different sizes may share a buffer even though their data
-// regions overlap.
+// counters, then the data of the call in two parts:
+//  - tagged words, from the start of the data area: the sampling kernel's
+//    statistics slots, or the dense kernel's records when its splits exchange
+//    them.  A reader accepts such a word only if it carries this launch's
+//    tag, and words written by earlier launches carry earlier tags;
+//  - untagged data, at the end of the buffer: the exact output sums of the
+//    deterministic mode, the Gumbel-max winners, the prepared Bernoulli
+//    queries, or the dense kernel's float records.  They are written (or
+//    cleared) before they are read in every call.
+// The header's work counter and the arrival counters must be zero when a
+// launch starts (every dense launch leaves them at zero; the caller zero-fills
+// a new buffer), and no data region overlaps them.  santa_workspace_bytes(P)
+// leaves room for the larger tagged part and the larger untagged part of P's
+// calls of either kind.  Every part grows with each dimension of the problem
+// and with S, so in a buffer of that size (passed with the same size every
+// time) the tagged words of any call whose problem is no larger never overlap
+// the untagged data of another: stale untagged data, whose bits are
+// arbitrary, can never be taken for a slot of this launch.
 constexpr size_t kCounterBytes = (size_t)santa::kMaxDenseGroups * sizeof(uint32_t);
 constexpr size_t kHeaderBytes = 1024;  // error bits, work counter, kLaunchCounters launch counters (one per 128 bytes)
 
 struct Layout {
-  size_t partial, stats, acc, win, bern;
-  size_t dense_total() const { return kHeaderBytes + kCounterBytes + partial; }
+  size_t xrec, partial, stats, acc, win, bern;
+  size_t tagged() const { return xrec > stats ? xrec : stats; }
+  size_t untagged() const { return partial > acc + win + bern ? partial : acc + win + bern; }
+  size_t dense_total() const { return kHeaderBytes + kCounterBytes + xrec + partial; }
   size_t sampling_total() const { return kHeaderBytes + kCounterBytes + stats + acc + win + bern; }
-  size_t total() const { return dense_total() > sampling_total() ? dense_total() : sampling_total(); }
+  size_t total() const { return kHeaderBytes + kCounterBytes + tagged() + untagged(); }
 };
 
 // S: the sample count of the call (the Gumbel-max draws keep one winner per
@@ -67,7 +75,8 @@ Layout layout_of(const santa_problem* p, int32_t S) {
   const size_t groups = (size_t)p->batch * p->num_kv_heads;
   const size_t G = (size_t)group_size(p), D = (size_t)p->head_dim;
   const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
-  L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(uint64_t));  // tagged words at either split
+  L.xrec = round_up(groups * ns_min * G * (D + 2) * sizeof(uint64_t));  // at either split length
+  L.partial = round_up(groups * ns_min * G * (D + 2) * sizeof(float));
   L.stats = round_up(groups * ns_min * G * (size_t)santa::slot_words_for(groups * ns_min * G) * sizeof(uint64_t));
   L.acc = round_up(groups * G * D * sizeof(uint64_t));
   L.win = round_up((size_t)p->batch * p->num_q_heads * (size_t)S * sizeof(uint64_t));
@@ -75,8 +84,10 @@ Layout layout_of(const santa_problem* p, int32_t S) {
   return L;
 }
 
-// err, if not null, takes the place of the header's error word.
-Workspace carve(void* base, const santa_problem* p, int32_t S, bool dense, uint32_t* err = nullptr) {
+// ws_bytes: the buffer's size as passed (the untagged part ends there).  err,
+// if not null, takes the place of the header's error word.
+Workspace carve(void* base, size_t ws_bytes, const santa_problem* p, int32_t S, bool dense,
+                uint32_t* err = nullptr) {
   unsigned char* b = (unsigned char*)base;
   const Layout L = layout_of(p, S);
   Workspace w{};
@@ -85,14 +96,15 @@ Workspace carve(void* base, const santa_problem* p, int32_t S, bool dense, uint3
   w.launches = (uint64_t*)(b + 128);  // counter i at launches + i * kLaunchStride
   w.arrive = (uint32_t*)(b + kHeaderBytes);
   unsigned char* x = b + kHeaderBytes + kCounterBytes;
+  unsigned char* end = b + ws_bytes / kAlign * kAlign;
   if (dense) {
-    w.partial = (float*)x;
     w.xrec = (uint64_t*)x;
+    w.partial = (float*)(end - L.partial);
   } else {
     w.stats = (uint64_t*)x;
-    w.acc = (uint64_t*)(x + L.stats);
-    w.win = (uint64_t*)(x + L.stats + L.acc);
-    w.bern = (uint4*)(x + L.stats + L.acc + L.win);
+    w.acc = (uint64_t*)(end - (L.acc + L.win + L.bern));
+    w.win = (uint64_t*)(end - (L.win + L.bern));
+    w.bern = (uint4*)(end - L.bern);
   }
   return w;
 }
@@ -165,7 +177,8 @@ int common_checks(const santa_problem* p, const void* q, const void* K, const vo
 }
 
 DecodeParams base_params(const santa_problem* p, const void* q, const void* K, const void* V,
-                         const int32_t* n_k, float* out, void* ws, int32_t S, bool dense, uint32_t* err = nullptr) {
+                         const int32_t* n_k, float* out, void* ws, size_t ws_bytes, int32_t S, bool dense,
+                         uint32_t* err = nullptr) {
   DecodeParams d{};
   d.q = q;
   d.K = K;
@@ -181,7 +194,7 @@ DecodeParams base_params(const santa_problem* p, const void* q, const void* K, c
   d.scale = p->scale;
   d.ns = (p->max_n_k + santa::kSplit - 1) / santa::kSplit;
   d.total_items = p->batch * p->num_kv_heads * d.ns;
-  d.ws = carve(ws, p, S, dense, err);
+  d.ws = carve(ws, ws_bytes, p, S, dense, err);
   d.det = (p->flags & SANTA_DETERMINISTIC) ? 1 : 0;
   const size_t ns_min = ((size_t)p->max_n_k + santa::kMinSplit - 1) / santa::kMinSplit;
   d.slot_words = santa::slot_words_for((size_t)p->batch * p->num_kv_heads * ns_min * d.G);  // as layout_of
@@ -264,7 +277,7 @@ int sampled_step(const santa_problem* p, const void* q, const void* K, const voi
   const bool bern = kind == santa::kOpBernoulli || kind == santa::kOpBernoulliBudget;
   if (bern && p->max_n_k % santa::kTile != 0) return SANTA_ERR_SHAPE;
   if (kind == santa::kOpBernoulliBudget && (budget < 1 || budget > p->head_dim)) return SANTA_ERR_SHAPE;
-  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, S, false, err);
+  DecodeParams d = base_params(p, q, K, V, n_k, out, ws, ws_bytes, S, false, err);
   d.idx_out = indices_out;
   d.scores_out = scores_out;
   d.kept_out = kept_out;
@@ -307,8 +320,14 @@ int decode_on(const santa_problem* problem, const void* q, const void* K, const 
   return sampled_step(problem, q, K, V, n_k, S, mode, seed, out, indices_out, scores_out, nullptr, nullptr,
                       Paging{}, workspace, workspace_bytes, stream, kOpDecode, 0, err);
 }
+// Bytes a sampling call needs in a fixed-size buffer shared by problems of
+// any size: its tagged part and its untagged part must each fit in half of the
+// data area, so that no call's tagged words overlap another's untagged data.
 size_t sampling_workspace_bytes(const santa_problem* problem, int32_t S) {
-  return problem_ok(problem) && S >= 1 && S <= SANTA_MAX_S ? layout_of(problem, S).sampling_total() : 0;
+  if (!problem_ok(problem) || S < 1 || S > SANTA_MAX_S) return 0;
+  const Layout L = layout_of(problem, S);
+  const size_t u = L.acc + L.win + L.bern, half = L.stats > u ? L.stats : u;
+  return kHeaderBytes + kCounterBytes + 2 * half;
 }
 }  // namespace santa
 
@@ -374,7 +393,7 @@ int santa_dense_decode(const santa_problem* problem, const void* q, const void* 
   int st = common_checks(problem, q, K, V, n_k, out, workspace, workspace_bytes, true);
   if (st != SANTA_OK) return st;
   if ((long long)problem->batch * problem->num_kv_heads > santa::kMaxDenseGroups) return SANTA_ERR_UNSUPPORTED;
-  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, 1, true);
+  DecodeParams d = base_params(problem, q, K, V, n_k, out, workspace, workspace_bytes, 1, true);
   st = choose_grid(d, santa::kOpDense);
   if (st != SANTA_OK) return st;
   const hipError_t e = santa::launch_dense(d, (hipStream_t)stream);

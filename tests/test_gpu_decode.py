@@ -486,3 +486,33 @@ def test_iid_many_points_in_one_split_parity():
         in_first = (idx_o[0] < 1024).sum(axis=-1)
         assert in_first.max() > 128 and (idx_o[0] >= 1024).any(), in_first
         check_parity(wl, S, 0, seed, "iid-heavy-split")
+
+
+def test_stale_exact_sums_never_pass_for_slots(llama32k):
+    """The exact sums of a deterministic call carry markers of 2^52 per
+    element, so the upper halves of their 64-bit words are launch numbers the
+    counters will reach.  Such words left in a shared workspace must never be
+    taken for statistics slots of a later launch.  Here the launch counters
+    are set so that the next launch number equals the upper half of a stale
+    word, and the Llama-layer call must still reproduce, bit for bit, the
+    same call on a fresh workspace (deterministic mode)."""
+    small = W.random_case(2, 8, 2, 128, [3000, 1500], max_n_k=3100, seed=2, planted=True)
+    prob = santa.problem(torch.from_numpy(llama32k.q), torch.from_numpy(llama32k.K), llama32k.scale)
+    ws = santa.new_workspace(prob, "cuda")
+    run_decode_det(small, 64, 2, 3, workspace=ws)
+    words = ws.cpu().numpy().view(np.uint64)
+    upper = (words[(1024 + 65536) // 8:] >> np.uint64(32)).astype(np.int64)
+    marked = upper[upper >= (1 << 20)]
+    assert marked.size > 0  # the exact sums are there
+    vals, counts = np.unique(marked, return_counts=True)
+    target = int(vals[np.argmax(counts)])
+    hdr = words[:128].copy()
+    launches = int(sum(int(hdr[16 + 16 * i]) for i in range(7))) >> 20
+    assert target > launches + 1  # a launch number not used yet
+    hdr[16] = np.uint64((target - 1) << 20)
+    for i in range(1, 7):
+        hdr[16 + 16 * i] = np.uint64(0)
+    ws[:1024].copy_(torch.from_numpy(hdr.view(np.uint8)).to(ws.device))
+    got = run_decode_det(llama32k, 128, 2, 11, workspace=ws)
+    ref = run_decode_det(llama32k, 128, 2, 11)
+    _same(got, ref)
